@@ -1,0 +1,204 @@
+"""Benchmark: bs=1 block-diffusion decode of the Qwen3-4B-shaped random-init model on one GPU.
+
+A step is one block: ceil(32 / k) denoising rounds (self-conditioning input, 36 layers,
+fused head statistics, commit) plus the commit pass that writes the block's K/V, as one
+replay of the library's captured graph.  The timed region runs --steps consecutive blocks
+after a 256-token prompt (prefill excluded), with the block's token readback queued after
+each block.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+METRIC = "bs=1 block-decode tokens/s at fixed k commits/round; rounds/s; % HBM roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(shape, L, head_rows=32):
+    """HBM bytes one round must move at prefix length L: every weight once, the
+    embedding once for the head, the adapter, the prefix + block K/V of every layer."""
+    s = shape
+    D = s.head_dim
+    per_layer = 2 * ((s.hq + 2 * s.hkv) * D * s.d + s.d * s.hq * D + 3 * s.ffn * s.d)
+    w = s.n_layers * per_layer + 2 * s.d * s.d          # layers + W_sc
+    head = 2 * s.vocab * s.d
+    kv = s.n_layers * 2 * 2 * s.hkv * D * (L + s.block)
+    return w + head + kv
+
+
+def commit_pass_bytes(shape, L):
+    s = shape
+    D = s.head_dim
+    per_layer = 2 * ((s.hq + 2 * s.hkv) * D * s.d + s.d * s.hq * D + 3 * s.ffn * s.d)
+    last = 2 * (s.hq + 2 * s.hkv) * D * s.d
+    kv = (s.n_layers - 1) * 2 * 2 * s.hkv * D * (L + s.block)
+    return (s.n_layers - 1) * per_layer + last + kv
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128, help="timed blocks (128 = 4096 new tokens)")
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--k", type=int, default=6, help="commits per round of the headline number")
+    ap.add_argument("--k-list", default="1,2,6,11", help="other k values also timed (empty to skip)")
+    ap.add_argument("--prompt", type=int, default=256)
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rounds", type=int, default=1)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
+                                   "note, not implemented", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import block_diffusion_decoding_denoise_amd as dlm
+
+    dlm.lib()
+    shape = synth.QWEN4B
+    B = shape.block
+    n_new = args.steps * B
+    cap = args.prompt + (max(args.steps, args.warmup) + 1) * B
+    t0 = time.time()
+    w = synth.Weights(shape, args.seed)
+    names = w.names_dense()
+    dev_w = {}
+    for n in names:
+        a = w[n]
+        dev_w[n] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    log(f"weights drawn and uploaded in {time.time() - t0:.1f}s")
+    model = dlm.Model(shape, dev_w, cap=cap)
+    prompt = torch.from_numpy(synth.prompt_ids(shape, args.prompt, args.seed))
+    host_tok = torch.empty(args.steps, B, dtype=torch.int32).pin_memory()
+
+    def run(k, steps, warmup):
+        rule = dlm.CommitRule.fixed_k(k)
+        model.set_len(0)
+        model.prefill(prompt)
+        for _ in range(warmup):
+            model.decode_block(rule)
+        torch.cuda.synchronize()
+        model.set_len(args.prompt)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t_host = time.perf_counter()
+        ev0.record()
+        for i in range(steps):
+            model.decode_block(rule)
+            host_tok[i].copy_(model.tokens, non_blocking=True)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_host
+        ms = ev0.elapsed_time(ev1)
+        st = dlm.state_dict(model.state)
+        R = math.ceil(B / k)
+        assert st["round"] == R, st
+        return ms / 1000.0, wall, R
+
+    results = {}
+    ks = [args.k] + [int(x) for x in args.k_list.split(",") if x and int(x) != args.k]
+    for k in ks:
+        sec, wall, R = run(k, args.steps, args.warmup)
+        L_mean = args.prompt + B * (args.steps - 1) / 2
+        rb = sum(algorithmic_bytes(shape, args.prompt + B * i) * R + commit_pass_bytes(shape, args.prompt + B * i)
+                 for i in range(args.steps))
+        results[k] = {"tok_s": n_new / sec, "rounds_s": args.steps * R / sec, "ms_per_block": 1e3 * sec / args.steps,
+                      "hbm_frac": rb / sec / HBM_PEAK, "rounds_per_block": R, "wall_s": wall,
+                      "bytes_per_block": rb / args.steps, "mean_prefix": L_mean}
+        log(f"k={k}: {results[k]['tok_s']:.0f} tok/s, {results[k]['rounds_s']:.0f} rounds/s, "
+            f"{results[k]['ms_per_block']:.2f} ms/block, {100 * results[k]['hbm_frac']:.1f}% of 8 TB/s")
+
+    # ---- dominant kernel: the gate/up projection GEMM, timed alone with HIP events on its stream
+    s = shape
+    Wgu = (torch.randn(2 * s.ffn, s.d, device="cuda") * 0.02).to(torch.bfloat16)
+    Wp = dlm.pack_matrix(Wgu)
+    x = dlm.pack_activations((torch.randn(32, s.d, device="cuda") * 0.1).to(torch.bfloat16))
+    y = torch.empty(32, 2 * s.ffn, device="cuda")
+    lws = torch.zeros(dlm.lib().dlm_linear_ws_bytes(2 * s.ffn, s.d), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        dlm.linear(Wp, x, y=y, ws=lws)
+    torch.cuda.synchronize()
+    n_rep = 50
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(n_rep):
+        dlm.linear(Wp, x, y=y, ws=lws)
+    ev1.record()
+    torch.cuda.synchronize()
+    t_launch = ev0.elapsed_time(ev1) / 1e3 / n_rep
+    gemm_bytes = 2 * (2 * s.ffn * s.d) + 2 * 32 * s.d + 4 * 32 * 2 * s.ffn
+    roofline = {"bound": "hbm", "achieved": gemm_bytes / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": gemm_bytes / t_launch / HBM_PEAK, "traffic": None,
+                "kernel": "gemm_bf16_kernel (gate/up projection, N=19456, K=2560, M=32)",
+                "bytes_per_launch": gemm_bytes, "us_per_launch": t_launch * 1e6}
+    log(f"gate/up GEMM: {t_launch * 1e6:.1f} us/launch, {roofline['achieved']:.0f} GB/s")
+
+    # ---- CPU baseline: the oracle in float32 on a bounded sample (one round + one commit pass)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle import OracleModel, KVCache, Prec, CommitRule as OCR
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+        except Exception:
+            cores = os.cpu_count()
+        prec = Prec("bf16", np.float32)
+        om = OracleModel(shape, w, prec, cache_layers=False)
+        kv = KVCache.empty(shape, args.prompt + 2 * B, np.float32)
+        kv.length = args.prompt
+        toks = np.zeros(B, np.int32)
+        committed = np.zeros(B, np.uint8)
+        t0 = time.perf_counter()
+        res = oracle.denoise_round(om, kv, toks, committed, None, 0, OCR(1, 0.9, args.k, False, 32), prec)
+        t_round = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.commit_pass(om, kv, toks, prec)
+        t_cp = time.perf_counter() - t0
+        R = math.ceil(B / args.k)
+        cpu_tok_s = B / (R * t_round + t_cp)
+        cpu = {"value": cpu_tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"one denoising round and one commit pass of the same model at prefix {args.prompt} "
+                         f"(numpy float32 mode), extrapolated to a {R}-round block: "
+                         f"{t_round:.1f} s/round, {t_cp:.1f} s/commit pass"}
+        log(f"cpu oracle: {cpu_tok_s:.3f} tok/s ({t_round:.1f} s/round)")
+        del res
+
+    h = results[args.k]
+    line = {
+        "metric": METRIC, "value": h["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": h["ms_per_block"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"qwen3-4b-shaped random-init block decode, bs=1, block 32, fixed k={args.k}, "
+                               f"prompt {args.prompt}, {n_new} new tokens",
+                   "k": args.k, "block": B, "prompt": args.prompt, "new_tokens": n_new, "layers": s.n_layers,
+                   "d": s.d, "ffn": s.ffn, "vocab": s.vocab},
+        "rounds_per_s": h["rounds_s"], "hbm_frac_step": h["hbm_frac"],
+        "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
+                  for k, r in results.items()},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    model.close()
+
+
+if __name__ == "__main__":
+    main()

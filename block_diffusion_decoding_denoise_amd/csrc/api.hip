@@ -1,0 +1,804 @@
+// C ABI of the library: argument validation, workspace layout, the per-round sequence of
+// kernels and the device-resident block loop captured in a HIP graph.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "attn.h"
+#include "gemm.h"
+#include "head.h"
+#include "small.h"
+#include "moe.h"
+
+// ------------------------------------------------------------------ errors
+namespace dlm {
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DLM_OK;
+  return fail(DLM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool device_ok() {
+  static int cached[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::call_once(once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    cached[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                   strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+  });
+  return cached[dev] == 1;
+}
+}  // namespace dlm
+
+using namespace dlm;
+
+#define DLM_DEVICE_CHECK() \
+  do { if (!dlm::device_ok()) return dlm::fail(DLM_ERR_UNSUPPORTED, "no gfx950 device is current"); } while (0)
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" int dlm_abi_version(void) { return DLM_ABI_VERSION; }
+extern "C" const char* dlm_last_error(void) { return dlm::g_err; }
+
+// ------------------------------------------------------------------ block attention op
+static int check_attn(const dlm_attn_desc* d) {
+  DLM_REQUIRE(d, DLM_ERR_ARG, "desc is null");
+  DLM_REQUIRE(d->dtype == DLM_BF16 || d->dtype == DLM_F32, DLM_ERR_DTYPE, "attn dtype %d", d->dtype);
+  DLM_REQUIRE(d->hq > 0 && d->hkv > 0 && d->block > 0 && d->cap > 0, DLM_ERR_ARG, "non-positive size");
+  DLM_REQUIRE(d->hq % d->hkv == 0, DLM_ERR_SHAPE, "hq %% hkv != 0");
+  DLM_REQUIRE(d->head_dim == 64 || d->head_dim == 128, DLM_ERR_SHAPE, "head_dim must be 64 or 128");
+  DLM_REQUIRE(d->block <= 32, DLM_ERR_SHAPE, "block must be <= 32");
+  const int maxL = d->prefix_len_dev ? d->max_prefix_len : d->prefix_len;
+  DLM_REQUIRE(maxL >= 0 && d->prefix_len >= 0, DLM_ERR_ARG, "negative prefix length");
+  DLM_REQUIRE(maxL + d->block <= d->cap, DLM_ERR_SHAPE, "prefix + block exceeds cap");
+  return DLM_OK;
+}
+
+extern "C" size_t dlm_block_attn_ws_bytes(const dlm_attn_desc* d) {
+  if (check_attn(d) != DLM_OK) return 0;
+  if (d->dtype == DLM_F32) return 256;
+  const int maxL = d->prefix_len_dev ? d->max_prefix_len : d->prefix_len;
+  return attn_ws_bytes(d->hq, d->hkv, d->head_dim, attn_plan(d->hq, d->hkv, d->head_dim, d->block, maxL));
+}
+
+extern "C" int dlm_block_attn(const dlm_attn_desc* d, const void* q, const void* k, const void* v, void* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn(d);
+  if (rc) return rc;
+  DLM_REQUIRE(q && k && v && out, DLM_ERR_ARG, "null tensor");
+  DLM_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), DLM_ERR_ARG, "tensors must be 16-byte aligned");
+  const size_t need = dlm_block_attn_ws_bytes(d);
+  DLM_REQUIRE(ws || need == 0, DLM_ERR_ARG, "null workspace");
+  DLM_REQUIRE(ws_bytes >= need, DLM_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  DLM_DEVICE_CHECK();
+  hipStream_t st = (hipStream_t)stream;
+  if (d->dtype == DLM_F32)
+    return attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, d->hq, d->hkv, d->head_dim,
+                    d->block, d->cap, d->softmax_scale, d->prefix_len_dev, d->prefix_len, nullptr, st);
+  const int maxL = d->prefix_len_dev ? d->max_prefix_len : d->prefix_len;
+  return attn_bf16(q, k, v, out, d->hq, d->hkv, d->head_dim, d->block, d->cap, d->softmax_scale,
+                   d->prefix_len_dev, d->prefix_len, nullptr,
+                   attn_plan(d->hq, d->hkv, d->head_dim, d->block, maxL), ws, /*out_packed=*/0, st);
+}
+
+// ------------------------------------------------------------------ head op
+static int check_head(const dlm_head_desc* d) {
+  DLM_REQUIRE(d, DLM_ERR_ARG, "desc is null");
+  DLM_REQUIRE(d->dtype == DLM_BF16 || d->dtype == DLM_F32, DLM_ERR_DTYPE, "head dtype %d", d->dtype);
+  DLM_REQUIRE(d->rows > 0 && d->d > 0 && d->vocab > 0, DLM_ERR_ARG, "non-positive size");
+  DLM_REQUIRE(d->rows <= DLM_MAX_ROWS, DLM_ERR_SHAPE, "rows must be <= %d", DLM_MAX_ROWS);
+  DLM_REQUIRE(d->d % 32 == 0 && d->d <= 4096, DLM_ERR_SHAPE, "d must be a multiple of 32 and <= 4096");
+  DLM_REQUIRE(d->dtype == DLM_BF16 || d->d <= 256, DLM_ERR_SHAPE, "f32 head supports d <= 256");
+  return DLM_OK;
+}
+
+extern "C" size_t dlm_head_rowstats_ws_bytes(const dlm_head_desc* d) {
+  if (check_head(d) != DLM_OK) return 0;
+  return head_ws_bytes(d->dtype, d->rows, d->d, d->vocab);
+}
+
+extern "C" int dlm_head_rowstats(const dlm_head_desc* d, const void* h, const void* emb, const uint8_t* committed,
+                                 float* lse, float* entropy, float* maxprob, int32_t* argmax, float* pe,
+                                 float* logits_dbg, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_head(d);
+  if (rc) return rc;
+  DLM_REQUIRE(h && emb && lse && entropy && maxprob && argmax && ws, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(aligned16(h) && aligned16(emb), DLM_ERR_ARG, "h and emb must be 16-byte aligned");
+  const size_t need = dlm_head_rowstats_ws_bytes(d);
+  DLM_REQUIRE(ws_bytes >= need, DLM_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  DLM_DEVICE_CHECK();
+  return head_launch(d->dtype, h, emb, committed, d->rows, d->d, d->vocab, lse, entropy, maxprob, argmax, pe,
+                     logits_dbg, ws, nullptr, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ commit op
+static int check_rule(const dlm_commit_rule* r) {
+  DLM_REQUIRE(r, DLM_ERR_ARG, "rule is null");
+  DLM_REQUIRE(r->mode == DLM_COMMIT_THRESHOLD || r->mode == DLM_COMMIT_FIXED_K, DLM_ERR_ARG, "bad commit mode");
+  DLM_REQUIRE(r->max_rounds >= 1 && r->max_rounds <= DLM_MAX_ROUNDS, DLM_ERR_ARG, "max_rounds out of range");
+  DLM_REQUIRE(r->mode != DLM_COMMIT_FIXED_K || r->k >= 1, DLM_ERR_ARG, "k must be >= 1");
+  return DLM_OK;
+}
+
+extern "C" int dlm_commit(const dlm_commit_rule* rule, int rows, const float* maxprob, const int32_t* argmax,
+                          uint8_t* committed, int32_t* tokens, dlm_round_state* state, void* stream) {
+  int rc = check_rule(rule);
+  if (rc) return rc;
+  DLM_REQUIRE(rows >= 1 && rows <= DLM_MAX_ROWS, DLM_ERR_SHAPE, "rows must be in [1, %d]", DLM_MAX_ROWS);
+  DLM_REQUIRE(maxprob && argmax && committed && tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_DEVICE_CHECK();
+  return commit_launch(*rule, rows, maxprob, argmax, nullptr, nullptr, committed, tokens, state,
+                       (hipStream_t)stream);
+}
+
+extern "C" int dlm_block_reset(int rows, uint8_t* committed, int32_t* tokens, dlm_round_state* state,
+                               void* stream) {
+  DLM_REQUIRE(rows >= 1 && rows <= DLM_MAX_ROWS, DLM_ERR_SHAPE, "rows must be in [1, %d]", DLM_MAX_ROWS);
+  DLM_REQUIRE(committed && tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_DEVICE_CHECK();
+  return block_reset(rows, committed, tokens, state, nullptr, 0, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ self-conditioning op
+static int check_sc(const dlm_selfcond_desc* d) {
+  DLM_REQUIRE(d, DLM_ERR_ARG, "desc is null");
+  DLM_REQUIRE(d->dtype == DLM_BF16 || d->dtype == DLM_F32, DLM_ERR_DTYPE, "selfcond dtype %d", d->dtype);
+  DLM_REQUIRE(d->rows > 0 && d->d > 0 && d->vocab > 0, DLM_ERR_ARG, "non-positive size");
+  DLM_REQUIRE(d->rows <= 32, DLM_ERR_SHAPE, "rows must be <= 32");
+  DLM_REQUIRE(d->d % 32 == 0, DLM_ERR_SHAPE, "d must be a multiple of 32");
+  return DLM_OK;
+}
+
+static size_t sc_gemm_ws(int d) { return gemm_ws_bytes(d, d, gemm_plan(d, d)); }
+
+extern "C" size_t dlm_selfcond_ws_bytes(const dlm_selfcond_desc* d) {
+  if (check_sc(d) != DLM_OK) return 0;
+  const size_t el = d->dtype == DLM_BF16 ? 2 : 4;
+  return align_up((size_t)32 * d->d * el, 256) + (d->dtype == DLM_BF16 ? sc_gemm_ws(d->d) : 0);
+}
+
+static EpiParams epi_zero() {
+  EpiParams e;
+  memset(&e, 0, sizeof(e));
+  return e;
+}
+
+extern "C" int dlm_selfcond(const dlm_selfcond_desc* d, const int32_t* tokens, const uint8_t* committed,
+                            const void* emb, const void* mask_emb, const void* w_sc, const float* pe_prev,
+                            float* x_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_sc(d);
+  if (rc) return rc;
+  DLM_REQUIRE(tokens && committed && emb && mask_emb && w_sc && x_out && ws, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(aligned16(w_sc) && aligned16(ws), DLM_ERR_ARG, "w_sc and ws must be 16-byte aligned");
+  DLM_REQUIRE(ws_bytes >= dlm_selfcond_ws_bytes(d), DLM_ERR_WORKSPACE, "workspace too small");
+  DLM_DEVICE_CHECK();
+  hipStream_t st = (hipStream_t)stream;
+  const int bf = d->dtype == DLM_BF16;
+  const size_t el = bf ? 2 : 4;
+  void* xsc = ws;
+  void* gws = (char*)ws + align_up((size_t)32 * d->d * el, 256);
+  rc = selfcond_prep(pe_prev, committed, xsc, d->rows, d->d, bf, nullptr, st);
+  if (rc) return rc;
+  EpiParams e = epi_zero();
+  e.kind = EPI_SELFCOND;
+  e.M = d->rows;
+  e.bf16_out = bf;
+  e.out = x_out;
+  e.ld_out = d->d;
+  e.mask_emb = mask_emb;
+  e.emb = emb;
+  e.tokens = tokens;
+  e.committed = committed;
+  e.vocab = d->vocab;
+  if (bf) return gemm_bf16(w_sc, xsc, d->d, d->d, MAP_IDENTITY, e, gemm_plan(d->d, d->d), gws, st);
+  F32Mats W{};
+  W.w[0] = (const float*)w_sc;
+  W.rows[0] = d->d;
+  return gemm_f32(W, (const float*)xsc, d->d, d->d, MAP_IDENTITY, e, st);
+}
+
+// ------------------------------------------------------------------ packing
+extern "C" int dlm_pack_matrix(const void* src, int n_rows, int k, const int32_t* row_map_dev, void* dst,
+                               void* stream) {
+  DLM_REQUIRE(src && dst, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(n_rows > 0 && k > 0 && n_rows % 32 == 0 && k % 32 == 0, DLM_ERR_SHAPE,
+              "n_rows %% 32 and k %% 32 must be 0");
+  DLM_REQUIRE(aligned16(src) && aligned16(dst), DLM_ERR_ARG, "16-byte alignment required");
+  DLM_DEVICE_CHECK();
+  const void* s[1] = {src};
+  int r[1] = {n_rows};
+  return pack_bf16(s, r, 1, n_rows, k, row_map_dev, dst, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ plain linear
+extern "C" size_t dlm_linear_ws_bytes(int n, int k) {
+  if (n <= 0 || k <= 0 || n % 32 || k % 32) return 0;
+  return gemm_ws_bytes(n, k, gemm_plan(n, k));
+}
+
+extern "C" int dlm_linear(const void* w_packed, const void* x, int m, int n, int k, float* y, void* ws,
+                          size_t ws_bytes, void* stream) {
+  DLM_REQUIRE(w_packed && x && y && ws, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(m >= 1 && m <= 32, DLM_ERR_SHAPE, "m must be in [1, 32]");
+  DLM_REQUIRE(n > 0 && k > 0 && n % 32 == 0 && k % 32 == 0, DLM_ERR_SHAPE, "n %% 32 and k %% 32 must be 0");
+  DLM_REQUIRE(aligned16(w_packed) && aligned16(x) && aligned16(ws), DLM_ERR_ARG, "16-byte alignment required");
+  DLM_REQUIRE(ws_bytes >= dlm_linear_ws_bytes(n, k), DLM_ERR_WORKSPACE, "workspace too small");
+  DLM_DEVICE_CHECK();
+  EpiParams e = epi_zero();
+  e.kind = EPI_STORE_F32;
+  e.M = m;
+  e.bf16_out = 1;
+  e.out = y;
+  e.ld_out = n;
+  return gemm_bf16(w_packed, x, n, k, MAP_IDENTITY, e, gemm_plan(n, k), ws, (hipStream_t)stream);
+}
+
+extern "C" int dlm_pack_activations(const void* x, int rows, int k, void* x_packed, void* stream) {
+  DLM_REQUIRE(x && x_packed, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(rows >= 1 && rows <= 32 && k > 0 && k % 32 == 0, DLM_ERR_SHAPE, "rows in [1, 32], k %% 32 == 0");
+  DLM_DEVICE_CHECK();
+  return pack_rows_bf16(x, rows, k, x_packed, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ model
+struct GraphKey {
+  std::tuple<int, float, int, int, int, const void*, const void*, const void*, const void*, const void*, const void*> t;
+  bool operator<(const GraphKey& o) const { return t < o.t; }
+};
+
+struct dlm_model {
+  dlm_model_desc d;
+  const void* emb;
+  const void* mask_emb;
+  const void* w_sc;
+  const void* final_norm;
+  std::vector<dlm_layer_weights> layers;
+  const void* packed;
+  // packed offsets (bytes)
+  size_t off_sc;
+  std::vector<size_t> off_qkv, off_o, off_gu, off_dn;
+  size_t packed_bytes;
+  GemmPlan pl_sc, pl_qkv, pl_o, pl_gu, pl_dn;
+  int n_qkv;
+  std::mutex mu;
+  std::map<GraphKey, hipGraphExec_t> graphs;
+  std::vector<hipGraph_t> graph_objs;
+  hipStream_t cap_stream = nullptr;
+};
+
+static int check_model_desc(const dlm_model_desc* d) {
+  DLM_REQUIRE(d, DLM_ERR_ARG, "desc is null");
+  DLM_REQUIRE(d->dtype == DLM_BF16 || d->dtype == DLM_F32, DLM_ERR_DTYPE, "model dtype %d", d->dtype);
+  DLM_REQUIRE(d->n_layers > 0 && d->d > 0 && d->hq > 0 && d->hkv > 0 && d->vocab > 0 && d->block > 0,
+              DLM_ERR_ARG, "non-positive size");
+  DLM_REQUIRE(d->hq % d->hkv == 0, DLM_ERR_SHAPE, "hq %% hkv != 0");
+  DLM_REQUIRE(d->head_dim == 64 || d->head_dim == 128, DLM_ERR_SHAPE, "head_dim must be 64 or 128");
+  DLM_REQUIRE(d->block <= 32, DLM_ERR_SHAPE, "block must be <= 32");
+  DLM_REQUIRE(d->d % 32 == 0 && d->d <= 4096, DLM_ERR_SHAPE, "d must be a multiple of 32, <= 4096");
+  const bool moe = d->n_experts > 0;
+  if (!moe) DLM_REQUIRE(d->ffn > 0 && d->ffn % 32 == 0, DLM_ERR_SHAPE, "ffn must be a positive multiple of 32");
+  if (moe) {
+    DLM_REQUIRE(d->dtype == DLM_BF16, DLM_ERR_DTYPE, "MoE models are bf16");
+    DLM_REQUIRE(d->top_k >= 1 && d->top_k <= 8 && d->top_k <= d->n_experts && d->n_experts <= 256,
+                DLM_ERR_SHAPE, "top_k in [1, 8], n_experts <= 256");
+    DLM_REQUIRE(d->expert_ffn % 32 == 0 && d->expert_ffn > 0 && d->n_shared >= 0 && d->n_shared <= 2,
+                DLM_ERR_SHAPE, "expert_ffn %% 32 == 0, n_shared <= 2");
+  }
+  if (d->dtype == DLM_F32) DLM_REQUIRE(d->d <= 256, DLM_ERR_SHAPE, "f32 models support d <= 256");
+  return DLM_OK;
+}
+
+static void layout_packed(dlm_model* m) {
+  const dlm_model_desc& d = m->d;
+  const int D = d.head_dim;
+  m->n_qkv = (d.hq + 2 * d.hkv) * D;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return o; };
+  m->off_sc = take((size_t)d.d * d.d * 2);
+  m->off_qkv.resize(d.n_layers);
+  m->off_o.resize(d.n_layers);
+  m->off_gu.resize(d.n_layers);
+  m->off_dn.resize(d.n_layers);
+  for (int l = 0; l < d.n_layers; ++l) {
+    m->off_qkv[l] = take((size_t)m->n_qkv * d.d * 2);
+    m->off_o[l] = take((size_t)d.d * d.hq * D * 2);
+    if (d.n_experts == 0) {
+      m->off_gu[l] = take((size_t)2 * d.ffn * d.d * 2);
+      m->off_dn[l] = take((size_t)d.d * d.ffn * 2);
+    }
+  }
+  m->packed_bytes = d.dtype == DLM_BF16 ? off : 0;
+  m->pl_sc = gemm_plan(d.d, d.d);
+  m->pl_qkv = gemm_plan(m->n_qkv, d.d);
+  m->pl_o = gemm_plan(d.d, d.hq * D);
+  if (d.n_experts == 0) {
+    m->pl_gu = gemm_plan(2 * d.ffn, d.d);
+    m->pl_dn = gemm_plan(d.d, d.ffn);
+  } else {
+    m->pl_gu = m->pl_dn = GemmPlan{1, 1};
+  }
+}
+
+extern "C" size_t dlm_packed_bytes(const dlm_model_desc* d) {
+  if (check_model_desc(d) != DLM_OK) return 0;
+  dlm_model m;
+  m.d = *d;
+  layout_packed(&m);
+  return m.packed_bytes;
+}
+
+extern "C" size_t dlm_pack_ws_bytes(const dlm_model_desc* d) {
+  if (check_model_desc(d) != DLM_OK) return 0;
+  const size_t qkv = (size_t)(d->hq + 2 * d->hkv) * d->head_dim;
+  return (qkv + 2 * (size_t)(d->ffn > 0 ? d->ffn : 0)) * 4 + 256;
+}
+
+static int check_layer(const dlm_model_desc* d, const dlm_layer_weights& L, int i) {
+  DLM_REQUIRE(L.attn_norm && L.wq && L.wk && L.wv && L.wo && L.ffn_norm, DLM_ERR_ARG,
+              "layer %d: null attention weight", i);
+  if (d->n_experts == 0)
+    DLM_REQUIRE(L.wg && L.wu && L.wd, DLM_ERR_ARG, "layer %d: null FFN weight", i);
+  else
+    DLM_REQUIRE(L.router && L.x_w13 && L.x_w13_scale && L.x_w2 && L.x_w2_scale, DLM_ERR_ARG,
+                "layer %d: null MoE weight", i);
+  return DLM_OK;
+}
+
+extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const dlm_layer_weights* layers, void* dst,
+                              void* row_map_ws, size_t ws_bytes, void* stream) {
+  int rc = check_model_desc(d);
+  if (rc) return rc;
+  DLM_REQUIRE(d->dtype == DLM_BF16, DLM_ERR_DTYPE, "only bf16 models are packed");
+  DLM_REQUIRE(w_sc && layers && dst && row_map_ws, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(ws_bytes >= dlm_pack_ws_bytes(d), DLM_ERR_WORKSPACE, "row-map workspace too small");
+  for (int i = 0; i < d->n_layers; ++i) {
+    rc = check_layer(d, layers[i], i);
+    if (rc) return rc;
+  }
+  DLM_DEVICE_CHECK();
+  dlm_model m;
+  m.d = *d;
+  layout_packed(&m);
+  hipStream_t st = (hipStream_t)stream;
+  const int D = d->head_dim;
+  std::vector<int32_t> maps((size_t)m.n_qkv + 2 * (size_t)(d->ffn > 0 ? d->ffn : 0));
+  build_row_map(MAP_QKV, m.n_qkv, d->hq, d->hkv, D, d->ffn, maps.data());
+  if (d->n_experts == 0) build_row_map(MAP_GU, 2 * d->ffn, d->hq, d->hkv, D, d->ffn, maps.data() + m.n_qkv);
+  int32_t* map_qkv = (int32_t*)row_map_ws;
+  int32_t* map_gu = map_qkv + m.n_qkv;
+  DLM_HIP(hipMemcpyAsync(row_map_ws, maps.data(), maps.size() * 4, hipMemcpyHostToDevice, st));
+  DLM_HIP(hipStreamSynchronize(st));
+  char* out = (char*)dst;
+  {
+    const void* s[1] = {w_sc};
+    int r[1] = {d->d};
+    rc = pack_bf16(s, r, 1, d->d, d->d, nullptr, out + m.off_sc, st);
+    if (rc) return rc;
+  }
+  for (int l = 0; l < d->n_layers; ++l) {
+    const dlm_layer_weights& L = layers[l];
+    const void* s3[3] = {L.wq, L.wk, L.wv};
+    int r3[3] = {d->hq * D, d->hkv * D, d->hkv * D};
+    if ((rc = pack_bf16(s3, r3, 3, m.n_qkv, d->d, map_qkv, out + m.off_qkv[l], st))) return rc;
+    const void* so[1] = {L.wo};
+    int ro[1] = {d->d};
+    if ((rc = pack_bf16(so, ro, 1, d->d, d->hq * D, nullptr, out + m.off_o[l], st))) return rc;
+    if (d->n_experts == 0) {
+      const void* s2[2] = {L.wg, L.wu};
+      int r2[2] = {d->ffn, d->ffn};
+      if ((rc = pack_bf16(s2, r2, 2, 2 * d->ffn, d->d, map_gu, out + m.off_gu[l], st))) return rc;
+      const void* sd[1] = {L.wd};
+      int rd[1] = {d->d};
+      if ((rc = pack_bf16(sd, rd, 1, d->d, d->ffn, nullptr, out + m.off_dn[l], st))) return rc;
+    }
+  }
+  return DLM_OK;
+}
+
+extern "C" int dlm_model_create(const dlm_model_desc* d, const void* emb, const void* mask_emb, const void* w_sc,
+                                const void* final_norm, const dlm_layer_weights* layers, const void* packed,
+                                dlm_model** out) {
+  int rc = check_model_desc(d);
+  if (rc) return rc;
+  DLM_REQUIRE(out, DLM_ERR_ARG, "out is null");
+  DLM_REQUIRE(emb && mask_emb && w_sc && final_norm && layers, DLM_ERR_ARG, "null model weight");
+  DLM_REQUIRE(d->dtype == DLM_F32 || packed, DLM_ERR_ARG, "bf16 models need the packed buffer");
+  for (int i = 0; i < d->n_layers; ++i) {
+    rc = check_layer(d, layers[i], i);
+    if (rc) return rc;
+  }
+  dlm_model* m = new dlm_model();
+  m->d = *d;
+  m->emb = emb;
+  m->mask_emb = mask_emb;
+  m->w_sc = w_sc;
+  m->final_norm = final_norm;
+  m->layers.assign(layers, layers + d->n_layers);
+  m->packed = packed;
+  layout_packed(m);
+  *out = m;
+  return DLM_OK;
+}
+
+extern "C" void dlm_model_destroy(dlm_model* m) {
+  if (!m) return;
+  for (auto& kv : m->graphs) hipGraphExecDestroy(kv.second);
+  for (auto g : m->graph_objs) hipGraphDestroy(g);
+  if (m->cap_stream) hipStreamDestroy(m->cap_stream);
+  delete m;
+}
+
+// ------------------------------------------------------------------ decode workspace
+struct DecodeWs {
+  float* x;
+  void* xn;
+  void* q;
+  void* o;
+  void* act;
+  void* xsc;
+  void* hn;
+  float* pe;
+  float* lse;
+  float* ent;
+  float* maxp;
+  int32_t* amax;
+  uint8_t* committed;
+  void* gemm_ws;
+  void* attn_ws;
+  void* head_ws;
+  void* moe_ws;
+  size_t total;
+};
+
+static AttnPlan model_attn_plan(const dlm_model* m, const dlm_kv* kv) {
+  return attn_plan(m->d.hq, m->d.hkv, m->d.head_dim, m->d.block, kv->max_len - m->d.block);
+}
+
+static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) {
+  const dlm_model_desc& d = m->d;
+  const size_t el = d.dtype == DLM_BF16 ? 2 : 4;
+  const int B = 32;  // buffers always hold 32 rows (the GEMM B operand reads 32)
+  const int qd = d.hq * d.head_dim;
+  const int F = d.n_experts ? d.expert_ffn : d.ffn;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return base + o; };
+  DecodeWs w;
+  w.x = (float*)take((size_t)B * d.d * 4);
+  w.xn = take((size_t)B * d.d * el);
+  w.q = take((size_t)B * qd * el);
+  w.o = take((size_t)B * qd * el);
+  w.act = take((size_t)B * F * el);
+  w.xsc = take((size_t)B * d.d * el);
+  w.hn = take((size_t)B * d.d * el);
+  w.pe = (float*)take((size_t)B * d.d * 4);
+  w.lse = (float*)take(B * 4);
+  w.ent = (float*)take(B * 4);
+  w.maxp = (float*)take(B * 4);
+  w.amax = (int32_t*)take(B * 4);
+  w.committed = (uint8_t*)take(64);
+  size_t g = 0;
+  if (d.dtype == DLM_BF16) {
+    g = std::max(g, gemm_ws_bytes(d.d, d.d, m->pl_sc));
+    g = std::max(g, gemm_ws_bytes(m->n_qkv, d.d, m->pl_qkv));
+    g = std::max(g, gemm_ws_bytes(d.d, qd, m->pl_o));
+    if (!d.n_experts) {
+      g = std::max(g, gemm_ws_bytes(2 * d.ffn, d.d, m->pl_gu));
+      g = std::max(g, gemm_ws_bytes(d.d, d.ffn, m->pl_dn));
+    }
+  }
+  w.gemm_ws = take(g + 256);
+  w.attn_ws = take(d.dtype == DLM_BF16 ? attn_ws_bytes(d.hq, d.hkv, d.head_dim, model_attn_plan(m, kv)) : 256);
+  w.head_ws = take(head_ws_bytes(d.dtype, d.block, d.d, d.vocab));
+  w.moe_ws = take(d.n_experts ? moe_ws_bytes(d) : 0);
+  w.total = off;
+  return w;
+}
+
+static int check_kv(const dlm_model* m, const dlm_kv* kv) {
+  DLM_REQUIRE(m, DLM_ERR_ARG, "model is null");
+  DLM_REQUIRE(kv && kv->k && kv->v && kv->len_dev, DLM_ERR_ARG, "kv is null");
+  DLM_REQUIRE(kv->cap > 0 && kv->max_len >= m->d.block && kv->max_len <= kv->cap, DLM_ERR_SHAPE,
+              "kv: need block <= max_len <= cap");
+  for (int l = 0; l < m->d.n_layers; ++l)
+    DLM_REQUIRE(kv->k[l] && kv->v[l] && aligned16(kv->k[l]) && aligned16(kv->v[l]), DLM_ERR_ARG,
+                "kv layer %d: null or misaligned", l);
+  return DLM_OK;
+}
+
+extern "C" size_t dlm_decode_ws_bytes(const dlm_model* m, const dlm_kv* kv) {
+  if (check_kv(m, kv) != DLM_OK) return 0;
+  return decode_layout(m, kv, nullptr).total;
+}
+
+extern "C" int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* ws, size_t ws_bytes,
+                                    dlm_decode_views* out) {
+  int rc = check_kv(m, kv);
+  if (rc) return rc;
+  DLM_REQUIRE(ws && out, DLM_ERR_ARG, "null pointer");
+  DecodeWs w = decode_layout(m, kv, (char*)ws);
+  DLM_REQUIRE(ws_bytes >= w.total, DLM_ERR_WORKSPACE, "workspace too small");
+  out->x = w.x;
+  out->hn = w.hn;
+  out->pe = w.pe;
+  out->lse = w.lse;
+  out->entropy = w.ent;
+  out->maxprob = w.maxp;
+  out->argmax = w.amax;
+  out->committed = w.committed;
+  return DLM_OK;
+}
+
+// ------------------------------------------------------------------ the forward pass
+// Runs the block's residual stream x through every layer.  last_kv_only: the last layer
+// stops after its K/V are written (commit pass).
+static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& w, const int32_t* cont,
+                          bool last_kv_only, hipStream_t st) {
+  const dlm_model_desc& d = m->d;
+  const int bf = d.dtype == DLM_BF16;
+  const int B = d.block, D = d.head_dim, qd = d.hq * D;
+  const char* pk = (const char*)m->packed;
+  int rc;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const dlm_layer_weights& L = m->layers[l];
+    const bool last = l == d.n_layers - 1;
+    if ((rc = rmsnorm(w.x, L.attn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st))) return rc;
+    EpiParams e = epi_zero();
+    e.kind = EPI_QKV_ROPE;
+    e.M = B;
+    e.bf16_out = bf;
+    e.q_out = w.q;
+    e.k_cache = kv->k[l];
+    e.v_cache = kv->v[l];
+    e.hq = d.hq;
+    e.hkv = d.hkv;
+    e.D = D;
+    e.cap = kv->cap;
+    e.len_dev = kv->len_dev;
+    e.rope_r = pow((double)d.rope_base, -2.0 / (double)D);
+    e.cont_dev = cont;
+    if (bf) rc = gemm_bf16(pk + m->off_qkv[l], w.xn, m->n_qkv, d.d, MAP_QKV, e, m->pl_qkv, w.gemm_ws, st);
+    else {
+      F32Mats W{};
+      W.w[0] = (const float*)L.wq; W.rows[0] = d.hq * D;
+      W.w[1] = (const float*)L.wk; W.rows[1] = d.hkv * D;
+      W.w[2] = (const float*)L.wv; W.rows[2] = d.hkv * D;
+      rc = gemm_f32(W, (const float*)w.xn, m->n_qkv, d.d, MAP_QKV, e, st);
+    }
+    if (rc) return rc;
+    if (last && last_kv_only) break;
+    const float scale = 1.0f / sqrtf((float)D);
+    if (bf) rc = attn_bf16(w.q, kv->k[l], kv->v[l], w.o, d.hq, d.hkv, D, B, kv->cap, scale, kv->len_dev, 0, cont,
+                           model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st);
+    else rc = attn_f32((const float*)w.q, (const float*)kv->k[l], (const float*)kv->v[l], (float*)w.o, d.hq, d.hkv,
+                       D, B, kv->cap, scale, kv->len_dev, 0, cont, st);
+    if (rc) return rc;
+    e = epi_zero();
+    e.kind = EPI_RESID;
+    e.M = B;
+    e.bf16_out = bf;
+    e.out = w.x;
+    e.ld_out = d.d;
+    e.cont_dev = cont;
+    if (bf) rc = gemm_bf16(pk + m->off_o[l], w.o, d.d, qd, MAP_IDENTITY, e, m->pl_o, w.gemm_ws, st);
+    else {
+      F32Mats W{};
+      W.w[0] = (const float*)L.wo; W.rows[0] = d.d;
+      rc = gemm_f32(W, (const float*)w.o, d.d, qd, MAP_IDENTITY, e, st);
+    }
+    if (rc) return rc;
+    if ((rc = rmsnorm(w.x, L.ffn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st))) return rc;
+    if (d.n_experts) {
+      if ((rc = moe_ffn(d, L, w.xn, w.x, B, w.moe_ws, cont, st))) return rc;
+      continue;
+    }
+    e = epi_zero();
+    e.kind = EPI_SWIGLU;
+    e.M = B;
+    e.bf16_out = bf;
+    e.act_out = w.act;
+    e.F = d.ffn;
+    e.cont_dev = cont;
+    if (bf) rc = gemm_bf16(pk + m->off_gu[l], w.xn, 2 * d.ffn, d.d, MAP_GU, e, m->pl_gu, w.gemm_ws, st);
+    else {
+      F32Mats W{};
+      W.w[0] = (const float*)L.wg; W.rows[0] = d.ffn;
+      W.w[1] = (const float*)L.wu; W.rows[1] = d.ffn;
+      rc = gemm_f32(W, (const float*)w.xn, 2 * d.ffn, d.d, MAP_GU, e, st);
+    }
+    if (rc) return rc;
+    e = epi_zero();
+    e.kind = EPI_RESID;
+    e.M = B;
+    e.bf16_out = bf;
+    e.out = w.x;
+    e.ld_out = d.d;
+    e.cont_dev = cont;
+    if (bf) rc = gemm_bf16(pk + m->off_dn[l], w.act, d.d, d.ffn, MAP_IDENTITY, e, m->pl_dn, w.gemm_ws, st);
+    else {
+      F32Mats W{};
+      W.w[0] = (const float*)L.wd; W.rows[0] = d.d;
+      rc = gemm_f32(W, (const float*)w.act, d.d, d.ffn, MAP_IDENTITY, e, st);
+    }
+    if (rc) return rc;
+  }
+  return DLM_OK;
+}
+
+static int enqueue_round(const dlm_model* m, const dlm_commit_rule& rule, const dlm_kv* kv, int32_t* tokens,
+                         dlm_round_state* state, const DecodeWs& w, hipStream_t st) {
+  const dlm_model_desc& d = m->d;
+  const int bf = d.dtype == DLM_BF16;
+  const int B = d.block;
+  const int32_t* cont = &state->cont;
+  int rc;
+  // round input: E[tok] for committed rows, mask + W_sc bf(pe) for open rows
+  if ((rc = selfcond_prep(w.pe, w.committed, w.xsc, B, d.d, bf, cont, st))) return rc;
+  EpiParams e = epi_zero();
+  e.kind = EPI_SELFCOND;
+  e.M = B;
+  e.bf16_out = bf;
+  e.out = w.x;
+  e.ld_out = d.d;
+  e.mask_emb = m->mask_emb;
+  e.emb = m->emb;
+  e.tokens = tokens;
+  e.committed = w.committed;
+  e.vocab = d.vocab;
+  e.cont_dev = cont;
+  if (bf) rc = gemm_bf16((const char*)m->packed + m->off_sc, w.xsc, d.d, d.d, MAP_IDENTITY, e, m->pl_sc,
+                         w.gemm_ws, st);
+  else {
+    F32Mats W{};
+    W.w[0] = (const float*)m->w_sc;
+    W.rows[0] = d.d;
+    rc = gemm_f32(W, (const float*)w.xsc, d.d, d.d, MAP_IDENTITY, e, st);
+  }
+  if (rc) return rc;
+  if ((rc = enqueue_layers(m, kv, w, cont, false, st))) return rc;
+  if ((rc = rmsnorm(w.x, m->final_norm, w.hn, B, d.d, bf, 0, d.eps, cont, st))) return rc;
+  if ((rc = head_launch(d.dtype, w.hn, m->emb, w.committed, B, d.d, d.vocab, w.lse, w.ent, w.maxp, w.amax, w.pe,
+                        nullptr, w.head_ws, cont, st)))
+    return rc;
+  return commit_launch(rule, B, w.maxp, w.amax, w.lse, w.ent, w.committed, tokens, state, st);
+}
+
+static int enqueue_commit_pass(const dlm_model* m, const dlm_kv* kv, const int32_t* tokens, const DecodeWs& w,
+                               hipStream_t st) {
+  const dlm_model_desc& d = m->d;
+  int rc;
+  if ((rc = embed(tokens, m->emb, w.x, d.block, d.d, d.vocab, d.dtype == DLM_BF16, st))) return rc;
+  if ((rc = enqueue_layers(m, kv, w, nullptr, true, st))) return rc;
+  return len_add(kv->len_dev, d.block, st);
+}
+
+static int n_rounds(const dlm_model* m, const dlm_commit_rule& r) {
+  if (r.mode == DLM_COMMIT_FIXED_K) {
+    const int n = (m->d.block + r.k - 1) / r.k;
+    return n < r.max_rounds ? n : r.max_rounds;
+  }
+  return r.max_rounds;
+}
+
+static int enqueue_block(const dlm_model* m, const dlm_commit_rule& rule, const dlm_kv* kv, int32_t* tokens,
+                         dlm_round_state* state, const DecodeWs& w, hipStream_t st) {
+  int rc;
+  if ((rc = block_reset(m->d.block, w.committed, tokens, state, w.pe, 32 * m->d.d, st))) return rc;
+  const int R = n_rounds(m, rule);
+  for (int r = 0; r < R; ++r)
+    if ((rc = enqueue_round(m, rule, kv, tokens, state, w, st))) return rc;
+  return enqueue_commit_pass(m, kv, tokens, w, st);
+}
+
+static int check_decode(const dlm_model* m, const dlm_kv* kv, void* ws, size_t ws_bytes) {
+  int rc = check_kv(m, kv);
+  if (rc) return rc;
+  DLM_REQUIRE(ws && aligned16(ws), DLM_ERR_ARG, "workspace null or misaligned");
+  DLM_REQUIRE(ws_bytes >= decode_layout(m, kv, nullptr).total, DLM_ERR_WORKSPACE, "workspace too small");
+  return DLM_OK;
+}
+
+extern "C" int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv, int32_t* tokens,
+                                dlm_round_state* state, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_rule(rule))) return rc;
+  DLM_REQUIRE(tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_DEVICE_CHECK();
+  dlm_model* mm = const_cast<dlm_model*>(m);
+  DecodeWs w = decode_layout(m, kv, (char*)ws);
+  hipStream_t st = (hipStream_t)stream;
+  GraphKey key;
+  const void* kv0 = kv->k[0];
+  key.t = std::make_tuple(rule->mode, rule->tau, rule->k, rule->forced_top1, rule->max_rounds, (const void*)tokens,
+                          (const void*)state, ws, kv0, (const void*)kv->len_dev, (const void*)kv->v[0]);
+  std::lock_guard<std::mutex> lock(mm->mu);
+  auto it = mm->graphs.find(key);
+  if (it == mm->graphs.end()) {
+    if (!mm->cap_stream) DLM_HIP(hipStreamCreateWithFlags(&mm->cap_stream, hipStreamNonBlocking));
+    DLM_HIP(hipStreamBeginCapture(mm->cap_stream, hipStreamCaptureModeThreadLocal));
+    rc = enqueue_block(m, *rule, kv, tokens, state, w, mm->cap_stream);
+    hipGraph_t g = nullptr;
+    hipError_t e2 = hipStreamEndCapture(mm->cap_stream, &g);
+    if (rc) {
+      if (g) hipGraphDestroy(g);
+      return rc;
+    }
+    if (e2 != hipSuccess) return check_hip(e2, "hipStreamEndCapture");
+    hipGraphExec_t ex = nullptr;
+    hipError_t e3 = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    if (e3 != hipSuccess) {
+      hipGraphDestroy(g);
+      return check_hip(e3, "hipGraphInstantiate");
+    }
+    mm->graph_objs.push_back(g);
+    it = mm->graphs.emplace(key, ex).first;
+  }
+  return check_hip(hipGraphLaunch(it->second, st), "hipGraphLaunch");
+}
+
+extern "C" int dlm_decode_begin(const dlm_model* m, const dlm_kv* kv, int32_t* tokens, dlm_round_state* state,
+                                void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  DLM_REQUIRE(tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_DEVICE_CHECK();
+  DecodeWs w = decode_layout(m, kv, (char*)ws);
+  return block_reset(m->d.block, w.committed, tokens, state, w.pe, 32 * m->d.d, (hipStream_t)stream);
+}
+
+extern "C" int dlm_decode_round(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv, int32_t* tokens,
+                                dlm_round_state* state, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_rule(rule))) return rc;
+  DLM_REQUIRE(tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_DEVICE_CHECK();
+  DecodeWs w = decode_layout(m, kv, (char*)ws);
+  return enqueue_round(m, *rule, kv, tokens, state, w, (hipStream_t)stream);
+}
+
+extern "C" int dlm_commit_pass(const dlm_model* m, const dlm_kv* kv, const int32_t* tokens, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  DLM_REQUIRE(tokens, DLM_ERR_ARG, "null tokens");
+  DLM_DEVICE_CHECK();
+  DecodeWs w = decode_layout(m, kv, (char*)ws);
+  return enqueue_commit_pass(m, kv, tokens, w, (hipStream_t)stream);
+}
+
+extern "C" int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  DLM_REQUIRE(ids, DLM_ERR_ARG, "null ids");
+  DLM_REQUIRE(n >= 0 && n % m->d.block == 0, DLM_ERR_SHAPE, "n must be a multiple of the block size");
+  DLM_DEVICE_CHECK();
+  DecodeWs w = decode_layout(m, kv, (char*)ws);
+  for (int b = 0; b < n / m->d.block; ++b)
+    if ((rc = enqueue_commit_pass(m, kv, ids + (size_t)b * m->d.block, w, (hipStream_t)stream))) return rc;
+  return DLM_OK;
+}

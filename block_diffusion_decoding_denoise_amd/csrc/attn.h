@@ -1,0 +1,21 @@
+// Block attention (prefix + bidirectional block) -- internal interface.
+#pragma once
+#include "common.h"
+
+namespace dlm {
+
+struct AttnPlan {
+  int chunk;       // keys per split (multiple of 32)
+  int nsplit_max;  // splits per kv head at the largest prefix
+};
+
+AttnPlan attn_plan(int hq, int hkv, int D, int B, int max_len);
+size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl);
+int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, int hkv, int D,
+              int B, int cap, float scale, const int32_t* len_dev, int len_host,
+              const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st);
+int attn_f32(const float* q, const float* k, const float* v, float* out, int hq, int hkv, int D,
+             int B, int cap, float scale, const int32_t* len_dev, int len_host,
+             const int32_t* cont_dev, hipStream_t st);
+
+}  // namespace dlm

@@ -1,0 +1,77 @@
+// Skinny GEMM (M = block rows <= 32) with fused epilogues -- internal interface.
+#pragma once
+#include "common.h"
+
+namespace dlm {
+
+enum EpiKind {
+  EPI_STORE_F32 = 0,   // out[m][n] = acc
+  EPI_RESID = 1,       // out[m][n] += acc            (residual stream, f32)
+  EPI_QKV_ROPE = 2,    // q/k rotated at position L + m, q -> q_out, k/v -> caches at row L + m
+  EPI_SWIGLU = 3,      // act[m][j] = silu(gate_j) * up_j
+  EPI_SELFCOND = 4,    // out[m][n] = committed[m] ? E[tok[m]][n] : mask[n] + acc
+};
+
+// Logical row orders of the fused matrices (packed row order is described in gemm.hip):
+//   QKV: rows [0, hq*D) = Wq, then Wk (hkv*D rows), then Wv (hkv*D rows).
+//   GU:  rows [0, F) = Wg, then Wu.
+enum RowMapKind { MAP_IDENTITY = 0, MAP_QKV = 1, MAP_GU = 2 };
+
+struct EpiParams {
+  int kind;
+  int M;                  // valid activation rows
+  int bf16_out;           // activations / caches are bf16 (else f32)
+  // f32 outputs
+  float* out;             // STORE_F32 / RESID / SELFCOND: [M, ld_out]
+  int ld_out;
+  // QKV
+  void* q_out;            // [M, hq*D]
+  void* k_cache;          // [hkv, cap, D]
+  void* v_cache;
+  int hq, hkv, D, cap;
+  const int32_t* len_dev; // prefix length L (device) ...
+  int len_host;           // ... or host value when len_dev == nullptr
+  double rope_r;          // base^(-2/D)
+  // SWIGLU
+  void* act_out;          // [M, F]
+  int F;
+  // SELFCOND
+  const void* mask_emb;   // [d] (model dtype)
+  const void* emb;        // [V, d]
+  const int32_t* tokens;
+  const uint8_t* committed;
+  int vocab;
+  // predication: when non-null and *cont_dev == 0 the kernel does nothing
+  const int32_t* cont_dev;
+};
+
+struct GemmPlan {
+  int tpw;      // (unused, 1)
+  int splits;   // number of stream-K workers (waves)
+};
+
+// Packed-row -> logical-row map used when packing (host side).
+void build_row_map(int kind, int n_rows, int hq, int hkv, int D, int F, int32_t* out);
+
+// bf16 path.  W: packed [N, K] (N % 32 == 0, K % 16 == 0); X: bf16 32 x K in the packed
+// operand order (xpk_index; rows >= M are read but ignored).  The SwiGLU epilogue writes its
+// bf16 output in the same packed order (it feeds the down projection).
+// partial/counters: workspace (counters zero before the first use; left zero).
+size_t gemm_ws_bytes(int N, int K, GemmPlan plan);
+GemmPlan gemm_plan(int N, int K);
+int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const EpiParams& ep,
+              GemmPlan plan, void* ws, hipStream_t st);
+
+// f32 path (natural [out, in] weights).  Up to 3 source matrices make the logical rows.
+struct F32Mats {
+  const float* w[3];
+  int rows[3];
+};
+int gemm_f32(const F32Mats& W, const float* X, int N, int K, int map_kind, const EpiParams& ep,
+             hipStream_t st);
+
+// Pack rows row_map[i] of the virtual concatenation of up to 3 bf16 matrices into dst.
+int pack_bf16(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
+              const int32_t* row_map_dev, void* dst, hipStream_t st);
+
+}  // namespace dlm

@@ -1,0 +1,442 @@
+// Skinny GEMMs of the denoising round: C[m][n] = sum_k X[m][k] W[n][k] for the block's
+// M <= 32 rows, with the consumer of C fused into the epilogue (RoPE + KV-cache write,
+// SwiGLU, residual add, self-conditioning input).
+//
+// bf16 path (matrix cores).  W is packed once at model load: 32-row tile t, 16-column step
+// kt is one contiguous 1 KiB run in which lane l's 16 bytes are
+// W[row(32t + l%32)][16kt + 8(l/32) .. +8] -- the A operand of v_mfma_f32_32x32x16_bf16.
+// The packed matrix is therefore one contiguous stream of (tile, step) units, and the kernel
+// is stream-K over it: worker (wave) w owns the contiguous unit range
+// [w T / NW, (w+1) T / NW) of the T = tiles x steps units, so every worker streams the same
+// number of bytes with 1 KiB loads and no tile-count tail.  Each wave keeps a ring of P
+// steps in flight (buffer loads, which return zeros past the range, so the ring runs without
+// branches); the block's activations (bf16, 32 x K, L2-resident) are the B operand (32 rows
+// in one MFMA), stored in the packed operand order so each fragment is one contiguous 1 KiB.  When a worker finishes a tile segment it runs the epilogue straight from its
+// accumulator registers if it owned the whole tile, else it stores a partial and the last
+// contributor of the tile (agent-scope counter) adds the partials in contributor order, so
+// results are deterministic.  Partials are handed over with coherent stores and loads, never
+// with whole-L2 fences.
+//
+// Row orders of fused matrices (packed row p, tile t = p/32, r = p%32):
+//   QKV: q and k heads hold rotate-half pairs side by side, p = 2i -> j = 16t'+i,
+//        p = 2i+1 -> j + D/2 (t' = tile within the head), so RoPE is applied to a pair of
+//        accumulators held by one lane; v rows keep their order.
+//   GU:  p = 2i -> gate row 16t + i, p = 2i+1 -> up row 16t + i, so SwiGLU takes a pair.
+#include "gemm.h"
+
+#include <vector>
+
+namespace dlm {
+
+// ------------------------------------------------------------------ row maps
+__host__ __device__ inline int qkv_logical(int prow, int hq, int hkv, int D) {
+  const int Nq = hq * D, Nk = hkv * D;
+  if (prow >= Nq + Nk) return prow;
+  const int base = prow < Nq ? 0 : Nq;
+  const int rel = prow - base;
+  const int head = rel / D, within = rel % D;
+  const int t = within / 32, r = within % 32;
+  return base + head * D + 16 * t + r / 2 + (r % 2) * (D / 2);
+}
+
+__host__ __device__ inline int gu_logical(int prow, int F) {
+  const int t = prow / 32, r = prow % 32;
+  return (r % 2) * F + 16 * t + r / 2;
+}
+
+void build_row_map(int kind, int n_rows, int hq, int hkv, int D, int F, int32_t* out) {
+  for (int p = 0; p < n_rows; ++p) {
+    if (kind == MAP_QKV) out[p] = qkv_logical(p, hq, hkv, D);
+    else if (kind == MAP_GU) out[p] = gu_logical(p, F);
+    else out[p] = p;
+  }
+}
+
+// ------------------------------------------------------------------ epilogues
+__device__ inline int prefix_len(const EpiParams& e) {
+  return e.len_dev ? *e.len_dev : e.len_host;
+}
+
+__device__ inline void store_act(void* base, size_t idx, float v, int bf16) {
+  if (bf16) ((uint16_t*)base)[idx] = f2bf(v);
+  else ((float*)base)[idx] = v;
+}
+
+__device__ inline float load_act(const void* base, size_t idx, int bf16) {
+  return bf16 ? bf2f(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
+}
+
+// single logical output n of row m (identity-mapped kinds)
+__device__ inline void epi_single(const EpiParams& e, int m, int n, float v) {
+  const size_t o = (size_t)m * e.ld_out + n;
+  switch (e.kind) {
+    case EPI_STORE_F32: e.out[o] = v; break;
+    case EPI_RESID: e.out[o] += v; break;
+    case EPI_SELFCOND: {
+      if (e.committed[m]) {
+        int tok = e.tokens[m];
+        tok = (tok < 0 || tok >= e.vocab) ? 0 : tok;   // ids are in range unless the caller broke them
+        e.out[o] = load_act(e.emb, (size_t)tok * e.ld_out + n, e.bf16_out);
+      }
+      else e.out[o] = load_act(e.mask_emb, n, e.bf16_out) + v;
+      break;
+    }
+    default: break;
+  }
+}
+
+// rotate-half RoPE of the pair (j, j + D/2) of a q (part 0) or k (part 1) head.  The angle
+// pos * base^(-2j/D) is formed in double (base^(-2j/D) = r^j with r = base^(-2/D) from the
+// host, by repeated squaring) and reduced to [-pi, pi] in double; only the final sine and
+// cosine of the reduced angle are single precision.
+__device__ inline double ipow(double r, int j) {
+  double out = 1.0;
+  while (j) {
+    if (j & 1) out *= r;
+    r *= r;
+    j >>= 1;
+  }
+  return out;
+}
+
+__device__ inline void epi_qk_rope(const EpiParams& e, int m, int part, int head, int j, float a,
+                                   float b) {
+  const int L = prefix_len(e);
+  const int pos = L + m;
+  const double ang = (double)pos * ipow(e.rope_r, j);
+  const double two_pi = 6.283185307179586476925286766559;
+  const double red = fma(-rint(ang / two_pi), two_pi, ang);
+  float sn, cs;
+  __sincosf((float)red, &sn, &cs);
+  const float a2 = a * cs - b * sn;
+  const float b2 = b * cs + a * sn;
+  if (part == 0) {
+    const size_t o = (size_t)m * e.hq * e.D + (size_t)head * e.D + j;
+    // (q rows are always in range; cache rows are guarded below)
+    store_act(e.q_out, o, a2, e.bf16_out);
+    store_act(e.q_out, o + e.D / 2, b2, e.bf16_out);
+  } else {
+    if (L + m >= e.cap) return;   // a prefix length past the cache capacity writes nothing
+    const size_t o = ((size_t)head * e.cap + (L + m)) * e.D + j;
+    store_act(e.k_cache, o, a2, e.bf16_out);
+    store_act(e.k_cache, o + e.D / 2, b2, e.bf16_out);
+  }
+}
+
+__device__ inline void epi_v(const EpiParams& e, int m, int rel, float v) {
+  const int L = prefix_len(e);
+  if (L + m >= e.cap) return;
+  const int head = rel / e.D, j = rel % e.D;
+  store_act(e.v_cache, ((size_t)head * e.cap + (L + m)) * e.D + j, v, e.bf16_out);
+}
+
+__device__ inline void epi_swiglu(const EpiParams& e, int m, int j, float g, float u) {
+  const float s = g / (1.0f + expf(-g));
+  store_act(e.act_out, e.bf16_out ? xpk_index(m, j) : (size_t)m * e.F + j, s * u, e.bf16_out);
+}
+
+// pair of packed rows (p, p+1), p even
+__device__ inline void epi_pair_packed(const EpiParams& e, int map, int p, int m, float a, float b) {
+  if (map == MAP_QKV) {
+    const int Nq = e.hq * e.D, Nk = e.hkv * e.D;
+    if (p < Nq + Nk) {
+      const int first = qkv_logical(p, e.hq, e.hkv, e.D);
+      const int part = first < Nq ? 0 : 1;
+      const int rel = first - (part ? Nq : 0);
+      epi_qk_rope(e, m, part, rel / e.D, rel % e.D, a, b);
+    } else {
+      epi_v(e, m, p - Nq - Nk, a);
+      epi_v(e, m, p + 1 - Nq - Nk, b);
+    }
+  } else if (map == MAP_GU) {
+    epi_swiglu(e, m, gu_logical(p, e.F), a, b);
+  } else {
+    epi_single(e, m, p, a);
+    epi_single(e, m, p + 1, b);
+  }
+}
+
+// ------------------------------------------------------------------ bf16 kernel
+struct GemmP {
+  const uint16_t* W;
+  const uint16_t* X;
+  int K, KT, tiles, NW, cmax, map;
+  float* partial;    // [tiles][cmax][16][64]
+  int* counters;     // [tiles]
+  EpiParams ep;
+};
+
+// workgroup owning unit s when workgroup g owns [floor(g T / NW), floor((g+1) T / NW))
+__device__ inline int owner_of(long long s, long long T, int NW) {
+  return (int)(((s + 1) * NW - 1) / T);
+}
+
+__device__ inline void epilogue_quarter(const GemmP& p, int t, const float (&v4)[4], int wave, int lane) {
+  const int m = lane & 31;
+  if (m >= p.ep.M) return;
+#pragma unroll
+  for (int q = 0; q < 4; q += 2) {
+    const int r = 4 * wave + q;
+    const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+    epi_pair_packed(p.ep, p.map, t * 32 + row, m, v4[q], v4[q + 1]);
+  }
+}
+
+// A workgroup is one stream-K worker: it owns the contiguous unit range [s0, s1) (at most K/16
+// units, so at most two tiles); its 4 waves take every 4th unit of it, then the wave results
+// are added in LDS (fixed order).  A tile the workgroup owns entirely gets its epilogue here;
+// otherwise the workgroup stores its partial and the last contributor of the tile adds all
+// partials in contributor order.
+template <int P>
+__global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmP p) {
+  if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
+  __shared__ float red[4][2][16][64];
+  __shared__ int s_last[2];
+  const int lane = threadIdx.x & 63;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.x;
+  const long long T = (long long)p.tiles * p.KT;
+  const int s0 = (int)((long long)g * T / p.NW), s1 = (int)((long long)(g + 1) * T / p.NW);
+  const int n = s1 - s0;
+  const int nv = (n - v + 3) / 4;             // units of this wave: WG units v, v+4, ...
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.W + (size_t)s0 * 512, (uint32_t)n * 1024u);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, (uint32_t)(32 * p.K * 2));
+  const uint32_t wo = (uint32_t)lane * 16u;
+  const uint32_t xo = (uint32_t)lane * 16u;
+  u32x4_t wf[P], xf[P];
+  int kpf = (s0 + v) % p.KT;   // step-in-tile of the next unit this wave prefetches
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    wf[u] = bload16(wr, wo + (uint32_t)(v + 4 * u) * 1024u);
+    xf[u] = bload16(xr, xo + (uint32_t)kpf * 1024u);
+    kpf += 4;
+    if (kpf >= p.KT) kpf %= p.KT;
+  }
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // the WG's units [0, bnd) belong to tile t0, [bnd, n) to tile t0 + 1 (a WG owns at most K/16
+  // units); this wave's first unit of tile t0 + 1 is its ring step kb
+  const int t0 = s0 / p.KT;
+  const int bnd = min(n, (t0 + 1) * p.KT - s0);
+  const int kb = bnd > v ? (bnd - v + 3) / 4 : 0;
+  int seg = kb == 0 ? 1 : 0;
+  if (kb == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[v][0][r][lane] = 0.f;
+  }
+  // streaming loop: no stores to global memory inside, so the ring's memory-counter waits
+  // stay exact; the switch to the second tile parks the accumulator in LDS
+  for (int k0 = 0; k0 < nv; k0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      if (k0 + u == kb && seg == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          red[v][0][r][lane] = acc[r];
+          acc[r] = 0.f;
+        }
+        seg = 1;
+      }
+      acc = mfma32x32x16(wf[u], xf[u], acc);
+      wf[u] = bload16(wr, wo + (uint32_t)(v + 4 * (k0 + u + P)) * 1024u);
+      xf[u] = bload16(xr, xo + (uint32_t)kpf * 1024u);
+      kpf += 4;
+      if (kpf >= p.KT) kpf %= p.KT;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    red[v][seg][r][lane] = acc[r];
+    if (seg == 0) red[v][1][r][lane] = 0.f;
+  }
+  __syncthreads();
+  const int nseg = bnd < n ? 2 : 1;
+  bool need[2] = {false, false};
+  int cnt[2] = {1, 1};
+  for (int sg = 0; sg < nseg; ++sg) {
+    float sums[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * v + q;
+      sums[q] = ((red[0][sg][r][lane] + red[1][sg][r][lane]) + red[2][sg][r][lane]) + red[3][sg][r][lane];
+    }
+    const int t = t0 + sg;
+    const int fo = owner_of((long long)t * p.KT, T, p.NW), lo = owner_of((long long)(t + 1) * p.KT - 1, T, p.NW);
+    cnt[sg] = lo - fo + 1;
+    if (cnt[sg] == 1) {
+      epilogue_quarter(p, t, sums, v, lane);
+    } else {
+      need[sg] = true;
+      float* dst = p.partial + ((size_t)t * p.cmax + (g - fo)) * 1024;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_coherent(&dst[(4 * v + q) * 64 + lane], sums[q]);
+    }
+  }
+  if (!need[0] && !need[1]) return;
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int sg = threadIdx.x;
+    s_last[sg] = need[sg] ? (atomic_add_agent(&p.counters[t0 + sg], 1) == cnt[sg] - 1) : 0;
+  }
+  __syncthreads();
+  for (int sg = 0; sg < nseg; ++sg) {
+    if (!s_last[sg]) continue;
+    const int t = t0 + sg;
+    const float* base = p.partial + (size_t)t * p.cmax * 1024;
+    float tot[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < cnt[sg]; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[q] += load_coherent(&base[(size_t)j * 1024 + (4 * v + q) * 64 + lane]);
+    if (threadIdx.x == 0) store_agent(&p.counters[t], 0);
+    epilogue_quarter(p, t, tot, v, lane);
+  }
+}
+
+GemmPlan gemm_plan(int N, int K) {
+  GemmPlan pl;
+  const long long T = (long long)(N / 32) * (K / 16);
+  long long nw = T / 96;                 // about 96 KiB of weights per workgroup
+  if (nw < 256) nw = T / 48;
+  if (nw < 256) nw = 256;
+  if (nw < N / 32) nw = N / 32;          // at most K/16 units per workgroup: <= 2 tiles
+  if (nw > T) nw = T;                    // every workgroup owns at least one unit
+  pl.tpw = 1;
+  pl.splits = (int)nw;                   // number of stream-K workgroups
+  return pl;
+}
+
+static int gemm_cmax(int N, int K, int nw) {
+  const long long T = (long long)(N / 32) * (K / 16);
+  const long long minsteps = T / nw > 0 ? T / nw : 1;
+  return (int)((K / 16) / minsteps + 2);
+}
+
+// Workspace: a fixed block of per-tile counters at the start (shared by every GEMM that uses
+// the same workspace; each GEMM leaves its counters at zero), then the partial sums.
+constexpr int kMaxTiles = 4096;
+constexpr size_t kCounterBytes = kMaxTiles * 4;
+
+size_t gemm_ws_bytes(int N, int K, GemmPlan plan) {
+  const size_t part = (size_t)(N / 32) * gemm_cmax(N, K, plan.splits) * 1024 * 4;
+  return kCounterBytes + align_up(part, 256);
+}
+
+int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const EpiParams& ep,
+              GemmPlan plan, void* ws, hipStream_t st) {
+  GemmP p;
+  p.W = (const uint16_t*)W;
+  p.X = (const uint16_t*)X;
+  p.K = K;
+  p.KT = K / 16;
+  p.tiles = N / 32;
+  p.NW = plan.splits;
+  p.cmax = gemm_cmax(N, K, plan.splits);
+  p.map = map_kind;
+  if (p.tiles > kMaxTiles) return fail(DLM_ERR_SHAPE, "gemm: %d tiles exceed %d", p.tiles, kMaxTiles);
+  p.counters = (int*)ws;
+  p.partial = (float*)((char*)ws + kCounterBytes);
+  p.ep = ep;
+  hipLaunchKernelGGL(gemm_bf16_kernel<8>, dim3(p.NW), dim3(256), 0, st, p);
+  return check_hip(hipGetLastError(), "gemm_bf16 launch");
+}
+
+// ------------------------------------------------------------------ f32 kernel
+struct F32P {
+  F32Mats W;
+  const float* X;
+  int N, K, map, units;
+  EpiParams ep;
+};
+
+
+__device__ inline float dot_row(const F32P& p, int n, const float* x) {
+  int r = n, i = 0;
+  while (i < 2 && r >= p.W.rows[i]) { r -= p.W.rows[i]; ++i; }
+  const float* w = p.W.w[i] + (size_t)r * p.K;
+  float acc = 0.f;
+  for (int k = 0; k < p.K; ++k) acc = fmaf(x[k], w[k], acc);
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void gemm_f32_kernel(F32P p) {
+  if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int m = idx / p.units, u = idx % p.units;
+  if (m >= p.ep.M) return;
+  const float* x = p.X + (size_t)m * p.K;
+  const EpiParams& e = p.ep;
+  if (p.map == MAP_QKV) {
+    const int Nq = e.hq * e.D, Nk = e.hkv * e.D;
+    const int pairs = (Nq + Nk) / 2;
+    if (u < pairs) {
+      const int part = u < Nq / 2 ? 0 : 1;
+      const int rel = u - (part ? Nq / 2 : 0);
+      const int head = rel / (e.D / 2), j = rel % (e.D / 2);
+      const int first = (part ? Nq : 0) + head * e.D + j;
+      epi_qk_rope(e, m, part, head, j, dot_row(p, first, x), dot_row(p, first + e.D / 2, x));
+    } else {
+      const int rel = u - pairs;
+      epi_v(e, m, rel, dot_row(p, Nq + Nk + rel, x));
+    }
+  } else if (p.map == MAP_GU) {
+    epi_swiglu(e, m, u, dot_row(p, u, x), dot_row(p, e.F + u, x));
+  } else {
+    epi_single(e, m, u, dot_row(p, u, x));
+  }
+}
+
+int gemm_f32(const F32Mats& W, const float* X, int N, int K, int map_kind, const EpiParams& ep,
+             hipStream_t st) {
+  F32P p;
+  p.W = W;
+  p.X = X;
+  p.N = N;
+  p.K = K;
+  p.map = map_kind;
+  if (map_kind == MAP_QKV) p.units = (ep.hq * ep.D + ep.hkv * ep.D) / 2 + ep.hkv * ep.D;
+  else if (map_kind == MAP_GU) p.units = N / 2;
+  else p.units = N;
+  p.ep = ep;
+  const int total = ep.M * p.units;
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3((total + 255) / 256), dim3(256), 0, st, p);
+  return check_hip(hipGetLastError(), "gemm_f32 launch");
+}
+
+// ------------------------------------------------------------------ packing
+struct PackP {
+  const uint16_t* src[3];
+  int rows[3];
+  int n_src, k, KT;
+  const int32_t* map;
+  uint16_t* dst;
+};
+
+__global__ __launch_bounds__(64) void pack_kernel(PackP p) {
+  const int t = blockIdx.x / p.KT, kt = blockIdx.x % p.KT, lane = threadIdx.x;
+  int row = p.map ? p.map[t * 32 + (lane & 31)] : t * 32 + (lane & 31);
+  int i = 0;
+  while (i < p.n_src - 1 && row >= p.rows[i]) { row -= p.rows[i]; ++i; }
+  const uint16_t* s = p.src[i] + (size_t)row * p.k + kt * 16 + 8 * (lane >> 5);
+  u32x4_t v = *(const u32x4_t*)s;
+  *(u32x4_t*)(p.dst + ((size_t)blockIdx.x * 64 + lane) * 8) = v;
+}
+
+int pack_bf16(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
+              const int32_t* row_map_dev, void* dst, hipStream_t st) {
+  PackP p;
+  for (int i = 0; i < 3; ++i) {
+    p.src[i] = i < n_src ? (const uint16_t*)srcs[i] : nullptr;
+    p.rows[i] = i < n_src ? src_rows[i] : 0;
+  }
+  p.n_src = n_src;
+  p.k = k;
+  p.KT = k / 16;
+  p.map = row_map_dev;
+  p.dst = (uint16_t*)dst;
+  hipLaunchKernelGGL(pack_kernel, dim3((n_rows / 32) * p.KT), dim3(64), 0, st, p);
+  return check_hip(hipGetLastError(), "pack launch");
+}
+
+}  // namespace dlm

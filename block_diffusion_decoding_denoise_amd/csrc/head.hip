@@ -1,0 +1,437 @@
+// Tied-embedding head with fused row statistics and the p.E feedback mix.
+//
+// For the open rows h_i of the block: l = h_i E^T over the whole vocabulary, then
+// lse, entropy, max-prob, argmax and pe_i = sum_v softmax(l)_v E_v, with the logits never
+// stored (page "ORL: diffusion LLMs get a learnable 'tokens per forward'", section "What
+// shipped": per-round distribution over unresolved tokens, self-conditioning on the tied
+// embedding; "QwenDLM-4B-ORL" model card, evaluation pipeline: fused row statistics).
+//
+// bf16 path: one workgroup of NW waves per (vocabulary chunk, group of 16 open rows).
+// Wave w owns the d-slice [w d/NW, (w+1) d/NW): it keeps the rows' slice of h and its
+// slice of the p.E accumulator in registers for the whole kernel.  Per tile of 16 vocabulary
+// rows: (1) each wave streams its slice of the tile's E rows from HBM (prefetched one tile
+// ahead) and forms partial logits with v_mfma_f32_16x16x32_bf16 (A = E rows, B = h rows);
+// (2) the NW partials are summed through LDS in a fixed order and 256 threads update the
+// online statistics per row (running max, sum of e^(l-m), sum of e^(l-m)(l-m) for the
+// entropy, argmax with lowest-id ties) and publish p = e^(l - m_new) in bf16 and the
+// rescale factor; (3) each wave adds P (16 rows x 16 vocab) times its E slice, read back
+// transposed from a wave-private LDS copy, with v_mfma_f32_16x16x16bf16_1k.  E is read
+// from HBM once per row group; the groups of one chunk run on one XCD, so the second
+// group mostly hits L2.  Partial statistics and partial pe per chunk go to the workspace
+// and a combine kernel merges the chunks in index order (deterministic).
+#include "head.h"
+
+namespace dlm {
+
+namespace {
+
+struct HeadP {
+  const uint16_t* h;       // [rows, d] bf16 (f32 path: const float*)
+  const uint16_t* E;       // [V, d]
+  const uint8_t* committed;
+  int rows, d, V;
+  float* st;               // [CH][rows_max][8] partial stats
+  float* pe_part;          // [CH][rows_max][d]
+  float* logits_dbg;       // [rows, V] or null
+  int rows_max, chunks_fixed;
+  // outputs (combine)
+  float* lse;
+  float* ent;
+  float* maxp;
+  int32_t* amax;
+  float* pe;
+  const int32_t* cont_dev;
+};
+
+// open-row compaction shared by all kernels: returns n_open, and fills idx[k] = row of the
+// k-th open row (idx in LDS, size >= 64); thread-count independent.
+__device__ inline int compact_open(const uint8_t* committed, int rows, int* idx) {
+  int n = 0;
+  for (int i = 0; i < rows; ++i) {
+    const bool open = committed == nullptr || committed[i] == 0;
+    if (open) {
+      if (threadIdx.x == 0) idx[n] = i;
+      ++n;
+    }
+  }
+  __syncthreads();
+  return n;
+}
+
+// bf16 path: 256 workgroups = 8 XCDs x 32 slots; the n_groups row groups of a chunk share
+// an XCD slot range, so the chunk count is 8 * floor(32 / n_groups).
+__device__ inline int n_chunks_for(int n_groups, int chunks_fixed) {
+  return chunks_fixed > 0 ? chunks_fixed : 8 * (32 / n_groups);
+}
+
+// statistics layout per (chunk, open row): m, s, T, best value, best index (as float bits)
+enum { ST_M = 0, ST_S = 1, ST_T = 2, ST_BV = 3, ST_BI = 4 };
+
+template <int MAXK, int NW>
+__global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  __shared__ int s_idx[DLM_MAX_ROWS];
+  __shared__ float lpart[NW][16][17];            // [wave][v][row]
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[16][16];   // [row][v] bf16
+  __shared__ float alpha_s[16];
+  __shared__ __attribute__((aligned(16))) uint16_t Et[NW][MAXK * 32][16];  // wave-private E^T
+  const int n_open = compact_open(p.committed, p.rows, s_idx);
+  if (n_open == 0) return;
+  const int n_groups = (n_open + 15) / 16;
+  const int CH = n_chunks_for(n_groups, 0);
+  const int b = blockIdx.x;
+  int chunk, grp;
+  {
+    const int xcd = b & 7, j = b >> 3;
+    chunk = (j / n_groups) * 8 + xcd;
+    grp = j % n_groups;
+  }
+  if (chunk >= CH) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int KST = p.d / 32;
+  const int kw0 = (w * KST) / NW, kw1 = ((w + 1) * KST) / NW;
+  const int nk = kw1 - kw0;
+  const int VT = (p.V + 15) / 16;
+  const int t0 = (int)(((long long)chunk * VT) / CH), t1 = (int)(((long long)(chunk + 1) * VT) / CH);
+
+  // h fragments (B operand of the logit MFMA): lane l: row 16grp + l%16, d = 32kt + 8(l/16)..
+  u32x4_t hf[MAXK];
+  {
+    const int k = 16 * grp + (lane & 15);
+    const bool ok = k < n_open;
+    const int row = ok ? s_idx[k] : 0;
+#pragma unroll
+    for (int u = 0; u < MAXK; ++u)
+      hf[u] = (ok && u < nk) ? ld16(p.h + (size_t)row * p.d + (kw0 + u) * 32 + 8 * (lane >> 4))
+                             : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  f32x4_t acc[MAXK][2];
+#pragma unroll
+  for (int u = 0; u < MAXK; ++u) acc[u][0] = acc[u][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // running statistics for row (tid / 16) of the group, replicated over 16 lanes
+  float rm = -INFINITY, rs = 0.f, rT = 0.f, bv = -INFINITY;
+  int bi = 0x7fffffff;
+  const int my_row = tid >> 4, my_v = tid & 15;
+
+  auto load_tile = [&](int t, u32x4_t* ef) {
+    const int v = t * 16 + (lane & 15);
+    const bool ok = v < p.V;
+#pragma unroll
+    for (int u = 0; u < MAXK; ++u)
+      ef[u] = (ok && u < nk) ? ld16(p.E + (size_t)v * p.d + (kw0 + u) * 32 + 8 * (lane >> 4))
+                             : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  u32x4_t ef[MAXK], en[MAXK];
+  if (t0 < t1) load_tile(t0, ef);
+  for (int t = t0; t < t1; ++t) {
+    if (t + 1 < t1) load_tile(t + 1, en);
+    // (1) partial logits over this wave's d-slice: L^T[v][row]
+    f32x4_t lp = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < MAXK; ++u)
+      if (u < nk) lp = mfma16x16x32(ef[u], hf[u], lp);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lpart[w][4 * (lane >> 4) + r][lane & 15] = lp[r];
+    // keep this wave's E slice, transposed, for the p.E product
+#pragma unroll
+    for (int u = 0; u < MAXK; ++u)
+      if (u < nk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dl = u * 32 + 8 * (lane >> 4) + 2 * i;
+          Et[w][dl][lane & 15] = (uint16_t)(ef[u][i] & 0xffffu);
+          Et[w][dl + 1][lane & 15] = (uint16_t)(ef[u][i] >> 16);
+        }
+      }
+    __syncthreads();
+    // (2) reduce partials, update the statistics of row my_row (threads 0..255)
+    if (tid < 256) {
+      float l = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) l += lpart[q][my_v][my_row];
+      const int vg = t * 16 + my_v;
+      const bool valid = vg < p.V;
+      if (!valid) l = -INFINITY;
+      const int k = 16 * grp + my_row;
+      if (p.logits_dbg && valid && k < n_open) p.logits_dbg[(size_t)s_idx[k] * p.V + vg] = l;
+      float tm = l;
+      for (int o = 1; o < 16; o <<= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
+      // tile argmax (lowest id among equal values)
+      float cv = l;
+      int ci = valid ? vg : 0x7fffffff;
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ov = __shfl_xor(cv, o, 64);
+        const int oi = __shfl_xor(ci, o, 64);
+        if (ov > cv || (ov == cv && oi < ci)) { cv = ov; ci = oi; }
+      }
+      if (cv > bv || (cv == bv && ci < bi)) { bv = cv; bi = ci; }
+      const float mn = fmaxf(rm, tm);
+      const float al = rs > 0.f ? expf(rm - mn) : 0.f;
+      const float e = valid ? expf(l - mn) : 0.f;
+      float se = e, te = valid ? e * (l - mn) : 0.f;
+      for (int o = 1; o < 16; o <<= 1) {
+        se += __shfl_xor(se, o, 64);
+        te += __shfl_xor(te, o, 64);
+      }
+      rT = rs > 0.f ? al * (rT + (rm - mn) * rs) + te : te;
+      rs = al * rs + se;
+      rm = mn;
+      Pt[my_row][my_v] = f2bf(e);
+      if (my_v == 0) alpha_s[my_row] = al;
+    }
+    __syncthreads();
+    // (3) acc[rows][d-slice] = alpha * acc + P E_slice
+    {
+      const u32x2_t pa = *(const u32x2_t*)&Pt[lane & 15][4 * (lane >> 4)];
+      float al4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al4[r] = alpha_s[4 * (lane >> 4) + r];
+#pragma unroll
+      for (int u = 0; u < MAXK; ++u)
+        if (u < nk) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const u32x2_t eb = *(const u32x2_t*)&Et[w][u * 32 + 16 * hb + (lane & 15)][4 * (lane >> 4)];
+            f32x4_t a = acc[u][hb];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] *= al4[r];
+            acc[u][hb] = mfma16x16x16(pa, eb, a);
+          }
+        }
+    }
+    if (t + 1 < t1) {
+#pragma unroll
+      for (int u = 0; u < MAXK; ++u) ef[u] = en[u];
+    }
+  }
+  // partial outputs for rows k = 16grp + r
+  if (tid < 256 && my_v == 0) {
+    const int k = 16 * grp + my_row;
+    if (k < n_open) {
+      float* st = p.st + ((size_t)chunk * p.rows_max + k) * 8;
+      st[ST_M] = rm;
+      st[ST_S] = rs;
+      st[ST_T] = rT;
+      st[ST_BV] = bv;
+      st[ST_BI] = __int_as_float(bi);
+    }
+  }
+  // acc[u][hb] lane l: row 4(l/16)+r, d = kw0*32 + u*32 + 16hb + l%16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k = 16 * grp + 4 * (lane >> 4) + r;
+    if (k < n_open) {
+      float* dst = p.pe_part + ((size_t)chunk * p.rows_max + k) * p.d + kw0 * 32;
+#pragma unroll
+      for (int u = 0; u < MAXK; ++u)
+        if (u < nk) {
+          dst[u * 32 + (lane & 15)] = acc[u][0][r];
+          dst[u * 32 + 16 + (lane & 15)] = acc[u][1][r];
+        }
+    }
+  }
+}
+
+// f32 path: one 256-thread workgroup per (open row k, chunk of 256 vocabulary rows)
+__global__ __launch_bounds__(256) void head_f32_kernel(HeadP p) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  __shared__ int s_idx[DLM_MAX_ROWS];
+  __shared__ float ev[256];
+  __shared__ float red[4][3];
+  __shared__ int redi[4];
+  const int n_open = compact_open(p.committed, p.rows, s_idx);
+  const int k = blockIdx.x / p.chunks_fixed, chunk = blockIdx.x % p.chunks_fixed;
+  if (k >= n_open) return;
+  const int row = s_idx[k];
+  const float* h = (const float*)p.h + (size_t)row * p.d;
+  const float* E = (const float*)p.E;
+  const int per = (p.V + p.chunks_fixed - 1) / p.chunks_fixed;
+  const int v0 = chunk * per, v1 = min(p.V, v0 + per);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float rm = -INFINITY, rs = 0.f, rT = 0.f, bv = -INFINITY;
+  int bi = 0x7fffffff;
+  float pacc = 0.f;   // pe partial for d = tid (the host keeps d <= 256 on this path)
+  for (int base = v0; base < v1; base += 256) {
+    const int v = base + tid;
+    float l = -INFINITY;
+    if (v < v1) {
+      float a = 0.f;
+      for (int t = 0; t < p.d; ++t) a = fmaf(h[t], E[(size_t)v * p.d + t], a);
+      l = a;
+      if (p.logits_dbg) p.logits_dbg[(size_t)row * p.V + v] = l;
+    }
+    // block max and argmax
+    float mx = l;
+    int mi = v < v1 ? v : 0x7fffffff;
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(mx, o, 64);
+      const int oi = __shfl_xor(mi, o, 64);
+      if (ov > mx || (ov == mx && oi < mi)) { mx = ov; mi = oi; }
+    }
+    if (lane == 0) { red[w][0] = mx; redi[w] = mi; }
+    __syncthreads();
+    float tm = red[0][0];
+    int ti = redi[0];
+    for (int q = 1; q < 4; ++q)
+      if (red[q][0] > tm || (red[q][0] == tm && redi[q] < ti)) { tm = red[q][0]; ti = redi[q]; }
+    __syncthreads();
+    if (tm > bv || (tm == bv && ti < bi)) { bv = tm; bi = ti; }
+    const float mn = fmaxf(rm, tm);
+    const float al = rs > 0.f ? expf(rm - mn) : 0.f;
+    const float e = v < v1 ? expf(l - mn) : 0.f;
+    const float te0 = v < v1 ? e * (l - mn) : 0.f;
+    const float se = wave_sum(e), te = wave_sum(te0);
+    if (lane == 0) { red[w][1] = se; red[w][2] = te; }
+    ev[tid] = e;
+    __syncthreads();
+    const float S = ((red[0][1] + red[1][1]) + red[2][1]) + red[3][1];
+    const float T = ((red[0][2] + red[1][2]) + red[2][2]) + red[3][2];
+    rT = rs > 0.f ? al * (rT + (rm - mn) * rs) + T : T;
+    rs = al * rs + S;
+    rm = mn;
+    // pe partial: this thread owns d = tid (first pass only; d <= 256 enforced by host)
+    if (tid < p.d) {
+      float a = pacc * al;
+      const int nv = min(256, v1 - base);
+      for (int i = 0; i < nv; ++i) a = fmaf(ev[i], E[(size_t)(base + i) * p.d + tid], a);
+      pacc = a;
+    }
+    __syncthreads();
+  }
+  float* st = p.st + ((size_t)chunk * p.rows_max + k) * 8;
+  if (tid == 0) {
+    st[ST_M] = rm;
+    st[ST_S] = rs;
+    st[ST_T] = rT;
+    st[ST_BV] = bv;
+    st[ST_BI] = __int_as_float(bi);
+  }
+  if (tid < p.d) p.pe_part[((size_t)chunk * p.rows_max + k) * p.d + tid] = pacc;
+}
+
+// combine: one workgroup (256 threads) per (output row, 256-wide d slice)
+__global__ __launch_bounds__(256) void head_combine_kernel(HeadP p, int bf16_path) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  __shared__ int s_idx[DLM_MAX_ROWS];
+  __shared__ float wts[256];
+  __shared__ float s_stats[4];
+  __shared__ int s_best;
+  const int n_open = compact_open(p.committed, p.rows, s_idx);
+  const int dblocks = (p.d + 255) / 256;
+  const int row = blockIdx.x / dblocks, db = blockIdx.x % dblocks;
+  const int tid = threadIdx.x;
+  const bool open = p.committed == nullptr || p.committed[row] == 0;
+  const int dcol = db * 256 + tid;
+  if (!open) {
+    if (db == 0 && tid == 0) {
+      p.lse[row] = 0.f;
+      p.ent[row] = 0.f;
+      p.maxp[row] = 0.f;
+      p.amax[row] = -1;
+    }
+    if (p.pe && dcol < p.d) p.pe[(size_t)row * p.d + dcol] = 0.f;
+    return;
+  }
+  int k = 0;
+  for (int i = 0; i < row; ++i) k += (p.committed == nullptr || p.committed[i] == 0) ? 1 : 0;
+  const int n_groups = (n_open + 15) / 16;
+  const int CH = bf16_path ? n_chunks_for(n_groups, 0) : p.chunks_fixed;
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int c = 0; c < CH; ++c) M = fmaxf(M, p.st[((size_t)c * p.rows_max + k) * 8 + ST_M]);
+    float S = 0.f, T = 0.f, bvv = -INFINITY;
+    int bii = 0x7fffffff;
+    for (int c = 0; c < CH; ++c) {
+      const float* st = p.st + ((size_t)c * p.rows_max + k) * 8;
+      if (st[ST_S] > 0.f) {
+        const float f = expf(st[ST_M] - M);
+        S += f * st[ST_S];
+        T += f * (st[ST_T] + (st[ST_M] - M) * st[ST_S]);
+      }
+      const float cv = st[ST_BV];
+      const int ci = __float_as_int(st[ST_BI]);
+      if (cv > bvv || (cv == bvv && ci < bii)) { bvv = cv; bii = ci; }
+    }
+    s_stats[0] = M;
+    s_stats[1] = S;
+    s_stats[2] = T;
+    s_best = bii;
+  }
+  __syncthreads();
+  const float M = s_stats[0], S = s_stats[1], T = s_stats[2];
+  if (db == 0 && tid == 0) {
+    const float lnS = logf(S);
+    p.lse[row] = M + lnS;
+    p.ent[row] = lnS - T / S;
+    p.maxp[row] = 1.0f / S;
+    p.amax[row] = (s_best >= 0 && s_best < p.V) ? s_best : 0;   // all-NaN rows still name a valid id
+  }
+  if (!p.pe) return;
+  for (int c = tid; c < CH; c += 256) {
+    const float* st = p.st + ((size_t)c * p.rows_max + k) * 8;
+    wts[c] = st[ST_S] > 0.f ? expf(st[ST_M] - M) / S : 0.f;
+  }
+  __syncthreads();
+  if (dcol < p.d) {
+    float a = 0.f;
+    for (int c = 0; c < CH; ++c) a = fmaf(wts[c], p.pe_part[((size_t)c * p.rows_max + k) * p.d + dcol], a);
+    p.pe[(size_t)row * p.d + dcol] = a;
+  }
+}
+
+}  // namespace
+
+size_t head_ws_bytes(int dtype, int rows, int d, int V) {
+  (void)V;
+  const int CH = dtype == DLM_BF16 ? 256 : 16;
+  return align_up((size_t)CH * rows * 8 * 4, 256) + align_up((size_t)CH * rows * d * 4, 256);
+}
+
+int head_launch(int dtype, const void* h, const void* E, const uint8_t* committed, int rows, int d,
+                int V, float* lse, float* ent, float* maxp, int32_t* amax, float* pe,
+                float* logits_dbg, void* ws, const int32_t* cont_dev, hipStream_t st) {
+  HeadP p;
+  p.h = (const uint16_t*)h;
+  p.E = (const uint16_t*)E;
+  p.committed = committed;
+  p.rows = rows;
+  p.d = d;
+  p.V = V;
+  p.rows_max = rows;
+  const int CH = dtype == DLM_BF16 ? 256 : 16;
+  p.st = (float*)ws;
+  p.pe_part = (float*)((char*)ws + align_up((size_t)CH * rows * 8 * 4, 256));
+  p.logits_dbg = logits_dbg;
+  p.chunks_fixed = dtype == DLM_BF16 ? 0 : 16;
+  p.lse = lse;
+  p.ent = ent;
+  p.maxp = maxp;
+  p.amax = amax;
+  p.pe = pe;
+  p.cont_dev = cont_dev;
+  if (dtype == DLM_BF16) {
+    const int grid = 256;   // n_groups * chunks <= 256, extra workgroups exit
+    const int k8 = (d / 32 + 7) / 8;     // k-steps per wave with 8 waves
+    if (k8 <= 10) {
+      switch (k8) {
+#define HEAD_CASE(K) case K: hipLaunchKernelGGL((head_bf16_kernel<K, 8>), dim3(grid), dim3(512), 0, st, p); break;
+        HEAD_CASE(1) HEAD_CASE(2) HEAD_CASE(3) HEAD_CASE(4) HEAD_CASE(5) HEAD_CASE(6) HEAD_CASE(7)
+        HEAD_CASE(8) HEAD_CASE(9) HEAD_CASE(10)
+#undef HEAD_CASE
+        default: break;
+      }
+    } else {
+      const int k16 = (d / 32 + 15) / 16;
+      if (k16 > 8) return fail(DLM_ERR_SHAPE, "head: d=%d too large", d);
+      hipLaunchKernelGGL((head_bf16_kernel<8, 16>), dim3(grid), dim3(1024), 0, st, p);
+    }
+  } else {
+    hipLaunchKernelGGL(head_f32_kernel, dim3(rows * 16), dim3(256), 0, st, p);
+  }
+  hipLaunchKernelGGL(head_combine_kernel, dim3(rows * ((d + 255) / 256)), dim3(256), 0, st, p,
+                     dtype == DLM_BF16 ? 1 : 0);
+  return check_hip(hipGetLastError(), "head launch");
+}
+
+}  // namespace dlm

@@ -1,0 +1,223 @@
+// Small kernels of the round: RMSNorm, the commit rule, block reset, the self-conditioning
+// operand, the embedding gather of the commit pass and the prefix-length update.
+#include "small.h"
+
+namespace dlm {
+
+namespace {
+
+// ------------------------------------------------------------------ RMSNorm
+// one workgroup (256 threads) per row; deterministic fixed-order reduction
+struct NormP {
+  const float* x;
+  const void* g;
+  void* out;
+  int d, bf16, packed;
+  float eps;
+  const int32_t* cont_dev;
+};
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const float* x = p.x + (size_t)row * p.d;
+  float s = 0.f;
+  for (int i = tid; i < p.d; i += 256) s = fmaf(x[i], x[i], s);
+  s = wave_sum(s);
+  if ((tid & 63) == 0) red[tid >> 6] = s;
+  __syncthreads();
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
+  for (int i = tid; i < p.d; i += 256) {
+    if (p.bf16) {
+      const float g = bf2f(((const uint16_t*)p.g)[i]);
+      ((uint16_t*)p.out)[p.packed ? xpk_index(row, i) : (size_t)row * p.d + i] = f2bf(x[i] * r * g);
+    } else {
+      const float g = ((const float*)p.g)[i];
+      ((float*)p.out)[(size_t)row * p.d + i] = x[i] * r * g;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ commit
+struct CommitP {
+  dlm_commit_rule rule;
+  int rows;
+  const float* maxp;
+  const int32_t* amax;
+  const float* lse;
+  const float* ent;
+  uint8_t* committed;
+  int32_t* tokens;
+  dlm_round_state* st;
+};
+
+__device__ inline float rank_key(float v) { return v != v ? -INFINITY : v; }
+
+// single wave; lane 0 runs the (tiny) selection so the tie-breaks read like the definition
+__global__ __launch_bounds__(64) void commit_kernel(CommitP p) {
+  if (threadIdx.x != 0) return;
+  dlm_round_state* st = p.st;
+  if (st->cont == 0) return;
+  const int round = st->round;
+  uint64_t open = 0;
+  int n_open = 0, flags = 0;
+  for (int i = 0; i < p.rows; ++i)
+    if (!p.committed[i]) {
+      open |= 1ull << i;
+      ++n_open;
+      const bool fin = isfinite(p.maxp[i]) && (!p.lse || isfinite(p.lse[i])) && (!p.ent || isfinite(p.ent[i]));
+      if (!fin) flags |= DLM_FLAG_NONFINITE;
+    }
+  uint64_t sel = 0;
+  auto best_of = [&](uint64_t cand) {
+    int b = -1;
+    float bv = 0.f;
+    for (int i = 0; i < p.rows; ++i)
+      if (cand >> i & 1ull) {
+        const float v = rank_key(p.maxp[i]);
+        if (b < 0 || v > bv) { b = i; bv = v; }
+      }
+    return b;
+  };
+  if (p.rule.mode == DLM_COMMIT_THRESHOLD) {
+    for (int i = 0; i < p.rows; ++i)
+      if ((open >> i & 1ull) && p.maxp[i] >= p.rule.tau) sel |= 1ull << i;
+    if (p.rule.forced_top1 && n_open > 0) sel |= 1ull << best_of(open);
+  } else {
+    const int k = min(p.rule.k, n_open);
+    uint64_t cand = open;
+    for (int j = 0; j < k; ++j) {
+      const int b = best_of(cand);
+      sel |= 1ull << b;
+      cand &= ~(1ull << b);
+    }
+  }
+  if (round >= p.rule.max_rounds - 1) {
+    if (open & ~sel) flags |= DLM_FLAG_HIT_MAX_ROUNDS;
+    sel = open;
+  }
+  int n_new = 0;
+  for (int i = 0; i < p.rows; ++i)
+    if (sel >> i & 1ull) {
+      p.tokens[i] = p.amax[i];
+      p.committed[i] = 1;
+      ++n_new;
+    }
+  if (round < DLM_MAX_ROUNDS) st->n_new[round] = n_new;
+  st->round = round + 1;
+  st->n_open = n_open - n_new;
+  st->flags |= flags;
+  st->cont = (st->n_open > 0 && round + 1 < p.rule.max_rounds) ? 1 : 0;
+}
+
+// ------------------------------------------------------------------ block reset
+__global__ __launch_bounds__(256) void reset_kernel(int rows, uint8_t* committed, int32_t* tokens,
+                                                    dlm_round_state* st, float* pe, int pe_elems) {
+  const int tid = blockIdx.x * 256 + threadIdx.x;
+  if (tid < rows) {
+    committed[tid] = 0;
+    tokens[tid] = 0;
+  }
+  if (st && tid < DLM_MAX_ROUNDS) st->n_new[tid] = 0;
+  if (st && tid == 0) {
+    st->round = 0;
+    st->n_open = rows;
+    st->cont = 1;
+    st->flags = 0;
+  }
+  if (pe)
+    for (int i = tid; i < pe_elems; i += gridDim.x * 256) pe[i] = 0.f;
+}
+
+// ------------------------------------------------------------------ self-cond operand
+// xsc = round(pe) for open rows, 0 for committed rows (so W_sc xsc = 0 there); bf16 output is
+// in the packed operand order of the skinny GEMM
+__global__ __launch_bounds__(256) void selfcond_prep_kernel(const float* pe, const uint8_t* committed,
+                                                            void* xsc, int rows, int d, int bf16,
+                                                            const int32_t* cont_dev) {
+  if (cont_dev && *cont_dev == 0) return;
+  const int n = (bf16 ? 32 : rows) * d;   // bf16: all 32 operand rows (rows >= `rows` are zero)
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int r = i / d;
+    const float v = (r < rows && pe && !(committed && committed[r])) ? pe[i] : 0.f;
+    if (bf16) ((uint16_t*)xsc)[xpk_index(r, i - r * d)] = f2bf(v);
+    else ((float*)xsc)[i] = v;
+  }
+}
+
+// ------------------------------------------------------------------ embedding gather
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const void* E, float* x,
+                                                    int rows, int d, int V, int bf16) {
+  const int n = rows * d;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int r = i / d, c = i % d;
+    int tok = tokens[r];
+    tok = (tok < 0 || tok >= V) ? 0 : tok;   // out-of-range ids read row 0 instead of faulting
+    const size_t src = (size_t)tok * d + c;
+    x[i] = bf16 ? bf2f(((const uint16_t*)E)[src]) : ((const float*)E)[src];
+  }
+}
+
+// row-major bf16 [rows, k] -> packed skinny-GEMM operand order (rows < 32; other rows zero)
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* x, int rows, int k, uint16_t* out) {
+  const int n = 32 * k;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int r = i / k, c = i % k;
+    out[xpk_index(r, c)] = r < rows ? x[i] : (uint16_t)0;
+  }
+}
+
+__global__ void len_add_kernel(int32_t* len, int add) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *len += add;
+}
+
+}  // namespace
+
+int rmsnorm(const float* x, const void* g, void* out, int rows, int d, int bf16, int packed, float eps,
+            const int32_t* cont_dev, hipStream_t st) {
+  NormP p{x, g, out, d, bf16, packed, eps, cont_dev};
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, st, p);
+  return check_hip(hipGetLastError(), "rmsnorm launch");
+}
+
+int commit_launch(const dlm_commit_rule& rule, int rows, const float* maxp, const int32_t* amax,
+                  const float* lse, const float* ent, uint8_t* committed, int32_t* tokens,
+                  dlm_round_state* state, hipStream_t st) {
+  CommitP p{rule, rows, maxp, amax, lse, ent, committed, tokens, state};
+  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, st, p);
+  return check_hip(hipGetLastError(), "commit launch");
+}
+
+int block_reset(int rows, uint8_t* committed, int32_t* tokens, dlm_round_state* state, float* pe,
+                int pe_elems, hipStream_t st) {
+  const int grid = pe ? 64 : 1;
+  hipLaunchKernelGGL(reset_kernel, dim3(grid), dim3(256), 0, st, rows, committed, tokens, state, pe,
+                     pe_elems);
+  return check_hip(hipGetLastError(), "reset launch");
+}
+
+int selfcond_prep(const float* pe, const uint8_t* committed, void* xsc, int rows, int d, int bf16,
+                  const int32_t* cont_dev, hipStream_t st) {
+  hipLaunchKernelGGL(selfcond_prep_kernel, dim3(64), dim3(256), 0, st, pe, committed, xsc, rows, d, bf16,
+                     cont_dev);
+  return check_hip(hipGetLastError(), "selfcond prep launch");
+}
+
+int embed(const int32_t* tokens, const void* E, float* x, int rows, int d, int V, int bf16, hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3(64), dim3(256), 0, st, tokens, E, x, rows, d, V, bf16);
+  return check_hip(hipGetLastError(), "embed launch");
+}
+
+int pack_rows_bf16(const void* x, int rows, int k, void* out, hipStream_t st) {
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(64), dim3(256), 0, st, (const uint16_t*)x, rows, k, (uint16_t*)out);
+  return check_hip(hipGetLastError(), "pack rows launch");
+}
+
+int len_add(int32_t* len, int add, hipStream_t st) {
+  hipLaunchKernelGGL(len_add_kernel, dim3(1), dim3(64), 0, st, len, add);
+  return check_hip(hipGetLastError(), "len add launch");
+}
+
+}  // namespace dlm

@@ -1,0 +1,324 @@
+/*
+ * dlm.h -- C ABI of the block-diffusion denoising-round library for MI355X (gfx950).
+ *
+ * What is computed (sources are web pages, cited by title and section):
+ *   [ORL-blog] "ORL: diffusion LLMs get a learnable 'tokens per forward' -- 2,788 tok/s
+ *              on one RTX 5090, 7,708 on 8x B200, fully open source", section "What shipped":
+ *              generation in blocks; each denoising round yields a distribution over the
+ *              still-unresolved tokens; the previous round's distribution is fed back
+ *              through a self-conditioning adapter on the tied embedding; positions that
+ *              clear the commit bar are committed; the round loop of a block runs on the
+ *              device with the continue decision taken after every round and the host only
+ *              launching the block and reading tokens back.
+ *   [ORL-card] "QwenDLM-4B-ORL" model card, section "The paper's evaluation pipeline":
+ *              block decoding against a prefix KV cache, fused per-row statistics of the
+ *              head, the commit step inside a captured graph.
+ *
+ * Conventions shared by every call:
+ *   - Every call returns an int status (dlm_status).  Arguments are validated on the host,
+ *     synchronously, before anything is enqueued; a failed call enqueues nothing.
+ *     dlm_last_error() returns a thread-local description of the last failure.
+ *   - Every call is enqueue-only on the caller's stream (a hipStream_t passed as void*;
+ *     NULL is the default stream).  Device faults surface at the caller's next sync.
+ *   - The caller owns every device buffer (weights, packed weights, KV cache, workspaces,
+ *     outputs).  The library never allocates device memory.  dlm_model is a host-side
+ *     handle holding pointers and shapes only.
+ *   - Layouts are row-major and contiguous.  [out, in] is the weight convention.
+ *     Token ids are int32; commit flags are uint8 0/1.
+ *   - Data-dependent conditions (max rounds hit, non-finite statistics) are not errors;
+ *     they are bits in the device-side round state (DLM_FLAG_*).
+ *   - Results are bitwise deterministic for identical inputs (no float atomics).  Calls
+ *     that share a workspace must not run concurrently.
+ */
+#ifndef DLM_H_
+#define DLM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLM_ABI_VERSION 1
+#define DLM_MAX_ROWS 64
+#define DLM_MAX_ROUNDS 64
+
+typedef enum {
+  DLM_OK = 0,
+  DLM_ERR_ARG = -1,         /* null pointer where one is required, negative size */
+  DLM_ERR_SHAPE = -2,       /* unsupported or inconsistent shape */
+  DLM_ERR_DTYPE = -3,       /* unsupported dtype */
+  DLM_ERR_WORKSPACE = -4,   /* workspace too small */
+  DLM_ERR_HIP = -5,         /* HIP launch / API failure */
+  DLM_ERR_UNSUPPORTED = -6  /* device is not gfx950 */
+} dlm_status;
+
+typedef enum { DLM_F32 = 0, DLM_BF16 = 1, DLM_MXFP4 = 2 } dlm_dtype;
+
+typedef enum { DLM_COMMIT_THRESHOLD = 0, DLM_COMMIT_FIXED_K = 1 } dlm_commit_mode;
+
+enum { DLM_FLAG_HIT_MAX_ROUNDS = 1, DLM_FLAG_NONFINITE = 2 };
+
+int dlm_abi_version(void);
+const char* dlm_last_error(void);
+
+/* ------------------------------------------------------------------------------------
+ * dlm_block_attn -- attention of a block of B query positions to a prefix KV cache of
+ * length L plus the block's own B keys, with no mask: every block query sees all L + B
+ * keys ([ORL-blog] "What shipped": a block's unresolved tokens are predicted together;
+ * [ORL-card] evaluation pipeline: block decoding against a prefix KV cache).
+ * Grouped-query attention: query head h reads kv head h / (hq / hkv).
+ *
+ *   q        [B, hq, D]     query rows, RoPE already applied.
+ *   k_cache  [hkv, cap, D]  keys; rows [0, L) are the prefix, [L, L+B) the block.
+ *   v_cache  [hkv, cap, D]  values, same layout.
+ *   out      [B, hq, D]     o = softmax(scale * q k^T) v, same dtype as q.
+ *   L is desc->prefix_len, or *desc->prefix_len_dev when that device pointer is non-null
+ *   (so a captured graph can replay with a growing prefix).  Shapes: D in {64, 128},
+ *   hq % hkv == 0, 1 <= B <= 64, L + B <= cap.
+ *   ws: device scratch of at least dlm_block_attn_ws_bytes(desc) bytes; must be zeroed
+ *   once before first use (the kernels leave it zeroed again).
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int dtype;            /* DLM_BF16 or DLM_F32 (all of q, caches, out) */
+  int hq, hkv, head_dim, block, cap;
+  float softmax_scale;  /* usually 1/sqrt(head_dim) */
+  int prefix_len;       /* host value of L (used if prefix_len_dev is NULL) */
+  const int32_t* prefix_len_dev;
+  int max_prefix_len;   /* upper bound of L when prefix_len_dev is used (sizes the workspace) */
+} dlm_attn_desc;
+
+size_t dlm_block_attn_ws_bytes(const dlm_attn_desc* desc);
+int dlm_block_attn(const dlm_attn_desc* desc, const void* q, const void* k_cache,
+                   const void* v_cache, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * dlm_head_rowstats -- tied-embedding head fused with per-row statistics and the p.E
+ * feedback mix ([ORL-blog] "What shipped": per-round distribution, self-conditioning on
+ * the tied embedding; [ORL-card] evaluation pipeline: fused row statistics).  For every
+ * open row i (committed == NULL or committed[i] == 0), with l = h_i E^T over the whole
+ * vocabulary (never written to memory):
+ *   lse = max l + ln sum exp(l - max l);  entropy = -sum p ln p (nats);
+ *   maxprob = max p;  argmax = lowest id with l == max l;  pe = sum_v p_v E_v.
+ * Committed rows get argmax = -1, lse = entropy = maxprob = 0 and a zero pe row.
+ *
+ *   h          [rows, d]  final-normed hidden rows (dtype).
+ *   emb        [V, d]     tied embedding (dtype).
+ *   committed  [rows] u8 or NULL.
+ *   lse, entropy, maxprob [rows] f32;  argmax [rows] i32;  pe [rows, d] f32 or NULL.
+ *   logits_dbg [rows, V] f32 or NULL (tests only; costs an extra write of the logits).
+ * Shapes: 1 <= rows <= 64, d % 32 == 0, d <= 4096, V >= 1.
+ * ws: at least dlm_head_rowstats_ws_bytes(desc) bytes (no zeroing needed).
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int dtype;
+  int rows, d, vocab;
+} dlm_head_desc;
+
+size_t dlm_head_rowstats_ws_bytes(const dlm_head_desc* desc);
+int dlm_head_rowstats(const dlm_head_desc* desc, const void* h, const void* emb,
+                      const uint8_t* committed, float* lse, float* entropy, float* maxprob,
+                      int32_t* argmax, float* pe, float* logits_dbg, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * dlm_commit -- one round's confidence commit ([ORL-blog] "What shipped": positions that
+ * clear the commit bar are committed; more clearing means fewer rounds per block).
+ *   THRESHOLD: commit open rows with maxprob >= tau, plus (forced_top1) the open row with
+ *              the largest maxprob.   FIXED_K: the min(k, n_open) open rows with the
+ *              largest maxprob.  Ties rank the lower row first; NaN ranks as -inf.
+ *   In round max_rounds - 1 every open row is committed (DLM_FLAG_HIT_MAX_ROUNDS if that
+ *   committed more than the rule would).  A committed row is never reopened; its token
+ *   is its argmax.
+ *   maxprob [rows] f32, argmax [rows] i32 (inputs); committed [rows] u8, tokens [rows] i32
+ *   (updated in place); state: device dlm_round_state (round, n_open, cont, flags,
+ *   n_new[round] updated).  Does nothing when state->cont == 0.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int mode;         /* dlm_commit_mode */
+  float tau;
+  int k;
+  int forced_top1;
+  int max_rounds;   /* 1 .. DLM_MAX_ROUNDS */
+} dlm_commit_rule;
+
+typedef struct {
+  int32_t round;    /* rounds run so far in this block */
+  int32_t n_open;   /* open rows */
+  int32_t cont;     /* 1 while the block loop continues */
+  int32_t flags;    /* DLM_FLAG_* */
+  int32_t n_new[DLM_MAX_ROUNDS];  /* commits per round */
+} dlm_round_state;
+
+int dlm_commit(const dlm_commit_rule* rule, int rows, const float* maxprob,
+               const int32_t* argmax, uint8_t* committed, int32_t* tokens,
+               dlm_round_state* state, void* stream);
+
+/* Reset a block: committed = 0, tokens = 0, state = {0, rows, 1, 0, 0...}. */
+int dlm_block_reset(int rows, uint8_t* committed, int32_t* tokens, dlm_round_state* state,
+                    void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * dlm_selfcond -- the round's input rows ([ORL-blog] "What shipped": the previous round's
+ * distribution is fed back through a self-conditioning adapter on the tied embedding, so
+ * each round starts from the model's own last guess).
+ *   x_i = E[tokens_i]                       if committed_i
+ *   x_i = mask_emb + W_sc . bf(pe_prev_i)   otherwise (pe_prev NULL: x_i = mask_emb)
+ *   tokens [rows] i32, committed [rows] u8, emb [V, d], mask_emb [d], w_sc [d, d] (dtype;
+ *   for DLM_BF16 w_sc is the packed form written by dlm_pack_matrix), pe_prev [rows, d] f32
+ *   or NULL, x_out [rows, d] f32.  bf() rounds to the dtype (bf16 for DLM_BF16).
+ * ws: at least dlm_selfcond_ws_bytes(desc) bytes, zeroed once before first use.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int dtype;
+  int rows, d, vocab;
+} dlm_selfcond_desc;
+
+size_t dlm_selfcond_ws_bytes(const dlm_selfcond_desc* desc);
+int dlm_selfcond(const dlm_selfcond_desc* desc, const int32_t* tokens, const uint8_t* committed,
+                 const void* emb, const void* mask_emb, const void* w_sc, const float* pe_prev,
+                 float* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Weight packing.  bf16 matrices used by the skinny GEMMs are re-laid out once, at model
+ * load, so that every 32-row x 16-column tile is one contiguous 1 KiB run in the order
+ * the matrix cores consume it (v_mfma_f32_32x32x16_bf16 A operand: lane l holds the 8
+ * columns 8(l/32).. of row l%32).  dlm_pack_matrix packs W[n_rows, k] (bf16, [out, in]);
+ * rows are taken in the order given by row_map (NULL = identity; row_map[i] is the source
+ * row of packed row i).  n_rows % 32 == 0, k % 32 == 0.  dst holds n_rows * k bf16.
+ * ------------------------------------------------------------------------------------ */
+int dlm_pack_matrix(const void* src, int n_rows, int k, const int32_t* row_map_dev, void* dst,
+                    void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * dlm_linear -- y = x W^T for the block's rows with a packed bf16 weight: the skinny
+ * matrix-core GEMM every projection of the round uses (same kernel, tiling and split plan
+ * as inside the decode step), with a plain f32 store as its epilogue.
+ *   w_packed [n, k] packed by dlm_pack_matrix;  x: 32 x k bf16 in the packed activation
+ *   order written by dlm_pack_activations (rows >= m are read but ignored);  y [m, n] f32.
+ *   1 <= m <= 32, n % 32 == 0, k % 32 == 0.  ws: dlm_linear_ws_bytes(n, k) bytes, zeroed
+ *   once before first use.
+ * dlm_pack_activations -- x [rows, k] bf16 row-major -> the packed activation order: for
+ *   16-column step kt the 64 lanes' 16-byte pieces X[l % 32][16 kt + 8 (l / 32) .. +8] form one
+ *   contiguous 1 KiB run (rows >= `rows` up to 32 are zero).  x_packed holds 32 * k bf16.
+ * ------------------------------------------------------------------------------------ */
+size_t dlm_linear_ws_bytes(int n, int k);
+int dlm_linear(const void* w_packed, const void* x, int m, int n, int k, float* y, void* ws,
+               size_t ws_bytes, void* stream);
+int dlm_pack_activations(const void* x, int rows, int k, void* x_packed, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Model.  Weight pointers (device) in natural layout for DLM_F32; for DLM_BF16 the
+ * matrices wqkv / wgu / wo / wd / w_sc must be packed by dlm_pack_model into one buffer
+ * of dlm_packed_bytes(desc) bytes (see dlm_pack_model).
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int dtype;                 /* DLM_F32 or DLM_BF16 */
+  int n_layers, d, hq, hkv, head_dim, ffn, vocab, block;
+  float rope_base, eps;
+  int n_experts, expert_ffn, top_k, n_shared;  /* 0 for dense models */
+} dlm_model_desc;
+
+typedef struct {
+  const void* attn_norm;     /* [d] */
+  const void* wq;            /* [hq*D, d] */
+  const void* wk;            /* [hkv*D, d] */
+  const void* wv;            /* [hkv*D, d] */
+  const void* wo;            /* [d, hq*D] */
+  const void* ffn_norm;      /* [d] */
+  const void* wg;            /* [F, d] (dense) */
+  const void* wu;            /* [F, d] (dense) */
+  const void* wd;            /* [d, F] (dense) */
+  const void* router;        /* [n_experts, d] bf16 (MoE) */
+  const void* x_w13;         /* MoE experts: packed MXFP4 gate/up  (see dlm_moe_layout) */
+  const void* x_w13_scale;
+  const void* x_w2;          /* MoE experts: packed MXFP4 down */
+  const void* x_w2_scale;
+} dlm_layer_weights;
+
+typedef struct dlm_model dlm_model;
+
+/* Creates a host handle.  emb [V, d], mask_emb [d], w_sc [d, d], final_norm [d]; layers
+ * is an array of n_layers entries (copied).  packed: the buffer written by dlm_pack_model
+ * (DLM_BF16; NULL for DLM_F32).  No device memory is allocated. */
+int dlm_model_create(const dlm_model_desc* desc, const void* emb, const void* mask_emb,
+                     const void* w_sc, const void* final_norm, const dlm_layer_weights* layers,
+                     const void* packed, dlm_model** out);
+void dlm_model_destroy(dlm_model* m);
+
+/* Bytes of the packed-weights buffer of a bf16 model (0 for f32). */
+size_t dlm_packed_bytes(const dlm_model_desc* desc);
+/* Pack every bf16 GEMM matrix of the model (natural layouts in emb/w_sc/layers) into dst.
+ * row_map_ws: device scratch of at least dlm_pack_ws_bytes(desc) bytes. */
+size_t dlm_pack_ws_bytes(const dlm_model_desc* desc);
+int dlm_pack_model(const dlm_model_desc* desc, const void* w_sc, const dlm_layer_weights* layers,
+                   void* dst, void* row_map_ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * KV cache.  k[l], v[l]: device bases of layer l, each [hkv, cap, D] (model dtype).
+ * len_dev: device int32 holding the committed prefix length L.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  void* const* k;            /* host array of n_layers device pointers */
+  void* const* v;
+  int cap;
+  int32_t* len_dev;
+  int max_len;               /* largest L + block the caller will use (sizes workspaces) */
+} dlm_kv;
+
+/* ------------------------------------------------------------------------------------
+ * dlm_decode_block -- decode one block of `block` fully masked positions after the cached
+ * prefix, entirely on the device ([ORL-blog] "What shipped": one launch per block, the
+ * denoising loop stays on the GPU, the continue decision is taken after every round, the
+ * host only reads tokens back).  Enqueues ceil(block / k) rounds (FIXED_K) or max_rounds
+ * rounds (THRESHOLD; rounds after the block is complete exit immediately), each round =
+ * self-conditioning input, every layer, final norm, head statistics, commit; then a commit
+ * pass that forwards the committed tokens and writes their K/V at [L, L + block), and
+ * L += block.  No host synchronisation inside; the first call with a given set of buffers
+ * captures the sequence into a HIP graph that later calls replay.
+ *   tokens [block] i32 (out), state: device dlm_round_state (out; n_new per round,
+ *   rounds used, flags).  ws: dlm_decode_ws_bytes(model, kv) bytes, zeroed once before
+ *   first use.  Every device input must stay valid while the captured graph may replay.
+ * ------------------------------------------------------------------------------------ */
+size_t dlm_decode_ws_bytes(const dlm_model* m, const dlm_kv* kv);
+int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                     int32_t* tokens, dlm_round_state* state, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Commit passes over n / block consecutive prompt blocks (n % block == 0): forwards each
+ * block of ids (device int32 [n]) and appends its K/V; L += n. */
+int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Debug/test hooks on the decode workspace (device pointers into ws; NULL if absent). */
+typedef struct {
+  float* x;          /* [block, d] residual stream of the last forward */
+  void* hn;          /* [block, d] final-normed rows (model dtype) */
+  float* pe;         /* [block, d] p.E of the last round */
+  float* lse;        /* [block] */
+  float* entropy;    /* [block] */
+  float* maxprob;    /* [block] */
+  int32_t* argmax;   /* [block] */
+  uint8_t* committed;/* [block] */
+} dlm_decode_views;
+int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* ws, size_t ws_bytes,
+                         dlm_decode_views* out);
+
+/* One round only (no commit pass), from the state held in ws (tests: lockstep parity).
+ * round_index is the index of this round in the block (device state is used for the
+ * commit; the host value only selects nothing and is accepted for logging). */
+int dlm_decode_round(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                     int32_t* tokens, dlm_round_state* state, void* ws, size_t ws_bytes,
+                     void* stream);
+/* Reset the block state held in ws (committed = 0, pe = 0) and state. */
+int dlm_decode_begin(const dlm_model* m, const dlm_kv* kv, int32_t* tokens,
+                     dlm_round_state* state, void* ws, size_t ws_bytes, void* stream);
+/* The commit pass alone: forwards tokens [block] at [L, L+block) and sets L += block. */
+int dlm_commit_pass(const dlm_model* m, const dlm_kv* kv, const int32_t* tokens, void* ws,
+                    size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLM_H_ */

@@ -1,0 +1,108 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared call, and rejects bad
+arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_diffusion_decoding_denoise_amd as dlm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dlm.h")
+
+OK, ARG, SHAPE, DTYPE, WS, HIP, UNSUP = 0, -1, -2, -3, -4, -5, -6
+FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced by a rejected call
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dlm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_call():
+    L = dlm.lib()
+    names = _declared()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert L.dlm_abi_version() == 1
+
+
+def _attn(**kw):
+    base = dict(dtype=dlm.DLM_BF16, hq=32, hkv=8, head_dim=128, block=32, cap=1024, softmax_scale=0.088,
+                prefix_len=100, prefix_len_dev=None, max_prefix_len=100)
+    base.update(kw)
+    return dlm.AttnDesc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=30), SHAPE), (dict(head_dim=96), SHAPE), (dict(block=33), SHAPE), (dict(prefix_len=1000), SHAPE),
+    (dict(dtype=7), DTYPE), (dict(hkv=0), ARG), (dict(prefix_len=-1), ARG),
+])
+def test_block_attn_validation(kw, code):
+    d = _attn(**kw)
+    L = dlm.lib()
+    assert L.dlm_block_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == code
+    assert L.dlm_last_error()
+
+
+def test_block_attn_null_and_workspace():
+    L = dlm.lib()
+    d = _attn()
+    assert L.dlm_block_attn(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == ARG
+    assert L.dlm_block_attn(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == ARG
+    need = L.dlm_block_attn_ws_bytes(ctypes.byref(d))
+    assert need > 0
+    assert L.dlm_block_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WS
+    misaligned = ctypes.c_void_p(0x10002)
+    assert L.dlm_block_attn(ctypes.byref(d), misaligned, FAKE, FAKE, FAKE, FAKE, need, None) == ARG
+
+
+def test_head_validation():
+    L = dlm.lib()
+    ok = dlm.HeadDesc(dlm.DLM_BF16, 32, 2560, 151936)
+    need = L.dlm_head_rowstats_ws_bytes(ctypes.byref(ok))
+    assert need > 151936 // 16
+    args = [FAKE] * 9
+    assert L.dlm_head_rowstats(ctypes.byref(dlm.HeadDesc(dlm.DLM_BF16, 65, 2560, 100)), *args, FAKE, need, None) == SHAPE
+    assert L.dlm_head_rowstats(ctypes.byref(dlm.HeadDesc(dlm.DLM_BF16, 32, 2561, 100)), *args, FAKE, need, None) == SHAPE
+    assert L.dlm_head_rowstats(ctypes.byref(dlm.HeadDesc(dlm.DLM_F32, 32, 512, 100)), *args, FAKE, need, None) == SHAPE
+    assert L.dlm_head_rowstats(ctypes.byref(dlm.HeadDesc(5, 32, 256, 100)), *args, FAKE, need, None) == DTYPE
+    assert L.dlm_head_rowstats(ctypes.byref(ok), *args, FAKE, need - 1, None) == WS
+    assert L.dlm_head_rowstats(ctypes.byref(ok), None, *args[1:], FAKE, need, None) == ARG
+
+
+def test_commit_validation():
+    L = dlm.lib()
+    r = dlm.CommitRule.fixed_k(0)
+    assert L.dlm_commit(ctypes.byref(r), 32, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ARG
+    r = dlm.CommitRule.threshold(max_rounds=65)
+    assert L.dlm_commit(ctypes.byref(r), 32, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ARG
+    r = dlm.CommitRule.threshold()
+    assert L.dlm_commit(ctypes.byref(r), 65, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.dlm_commit(ctypes.byref(r), 32, None, FAKE, FAKE, FAKE, FAKE, None) == ARG
+
+
+def test_model_desc_validation():
+    L = dlm.lib()
+    good = dlm.ModelDesc(dlm.DLM_BF16, 36, 2560, 32, 8, 128, 9728, 151936, 32, 1e4, 1e-6, 0, 0, 0, 0)
+    assert L.dlm_packed_bytes(ctypes.byref(good)) > 7_000_000_000
+    bad = dlm.ModelDesc(dlm.DLM_BF16, 36, 2560, 32, 7, 128, 9728, 151936, 32, 1e4, 1e-6, 0, 0, 0, 0)
+    assert L.dlm_packed_bytes(ctypes.byref(bad)) == 0
+    layers = (dlm.LayerWeights * 36)()
+    h = ctypes.c_void_p()
+    assert L.dlm_model_create(ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, layers, FAKE, ctypes.byref(h)) == ARG
+    f32 = dlm.ModelDesc(dlm.DLM_F32, 2, 512, 4, 2, 64, 768, 4096, 32, 1e4, 1e-6, 0, 0, 0, 0)
+    assert L.dlm_packed_bytes(ctypes.byref(f32)) == 0       # f32 models up to d = 256 only
+
+
+def test_valid_call_without_device_is_unsupported():
+    """A fully valid call reaches the device check; with no gfx950 device current it
+    returns DLM_ERR_UNSUPPORTED (on a GPU machine this test is skipped)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    L = dlm.lib()
+    r = dlm.CommitRule.threshold()
+    assert L.dlm_commit(ctypes.byref(r), 32, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUP

@@ -1,0 +1,215 @@
+"""GPU parity of the library's op calls against the CPU oracle on seeded inputs."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from oracle import Prec, head_rowstats as o_head, attention as o_attn, CommitRule as OCommitRule, commit as o_commit
+from tests.gpu_util import require_gpu, dev_bf16, dev_f32, storage
+
+pytestmark = pytest.mark.gpu
+
+
+def _dlm():
+    require_gpu()
+    import block_diffusion_decoding_denoise_amd as dlm
+    dlm.lib()
+    return dlm
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ head
+def _head_case(dtype, rows, d, V, n_committed, seed):
+    dlm = _dlm()
+    _say(f"head case dtype={dtype} rows={rows} d={d} V={V} committed={n_committed} seed={seed}")
+    h32 = synth.unit_rms_rows(seed, "head.h", rows, d)
+    E = synth.stored_normal(seed, "head.E", (V, d), 0.02, dtype)
+    h = synth.f32_to_bf16_bits(h32) if dtype == "bf16" else h32
+    committed = synth.committed_mask(seed, rows, n_committed)
+    out = dlm.head_rowstats(storage(h, dtype), storage(E, dtype), torch.from_numpy(committed).cuda(), logits=True)
+    torch.cuda.synchronize()
+    ref = o_head(oracle.decode_storage(h), E, committed, Prec(dtype, np.float64), want_logits=True)
+    open_rows = np.nonzero(committed == 0)[0]
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    # committed rows: sentinels
+    for i in np.nonzero(committed)[0]:
+        assert g["argmax"][i] == -1 and g["lse"][i] == 0 and g["entropy"][i] == 0 and g["maxprob"][i] == 0
+        assert not g["pe"][i].any()
+    if open_rows.size == 0:
+        return
+    lt = 1e-4 if dtype == "f32" else 2e-2
+    np.testing.assert_allclose(g["logits"][open_rows], ref["logits"][open_rows], atol=lt * 0.01 if dtype == "f32" else lt, rtol=0)
+    np.testing.assert_allclose(g["lse"][open_rows], ref["lse"][open_rows], rtol=1e-4 if dtype == "f32" else 1e-3)
+    np.testing.assert_allclose(g["entropy"][open_rows], ref["entropy"][open_rows], rtol=1e-4 if dtype == "f32" else 1e-2)
+    np.testing.assert_allclose(g["maxprob"][open_rows], ref["maxprob"][open_rows], rtol=1e-4 if dtype == "f32" else 1e-2)
+    # argmax exact except near-ties (top-2 gap below 1e-3 for bf16, 1e-6 for f32)
+    tie = 1e-6 if dtype == "f32" else 1e-3
+    mism = [i for i in open_rows if g["argmax"][i] != ref["argmax"][i]]
+    assert all(ref["top2_gap"][i] < tie for i in mism), f"argmax mismatch rows {mism}"
+    # pe: row-norm relative error
+    num = np.linalg.norm(g["pe"][open_rows] - ref["pe"][open_rows], axis=1)
+    den = np.linalg.norm(ref["pe"][open_rows], axis=1)
+    assert np.all(num / den < (1e-4 if dtype == "f32" else 1e-2)), (num / den).max()
+
+
+@pytest.mark.parametrize("rows,d,V,nc", [(32, 256, 1000, 8), (7, 512, 333, 0), (32, 2560, 5003, 16),
+                                         (64, 2048, 2049, 20), (32, 2560, 4096, 32), (1, 256, 17, 0)])
+def test_head_bf16_small(rows, d, V, nc):
+    _head_case("bf16", rows, d, V, nc, 1234)
+
+
+@pytest.mark.parametrize("rows,d,V,nc", [(32, 256, 4096, 0), (32, 256, 4096, 24), (5, 64, 100, 1)])
+def test_head_f32(rows, d, V, nc):
+    _head_case("f32", rows, d, V, nc, 1235)
+
+
+# ------------------------------------------------------------------ attention
+def _attn_case(dtype, hq, hkv, D, B, L, cap, seed):
+    dlm = _dlm()
+    _say(f"attn case dtype={dtype} hq={hq} hkv={hkv} D={D} B={B} L={L} seed={seed}")
+    q = synth.stored_normal(seed, "attn.q", (B, hq, D), 1.0, dtype)
+    k = synth.stored_normal(seed, "attn.k", (hkv, cap, D), 1.0, dtype)
+    v = synth.stored_normal(seed, "attn.v", (hkv, cap, D), 1.0, dtype)
+    out = dlm.block_attn(storage(q, dtype), storage(k, dtype), storage(v, dtype), L)
+    torch.cuda.synchronize()
+    qf, kf, vf = (oracle.decode_storage(a) for a in (q, k, v))
+    ref = o_attn(qf, kf[:, :L + B], vf[:, :L + B], 1 / math.sqrt(D))
+    got = out.float().cpu().numpy()
+    if dtype == "bf16":
+        # bf16 output: one rounding of the result plus bf16 probabilities inside P.V
+        np.testing.assert_allclose(got, ref, atol=2e-2, rtol=2e-2)
+    else:
+        np.testing.assert_allclose(got, ref, atol=1e-5, rtol=1e-4)
+
+
+@pytest.mark.parametrize("L", [0, 1, 33, 300, 511])
+def test_attn_bf16_small(L):
+    _attn_case("bf16", 32, 8, 128, 32, L, 1024, 1234)
+
+
+@pytest.mark.parametrize("L,B,hq,hkv,D", [(0, 1, 4, 2, 64), (17, 7, 8, 8, 128), (1000, 32, 16, 4, 128),
+                                          (64, 32, 4, 1, 64)])
+def test_attn_bf16_shapes(L, B, hq, hkv, D):
+    _attn_case("bf16", hq, hkv, D, B, L, L + B + 5, 1236)
+
+
+@pytest.mark.parametrize("L", [0, 64, 150])
+def test_attn_f32(L):
+    _attn_case("f32", 4, 2, 64, 32, L, 256, 1235)
+
+
+# ------------------------------------------------------------------ commit
+def _gpu_commit(rule_args, maxprob, committed=None, rounds=1, state_round=0):
+    dlm = _dlm()
+    n = len(maxprob)
+    mp = torch.tensor(maxprob, dtype=torch.float32, device="cuda")
+    am = torch.arange(100, 100 + n, dtype=torch.int32, device="cuda")
+    c = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    tok = torch.zeros(n, dtype=torch.int32, device="cuda")
+    st = dlm.new_round_state()
+    dlm.block_reset(c, tok, st)
+    if committed is not None:
+        c.copy_(torch.tensor(committed, dtype=torch.uint8))
+        st[1] = int(n - sum(committed))
+    if state_round:
+        st[0] = state_round
+    rule = dlm.CommitRule(*rule_args)
+    dlm.commit(rule, mp, am, c, tok, st)
+    torch.cuda.synchronize()
+    return c.cpu().numpy(), tok.cpu().numpy(), dlm.state_dict(st)
+
+
+@pytest.mark.parametrize("mp,rule,committed,expect", [
+    ([0.95, 0.5, 0.91, 0.2], (0, 0.9, 1, 1, 32), None, [0, 2]),
+    ([0.3, 0.6, 0.6, 0.1], (0, 0.9, 1, 1, 32), None, [1]),
+    ([0.99, 0.4, 0.3], (0, 0.9, 1, 1, 32), [1, 0, 0], [1]),
+    ([0.5, 0.7, 0.5, 0.5], (1, 0.0, 2, 0, 32), None, [0, 1]),
+    ([float("nan"), 0.2, 0.1], (0, 0.9, 1, 1, 32), None, [1]),
+])
+def test_commit_crafted(mp, rule, committed, expect):
+    c, tok, st = _gpu_commit(rule, mp, committed)
+    before = np.array(committed or [0] * len(mp))
+    now = [i for i in range(len(mp)) if c[i] and not before[i]]
+    assert now == expect
+    for i in now:
+        assert tok[i] == 100 + i
+    assert st["round"] == 1 and st["n_new"] == [len(expect)]
+
+
+def test_commit_matches_oracle_random():
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        n = int(rng.integers(1, 33))
+        mp = rng.uniform(0, 1, n).astype(np.float32)
+        mode = int(rng.integers(0, 2))
+        k = int(rng.integers(1, 12))
+        rule = (mode, 0.7, k, 1, 32)
+        c, tok, st = _gpu_commit(rule, mp.tolist())
+        oc = np.zeros(n, np.uint8)
+        ot = np.zeros(n, np.int32)
+        sel, _ = o_commit(OCommitRule(mode, 0.7, k, True, 32), mp.astype(np.float64), np.arange(100, 100 + n),
+                          oc, ot, 0)
+        assert list(np.nonzero(c)[0]) == sel
+
+
+def test_commit_max_rounds_flag():
+    c, tok, st = _gpu_commit((0, 0.9, 1, 1, 4), [0.1, 0.2, 0.3], state_round=3)
+    assert c.all() and st["flags"] & 1 and st["cont"] == 0
+
+
+# ------------------------------------------------------------------ self-conditioning
+@pytest.mark.parametrize("dtype,d", [("bf16", 256), ("bf16", 2560), ("f32", 256)])
+def test_selfcond(dtype, d):
+    dlm = _dlm()
+    _say(f"selfcond dtype={dtype} d={d}")
+    seed, V, rows = 1234, 500, 32
+    E = synth.stored_normal(seed, "sc.E", (V, d), 0.02, dtype)
+    m = synth.stored_normal(seed, "sc.m", (d,), 0.02, dtype)
+    W = synth.stored_normal(seed, "sc.W", (d, d), 0.02, dtype)
+    pe = synth.normal_f32(seed, "sc.pe", (rows, d), 0.02)
+    committed = synth.committed_mask(seed, rows, 10)
+    tokens = synth.uniform_ints(seed, "sc.tok", rows, V) * committed
+    Wd = storage(W, dtype)
+    wsc = dlm.pack_matrix(Wd) if dtype == "bf16" else Wd
+    x = dlm.selfcond(torch.from_numpy(tokens).cuda(), torch.from_numpy(committed).cuda(), storage(E, dtype),
+                     storage(m, dtype), wsc, dev_f32(pe))
+    x0 = dlm.selfcond(torch.from_numpy(tokens).cuda(), torch.from_numpy(committed).cuda(), storage(E, dtype),
+                      storage(m, dtype), wsc, None)
+    torch.cuda.synchronize()
+    shape = synth.small_shape(synth.TINY, d=d, vocab=V)
+    om = oracle.OracleModel(shape, {"emb": E, "mask_emb": m, "w_sc": W}, Prec(dtype))
+    ref = oracle.selfcond(om, tokens, committed, pe.astype(np.float64), Prec(dtype))
+    ref0 = oracle.selfcond(om, tokens, committed, None, Prec(dtype))
+    np.testing.assert_allclose(x.cpu().numpy(), ref, atol=1e-5, rtol=1e-4)
+    np.testing.assert_array_equal(x0.cpu().numpy(), ref0.astype(np.float32))
+
+
+# ------------------------------------------------------------------ skinny GEMM (stream-K)
+@pytest.mark.parametrize("m,n,k", [(32, 19456, 2560), (32, 6144, 2560), (32, 2560, 4096), (32, 2560, 9728),
+                                   (7, 96, 64), (1, 32, 32), (32, 64, 4128)])
+def test_linear_matches_fp64(m, n, k):
+    dlm = _dlm()
+    _say(f"linear m={m} n={n} k={k}")
+    seed = 1234
+    W = synth.stored_normal(seed, "lin.W", (n, k), 0.02, "bf16")
+    X = synth.stored_normal(seed, "lin.X", (32, k), 1.0, "bf16")
+    Wp = dlm.pack_matrix(dev_bf16(W))
+    Xp = dlm.pack_activations(dev_bf16(X)[:m].contiguous())
+    y = dlm.linear(Wp, Xp, m=m)
+    torch.cuda.synchronize()
+    ref = oracle.decode_storage(X)[:m] @ oracle.decode_storage(W).T
+    got = y.cpu().numpy()
+    scale = np.sqrt(k) * 0.02
+    np.testing.assert_allclose(got, ref, atol=2e-5 * scale * 10, rtol=1e-5)
+    # deterministic: a second call gives the same bits
+    y2 = dlm.linear(Wp, Xp, m=m)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
