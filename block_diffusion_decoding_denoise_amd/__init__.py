@@ -170,7 +170,7 @@ def _dev(t: torch.Tensor, name: str):
 def block_attn(q, k_cache, v_cache, prefix_len, out=None, prefix_len_dev=None, max_prefix_len=None,
                scale=None, ws=None):
     """o = softmax(q K^T * scale) V over the L prefix keys and the B block keys (no mask).
-    q [B, hq, D]; k_cache/v_cache [hkv, cap, D]; returns out [B, hq, D]."""
+    q [B, hq, D]; k_cache [hkv, cap, D]; v_cache transposed [hkv, D, cap]; returns out [B, hq, D]."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
     B, hq, D = q.shape
@@ -315,7 +315,8 @@ class Model:
         tdt = torch.bfloat16 if dt == DLM_BF16 else torch.float32
         self.cap = cap
         self.k = [torch.zeros(s.hkv, cap, s.head_dim, dtype=tdt, device=device) for _ in range(s.n_layers)]
-        self.v = [torch.zeros(s.hkv, cap, s.head_dim, dtype=tdt, device=device) for _ in range(s.n_layers)]
+        # V is cached transposed, [hkv, D, cap]
+        self.v = [torch.zeros(s.hkv, s.head_dim, cap, dtype=tdt, device=device) for _ in range(s.n_layers)]
         self._kptrs = (ctypes.c_void_p * s.n_layers)(*[t.data_ptr() for t in self.k])
         self._vptrs = (ctypes.c_void_p * s.n_layers)(*[t.data_ptr() for t in self.v])
         self.len_dev = torch.zeros(1, dtype=torch.int32, device=device)

@@ -652,7 +652,10 @@ static int enqueue_round(const dlm_model* m, const dlm_commit_rule& rule, const 
   const dlm_model_desc& d = m->d;
   const int bf = d.dtype == DLM_BF16;
   const int B = d.block;
-  const int32_t* cont = &state->cont;
+  // A fixed-k rule enqueues exactly the rounds the block needs, so its kernels need not read
+  // the continue flag; a threshold rule enqueues max_rounds rounds and every kernel of a round
+  // after the block completed exits at once.
+  const int32_t* cont = rule.mode == DLM_COMMIT_FIXED_K ? nullptr : &state->cont;
   int rc;
   // round input: E[tok] for committed rows, mask + W_sc bf(pe) for open rows
   if ((rc = selfcond_prep(w.pe, w.committed, w.xsc, B, d.d, bf, cont, st))) return rc;

@@ -123,11 +123,12 @@ __device__ inline void epi_qk_rope(const EpiParams& e, int m, int part, int head
   }
 }
 
+// the V cache is stored transposed, [kv head, D, cap]
 __device__ inline void epi_v(const EpiParams& e, int m, int rel, float v) {
   const int L = prefix_len(e);
   if (L + m >= e.cap) return;
   const int head = rel / e.D, j = rel % e.D;
-  store_act(e.v_cache, ((size_t)head * e.cap + (L + m)) * e.D + j, v, e.bf16_out);
+  store_act(e.v_cache, ((size_t)head * e.D + j) * e.cap + (L + m), v, e.bf16_out);
 }
 
 __device__ inline void epi_swiglu(const EpiParams& e, int m, int j, float g, float u) {

@@ -310,13 +310,34 @@ __global__ __launch_bounds__(256) void head_f32_kernel(HeadP p) {
   if (tid < p.d) p.pe_part[((size_t)chunk * p.rows_max + k) * p.d + tid] = pacc;
 }
 
-// combine: one workgroup (256 threads) per (output row, 256-wide d slice)
+// combine: one workgroup (256 threads) per (output row, 256-wide d slice).  Thread c loads
+// chunk c's statistics; the chunk statistics are merged with fixed-order tree reductions, and
+// the pe partials are read 16 chunks at a time so the loads overlap.
+__device__ inline float block_max(float v, float* red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ inline float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(256) void head_combine_kernel(HeadP p, int bf16_path) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   __shared__ int s_idx[DLM_MAX_ROWS];
   __shared__ float wts[256];
-  __shared__ float s_stats[4];
-  __shared__ int s_best;
+  __shared__ float red[4];
+  __shared__ float redv[4];
+  __shared__ int redi[4];
   const int n_open = compact_open(p.committed, p.rows, s_idx);
   const int dblocks = (p.d + 255) / 256;
   const int row = blockIdx.x / dblocks, db = blockIdx.x % dblocks;
@@ -337,45 +358,55 @@ __global__ __launch_bounds__(256) void head_combine_kernel(HeadP p, int bf16_pat
   for (int i = 0; i < row; ++i) k += (p.committed == nullptr || p.committed[i] == 0) ? 1 : 0;
   const int n_groups = (n_open + 15) / 16;
   const int CH = bf16_path ? n_chunks_for(n_groups, 0) : p.chunks_fixed;
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < CH; ++c) M = fmaxf(M, p.st[((size_t)c * p.rows_max + k) * 8 + ST_M]);
-    float S = 0.f, T = 0.f, bvv = -INFINITY;
-    int bii = 0x7fffffff;
-    for (int c = 0; c < CH; ++c) {
-      const float* st = p.st + ((size_t)c * p.rows_max + k) * 8;
-      if (st[ST_S] > 0.f) {
-        const float f = expf(st[ST_M] - M);
-        S += f * st[ST_S];
-        T += f * (st[ST_T] + (st[ST_M] - M) * st[ST_S]);
-      }
-      const float cv = st[ST_BV];
-      const int ci = __float_as_int(st[ST_BI]);
-      if (cv > bvv || (cv == bvv && ci < bii)) { bvv = cv; bii = ci; }
-    }
-    s_stats[0] = M;
-    s_stats[1] = S;
-    s_stats[2] = T;
-    s_best = bii;
+  float cm = -INFINITY, cs = 0.f, ct = 0.f, cbv = -INFINITY;
+  int cbi = 0x7fffffff;
+  if (tid < CH) {
+    const float* st = p.st + ((size_t)tid * p.rows_max + k) * 8;
+    cm = st[ST_M];
+    cs = st[ST_S];
+    ct = st[ST_T];
+    cbv = st[ST_BV];
+    cbi = __float_as_int(st[ST_BI]);
   }
+  const float M = block_max(cm, red);
+  const float f = cs > 0.f ? expf(cm - M) : 0.f;
+  const float S = block_sum(f * cs, red);
+  const float T = block_sum(cs > 0.f ? f * (ct + (cm - M) * cs) : 0.f, red);
+  // argmax over chunks: largest value, lowest id on ties
+  float bv = cbv;
+  int bi = cbi;
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  }
+  if ((tid & 63) == 0) { redv[tid >> 6] = bv; redi[tid >> 6] = bi; }
   __syncthreads();
-  const float M = s_stats[0], S = s_stats[1], T = s_stats[2];
   if (db == 0 && tid == 0) {
+    float fbv = redv[0];
+    int fbi = redi[0];
+    for (int q = 1; q < 4; ++q)
+      if (redv[q] > fbv || (redv[q] == fbv && redi[q] < fbi)) { fbv = redv[q]; fbi = redi[q]; }
     const float lnS = logf(S);
     p.lse[row] = M + lnS;
     p.ent[row] = lnS - T / S;
     p.maxp[row] = 1.0f / S;
-    p.amax[row] = (s_best >= 0 && s_best < p.V) ? s_best : 0;   // all-NaN rows still name a valid id
+    p.amax[row] = (fbi >= 0 && fbi < p.V) ? fbi : 0;   // all-NaN rows still name a valid id
   }
   if (!p.pe) return;
-  for (int c = tid; c < CH; c += 256) {
-    const float* st = p.st + ((size_t)c * p.rows_max + k) * 8;
-    wts[c] = st[ST_S] > 0.f ? expf(st[ST_M] - M) / S : 0.f;
-  }
+  if (tid < CH) wts[tid] = f / S;
   __syncthreads();
   if (dcol < p.d) {
+    const float* base = p.pe_part + (size_t)k * p.d + dcol;
+    const size_t cstride = (size_t)p.rows_max * p.d;
     float a = 0.f;
-    for (int c = 0; c < CH; ++c) a = fmaf(wts[c], p.pe_part[((size_t)c * p.rows_max + k) * p.d + dcol], a);
+    for (int c0 = 0; c0 < CH; c0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = c0 + j < CH ? base[(size_t)(c0 + j) * cstride] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = fmaf(c0 + j < CH ? wts[c0 + j] : 0.f, v[j], a);
+    }
     p.pe[(size_t)row * p.d + dcol] = a;
   }
 }

@@ -22,20 +22,42 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const float* x = p.x + (size_t)row * p.d;
+  // every load of the row is issued before any arithmetic (d <= 4096: <= 4 float4 per thread)
+  constexpr int MAXV = 4;
+  f32x4_t xv[MAXV];
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int c = 4 * (tid + 256 * j);
+    xv[j] = c < p.d ? *(const f32x4_t*)(x + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   float s = 0.f;
-  for (int i = tid; i < p.d; i += 256) s = fmaf(x[i], x[i], s);
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s = fmaf(xv[j][e], xv[j][e], s);
   s = wave_sum(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
   const float tot = ((red[0] + red[1]) + red[2]) + red[3];
   const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
-  for (int i = tid; i < p.d; i += 256) {
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int c = 4 * (tid + 256 * j);
+    if (c >= p.d) continue;
     if (p.bf16) {
-      const float g = bf2f(((const uint16_t*)p.g)[i]);
-      ((uint16_t*)p.out)[p.packed ? xpk_index(row, i) : (size_t)row * p.d + i] = f2bf(x[i] * r * g);
+      const uint2 gw = *(const uint2*)((const uint16_t*)p.g + c);
+      const float g4[4] = {lo_bf(gw.x), hi_bf(gw.x), lo_bf(gw.y), hi_bf(gw.y)};
+      uint2 ow;
+      ow.x = (uint32_t)f2bf(xv[j][0] * r * g4[0]) | ((uint32_t)f2bf(xv[j][1] * r * g4[1]) << 16);
+      ow.y = (uint32_t)f2bf(xv[j][2] * r * g4[2]) | ((uint32_t)f2bf(xv[j][3] * r * g4[3]) << 16);
+      // 4 consecutive columns stay contiguous in the packed operand order
+      *(uint2*)((uint16_t*)p.out + (p.packed ? xpk_index(row, c) : (size_t)row * p.d + c)) = ow;
     } else {
-      const float g = ((const float*)p.g)[i];
-      ((float*)p.out)[(size_t)row * p.d + i] = x[i] * r * g;
+      const f32x4_t g4 = *(const f32x4_t*)((const float*)p.g + c);
+      f32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = xv[j][e] * r * g4[e];
+      *(f32x4_t*)((float*)p.out + (size_t)row * p.d + c) = o;
     }
   }
 }

@@ -72,7 +72,9 @@ const char* dlm_last_error(void);
  *
  *   q        [B, hq, D]     query rows, RoPE already applied.
  *   k_cache  [hkv, cap, D]  keys; rows [0, L) are the prefix, [L, L+B) the block.
- *   v_cache  [hkv, cap, D]  values, same layout.
+ *   v_cache  [hkv, D, cap]  values, stored transposed (column j of key position t at
+ *                           v_cache[h][j][t]) so that consecutive keys of one value column
+ *                           are contiguous; positions as for k_cache.
  *   out      [B, hq, D]     o = softmax(scale * q k^T) v, same dtype as q.
  *   L is desc->prefix_len, or *desc->prefix_len_dev when that device pointer is non-null
  *   (so a captured graph can replay with a growing prefix).  Shapes: D in {64, 128},
@@ -256,7 +258,8 @@ int dlm_pack_model(const dlm_model_desc* desc, const void* w_sc, const dlm_layer
                    void* dst, void* row_map_ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
- * KV cache.  k[l], v[l]: device bases of layer l, each [hkv, cap, D] (model dtype).
+ * KV cache.  k[l]: device base of layer l's keys [hkv, cap, D]; v[l]: its values stored
+ * transposed, [hkv, D, cap] (model dtype).
  * len_dev: device int32 holding the committed prefix length L.
  * ------------------------------------------------------------------------------------ */
 typedef struct {

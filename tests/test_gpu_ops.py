@@ -78,7 +78,8 @@ def _attn_case(dtype, hq, hkv, D, B, L, cap, seed):
     q = synth.stored_normal(seed, "attn.q", (B, hq, D), 1.0, dtype)
     k = synth.stored_normal(seed, "attn.k", (hkv, cap, D), 1.0, dtype)
     v = synth.stored_normal(seed, "attn.v", (hkv, cap, D), 1.0, dtype)
-    out = dlm.block_attn(storage(q, dtype), storage(k, dtype), storage(v, dtype), L)
+    vt = np.ascontiguousarray(np.swapaxes(v, 1, 2))       # the library's V cache is [hkv, D, cap]
+    out = dlm.block_attn(storage(q, dtype), storage(k, dtype), storage(vt, dtype), L)
     torch.cuda.synchronize()
     qf, kf, vf = (oracle.decode_storage(a) for a in (q, k, v))
     ref = o_attn(qf, kf[:, :L + B], vf[:, :L + B], 1 / math.sqrt(D))
@@ -213,3 +214,10 @@ def test_linear_matches_fp64(m, n, k):
     y2 = dlm.linear(Wp, Xp, m=m)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("L", [512, 4096, 32768])
+def test_attn_bf16_full_size(L):
+    """The attention op at the block-attention workload's sizes: 32/8 heads of 128, a block
+    of 32 queries, prefix L (every query, every head compared with the oracle)."""
+    _attn_case("bf16", 32, 8, 128, 32, L, L + 32, 1234)
