@@ -125,31 +125,34 @@ def main():
         log(f"k={k}: {results[k]['tok_s']:.0f} tok/s, {results[k]['rounds_s']:.0f} rounds/s, "
             f"{results[k]['ms_per_block']:.2f} ms/block, {100 * results[k]['hbm_frac']:.1f}% of 8 TB/s")
 
-    # ---- dominant kernel: the gate/up projection GEMM, timed alone with HIP events on its stream
+    # ---- dominant kernel: the FFN gate/up projection + SwiGLU, the round's largest weight
+    # stream, launched alone exactly as inside the round (dlm_ffn_gate_up: same kernel, plan
+    # and packed weights), cycling through the 36 layers so no launch finds its weights in a
+    # cache, timed with HIP events on the stream the launches go to.
     s = shape
-    Wgu = (torch.randn(2 * s.ffn, s.d, device="cuda") * 0.02).to(torch.bfloat16)
-    Wp = dlm.pack_matrix(Wgu)
     x = dlm.pack_activations((torch.randn(32, s.d, device="cuda") * 0.1).to(torch.bfloat16))
-    y = torch.empty(32, 2 * s.ffn, device="cuda")
-    lws = torch.zeros(dlm.lib().dlm_linear_ws_bytes(2 * s.ffn, s.d), dtype=torch.uint8, device="cuda")
-    for _ in range(3):
-        dlm.linear(Wp, x, y=y, ws=lws)
+    act = torch.empty(32, s.ffn, dtype=torch.bfloat16, device="cuda")
+    gws = torch.zeros(max(dlm.lib().dlm_ffn_gate_up_ws_bytes(model.handle), 256), dtype=torch.uint8, device="cuda")
+    for l in range(s.n_layers):
+        model.ffn_gate_up(l, x, act=act, ws=gws)
     torch.cuda.synchronize()
-    n_rep = 50
+    n_cycles = 4
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for _ in range(n_rep):
-        dlm.linear(Wp, x, y=y, ws=lws)
+    for _ in range(n_cycles):
+        for l in range(s.n_layers):
+            model.ffn_gate_up(l, x, act=act, ws=gws)
     ev1.record()
     torch.cuda.synchronize()
-    t_launch = ev0.elapsed_time(ev1) / 1e3 / n_rep
-    gemm_bytes = 2 * (2 * s.ffn * s.d) + 2 * 32 * s.d + 4 * 32 * 2 * s.ffn
+    n_launch = n_cycles * s.n_layers
+    t_launch = ev0.elapsed_time(ev1) / 1e3 / n_launch
+    gemm_bytes = 2 * (2 * s.ffn * s.d) + 2 * 32 * s.d + 2 * 32 * s.ffn
     roofline = {"bound": "hbm", "achieved": gemm_bytes / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": gemm_bytes / t_launch / HBM_PEAK, "traffic": None,
-                "kernel": "gemm_bf16_kernel (gate/up projection, N=19456, K=2560, M=32)",
-                "bytes_per_launch": gemm_bytes, "us_per_launch": t_launch * 1e6}
-    log(f"gate/up GEMM: {t_launch * 1e6:.1f} us/launch, {roofline['achieved']:.0f} GB/s")
+                "kernel": "gemm_owned_kernel<3, 8> (FFN gate/up + SwiGLU, N=19456, K=2560, M=32)",
+                "bytes_per_launch": gemm_bytes, "us_per_launch": t_launch * 1e6, "launches": n_launch}
+    log(f"gate/up + SwiGLU: {t_launch * 1e6:.1f} us/launch, {roofline['achieved']:.0f} GB/s")
 
     # ---- CPU baseline: the oracle in float32 on a bounded sample (one round + one commit pass)
     cpu = None

@@ -126,6 +126,8 @@ def lib():
         "dlm_decode_round": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, sz, vp]),
         "dlm_decode_begin": (i, [vp, P(KV), vp, vp, vp, sz, vp]),
         "dlm_commit_pass": (i, [vp, P(KV), vp, vp, sz, vp]),
+        "dlm_ffn_gate_up_ws_bytes": (sz, [vp]),
+        "dlm_ffn_gate_up": (i, [vp, i, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -352,6 +354,18 @@ class Model:
         itemsize = torch.tensor([], dtype=dtype).element_size()
         off = ptr - self.ws.data_ptr()
         return self.ws[off:off + n * itemsize].view(dtype).view(*shape)
+
+    def ffn_gate_up(self, layer, x_packed, act=None, ws=None):
+        """The round's gate/up + SwiGLU sublayer of `layer` alone: packed bf16 32 x d in,
+        packed bf16 32 x ffn out (dlm_ffn_gate_up)."""
+        if act is None:
+            act = torch.empty(32, self.shape.ffn, dtype=torch.bfloat16, device=x_packed.device)
+        if ws is None:
+            ws = torch.zeros(max(lib().dlm_ffn_gate_up_ws_bytes(self.handle), 256), dtype=torch.uint8,
+                             device=x_packed.device)
+        _check(lib().dlm_ffn_gate_up(self.handle, layer, _ptr(x_packed), _ptr(act), _ptr(ws), ws.numel(),
+                                     _stream()), "dlm_ffn_gate_up")
+        return act
 
     def set_len(self, n):
         self.len_dev.fill_(int(n))

@@ -332,13 +332,13 @@ static void layout_packed(dlm_model* m) {
   }
   m->packed_bytes = d.dtype == DLM_BF16 ? off : 0;
   m->pl_sc = gemm_plan(d.d, d.d);
-  m->pl_qkv = gemm_plan(m->n_qkv, d.d);
+  m->pl_qkv = gemm_plan_owned(m->n_qkv, d.d);
   m->pl_o = gemm_plan(d.d, d.hq * D);
   if (d.n_experts == 0) {
-    m->pl_gu = gemm_plan(2 * d.ffn, d.d);
+    m->pl_gu = gemm_plan_owned(2 * d.ffn, d.d);
     m->pl_dn = gemm_plan(d.d, d.ffn);
   } else {
-    m->pl_gu = m->pl_dn = GemmPlan{1, 1};
+    m->pl_gu = m->pl_dn = GemmPlan{1, 1, 0};
   }
 }
 
@@ -402,17 +402,25 @@ extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const d
     const dlm_layer_weights& L = layers[l];
     const void* s3[3] = {L.wq, L.wk, L.wv};
     int r3[3] = {d->hq * D, d->hkv * D, d->hkv * D};
-    if ((rc = pack_bf16(s3, r3, 3, m.n_qkv, d->d, map_qkv, out + m.off_qkv[l], st))) return rc;
+    rc = m.pl_qkv.R ? pack_bf16_owned(s3, r3, 3, m.n_qkv, d->d, map_qkv, m.pl_qkv.R, out + m.off_qkv[l], st)
+                    : pack_bf16(s3, r3, 3, m.n_qkv, d->d, map_qkv, out + m.off_qkv[l], st);
+    if (rc) return rc;
     const void* so[1] = {L.wo};
     int ro[1] = {d->d};
-    if ((rc = pack_bf16(so, ro, 1, d->d, d->hq * D, nullptr, out + m.off_o[l], st))) return rc;
+    rc = m.pl_o.R ? pack_bf16_owned(so, ro, 1, d->d, d->hq * D, nullptr, m.pl_o.R, out + m.off_o[l], st)
+                  : pack_bf16(so, ro, 1, d->d, d->hq * D, nullptr, out + m.off_o[l], st);
+    if (rc) return rc;
     if (d->n_experts == 0) {
       const void* s2[2] = {L.wg, L.wu};
       int r2[2] = {d->ffn, d->ffn};
-      if ((rc = pack_bf16(s2, r2, 2, 2 * d->ffn, d->d, map_gu, out + m.off_gu[l], st))) return rc;
+      rc = m.pl_gu.R ? pack_bf16_owned(s2, r2, 2, 2 * d->ffn, d->d, map_gu, m.pl_gu.R, out + m.off_gu[l], st)
+                     : pack_bf16(s2, r2, 2, 2 * d->ffn, d->d, map_gu, out + m.off_gu[l], st);
+      if (rc) return rc;
       const void* sd[1] = {L.wd};
       int rd[1] = {d->d};
-      if ((rc = pack_bf16(sd, rd, 1, d->d, d->ffn, nullptr, out + m.off_dn[l], st))) return rc;
+      rc = m.pl_dn.R ? pack_bf16_owned(sd, rd, 1, d->d, d->ffn, nullptr, m.pl_dn.R, out + m.off_dn[l], st)
+                     : pack_bf16(sd, rd, 1, d->d, d->ffn, nullptr, out + m.off_dn[l], st);
+      if (rc) return rc;
     }
   }
   return DLM_OK;
@@ -554,17 +562,22 @@ extern "C" int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* 
 // ------------------------------------------------------------------ the forward pass
 // Runs the block's residual stream x through every layer.  last_kv_only: the last layer
 // stops after its K/V are written (commit pass).
+// The bf16 residual projections (attention output, FFN down) leave their sums as deferred
+// GEMM partials, which the next RMSNorm adds into the residual stream; *pending describes the
+// partials still to be added after the last layer (base == nullptr: none).
 static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& w, const int32_t* cont,
-                          bool last_kv_only, hipStream_t st) {
+                          bool last_kv_only, hipStream_t st, PartialSrc* pending) {
   const dlm_model_desc& d = m->d;
   const int bf = d.dtype == DLM_BF16;
   const int B = d.block, D = d.head_dim, qd = d.hq * D;
   const char* pk = (const char*)m->packed;
   int rc;
+  PartialSrc ps{};
   for (int l = 0; l < d.n_layers; ++l) {
     const dlm_layer_weights& L = m->layers[l];
     const bool last = l == d.n_layers - 1;
-    if ((rc = rmsnorm(w.x, L.attn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st))) return rc;
+    if ((rc = rmsnorm(w.x, L.attn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st, &ps))) return rc;
+    ps.base = nullptr;
     EpiParams e = epi_zero();
     e.kind = EPI_QKV_ROPE;
     e.M = B;
@@ -596,20 +609,23 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
                        D, B, kv->cap, scale, kv->len_dev, 0, cont, st);
     if (rc) return rc;
     e = epi_zero();
-    e.kind = EPI_RESID;
+    e.kind = bf && !m->pl_o.R ? EPI_PARTIAL : EPI_RESID;
     e.M = B;
     e.bf16_out = bf;
     e.out = w.x;
     e.ld_out = d.d;
     e.cont_dev = cont;
-    if (bf) rc = gemm_bf16(pk + m->off_o[l], w.o, d.d, qd, MAP_IDENTITY, e, m->pl_o, w.gemm_ws, st);
-    else {
+    if (bf) {
+      rc = gemm_bf16(pk + m->off_o[l], w.o, d.d, qd, MAP_IDENTITY, e, m->pl_o, w.gemm_ws, st);
+      if (!m->pl_o.R) ps = gemm_partials(d.d, qd, m->pl_o, w.gemm_ws);
+    } else {
       F32Mats W{};
       W.w[0] = (const float*)L.wo; W.rows[0] = d.d;
       rc = gemm_f32(W, (const float*)w.o, d.d, qd, MAP_IDENTITY, e, st);
     }
     if (rc) return rc;
-    if ((rc = rmsnorm(w.x, L.ffn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st))) return rc;
+    if ((rc = rmsnorm(w.x, L.ffn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st, &ps))) return rc;
+    ps.base = nullptr;
     if (d.n_experts) {
       if ((rc = moe_ffn(d, L, w.xn, w.x, B, w.moe_ws, cont, st))) return rc;
       continue;
@@ -630,20 +646,23 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     }
     if (rc) return rc;
     e = epi_zero();
-    e.kind = EPI_RESID;
+    e.kind = bf && !m->pl_dn.R ? EPI_PARTIAL : EPI_RESID;
     e.M = B;
     e.bf16_out = bf;
     e.out = w.x;
     e.ld_out = d.d;
     e.cont_dev = cont;
-    if (bf) rc = gemm_bf16(pk + m->off_dn[l], w.act, d.d, d.ffn, MAP_IDENTITY, e, m->pl_dn, w.gemm_ws, st);
-    else {
+    if (bf) {
+      rc = gemm_bf16(pk + m->off_dn[l], w.act, d.d, d.ffn, MAP_IDENTITY, e, m->pl_dn, w.gemm_ws, st);
+      if (!m->pl_dn.R) ps = gemm_partials(d.d, d.ffn, m->pl_dn, w.gemm_ws);
+    } else {
       F32Mats W{};
       W.w[0] = (const float*)L.wd; W.rows[0] = d.d;
       rc = gemm_f32(W, (const float*)w.act, d.d, d.ffn, MAP_IDENTITY, e, st);
     }
     if (rc) return rc;
   }
+  *pending = ps;
   return DLM_OK;
 }
 
@@ -680,8 +699,9 @@ static int enqueue_round(const dlm_model* m, const dlm_commit_rule& rule, const 
     rc = gemm_f32(W, (const float*)w.xsc, d.d, d.d, MAP_IDENTITY, e, st);
   }
   if (rc) return rc;
-  if ((rc = enqueue_layers(m, kv, w, cont, false, st))) return rc;
-  if ((rc = rmsnorm(w.x, m->final_norm, w.hn, B, d.d, bf, 0, d.eps, cont, st))) return rc;
+  PartialSrc ps{};
+  if ((rc = enqueue_layers(m, kv, w, cont, false, st, &ps))) return rc;
+  if ((rc = rmsnorm(w.x, m->final_norm, w.hn, B, d.d, bf, 0, d.eps, cont, st, &ps))) return rc;
   if ((rc = head_launch(d.dtype, w.hn, m->emb, w.committed, B, d.d, d.vocab, w.lse, w.ent, w.maxp, w.amax, w.pe,
                         nullptr, w.head_ws, cont, st)))
     return rc;
@@ -693,7 +713,8 @@ static int enqueue_commit_pass(const dlm_model* m, const dlm_kv* kv, const int32
   const dlm_model_desc& d = m->d;
   int rc;
   if ((rc = embed(tokens, m->emb, w.x, d.block, d.d, d.vocab, d.dtype == DLM_BF16, st))) return rc;
-  if ((rc = enqueue_layers(m, kv, w, nullptr, true, st))) return rc;
+  PartialSrc ps{};
+  if ((rc = enqueue_layers(m, kv, w, nullptr, true, st, &ps))) return rc;
   return len_add(kv->len_dev, d.block, st);
 }
 
@@ -721,6 +742,30 @@ static int check_decode(const dlm_model* m, const dlm_kv* kv, void* ws, size_t w
   DLM_REQUIRE(ws && aligned16(ws), DLM_ERR_ARG, "workspace null or misaligned");
   DLM_REQUIRE(ws_bytes >= decode_layout(m, kv, nullptr).total, DLM_ERR_WORKSPACE, "workspace too small");
   return DLM_OK;
+}
+
+extern "C" size_t dlm_ffn_gate_up_ws_bytes(const dlm_model* m) {
+  if (!m || m->d.dtype != DLM_BF16 || m->d.n_experts) return 0;
+  return gemm_ws_bytes(2 * m->d.ffn, m->d.d, m->pl_gu);
+}
+
+extern "C" int dlm_ffn_gate_up(const dlm_model* m, int layer, const void* x_packed, void* act_packed, void* ws,
+                               size_t ws_bytes, void* stream) {
+  DLM_REQUIRE(m && x_packed && act_packed && ws, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(m->d.dtype == DLM_BF16 && m->d.n_experts == 0, DLM_ERR_DTYPE, "dense bf16 models only");
+  DLM_REQUIRE(layer >= 0 && layer < m->d.n_layers, DLM_ERR_ARG, "layer out of range");
+  DLM_REQUIRE(aligned16(x_packed) && aligned16(act_packed) && aligned16(ws), DLM_ERR_ARG,
+              "16-byte alignment required");
+  DLM_REQUIRE(ws_bytes >= dlm_ffn_gate_up_ws_bytes(m), DLM_ERR_WORKSPACE, "workspace too small");
+  DLM_DEVICE_CHECK();
+  EpiParams e = epi_zero();
+  e.kind = EPI_SWIGLU;
+  e.M = m->d.block;
+  e.bf16_out = 1;
+  e.act_out = act_packed;
+  e.F = m->d.ffn;
+  return gemm_bf16((const char*)m->packed + m->off_gu[layer], x_packed, 2 * m->d.ffn, m->d.d, MAP_GU, e, m->pl_gu,
+                   ws, (hipStream_t)stream);
 }
 
 extern "C" int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv, int32_t* tokens,

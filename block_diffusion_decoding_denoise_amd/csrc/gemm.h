@@ -10,6 +10,15 @@ enum EpiKind {
   EPI_QKV_ROPE = 2,    // q/k rotated at position L + m, q -> q_out, k/v -> caches at row L + m
   EPI_SWIGLU = 3,      // act[m][j] = silu(gate_j) * up_j
   EPI_SELFCOND = 4,    // out[m][n] = committed[m] ? E[tok[m]][n] : mask[n] + acc
+  EPI_PARTIAL = 5,     // deferred: each workgroup stores its partial sums; a consumer adds them
+};
+
+// Where a deferred GEMM left its partial sums: tile t (32 output columns) has contributors
+// c = 0 .. cnt(t)-1, with cnt(t) from the stream-K split (see contributors()), and value
+// (m, n) of contributor c at base[(t * cmax + c) * 1024 + m * 32 + n % 32].
+struct PartialSrc {
+  const float* base;   // nullptr: no partials
+  int tiles, KT, NW, cmax;
 };
 
 // Logical row orders of the fused matrices (packed row order is described in gemm.hip):
@@ -47,7 +56,8 @@ struct EpiParams {
 
 struct GemmPlan {
   int tpw;      // (unused, 1)
-  int splits;   // number of stream-K workers (waves)
+  int splits;   // number of workgroups
+  int R;        // row-owned mode: output rows per workgroup (weights packed for it); 0: stream-K
 };
 
 // Packed-row -> logical-row map used when packing (host side).
@@ -59,8 +69,14 @@ void build_row_map(int kind, int n_rows, int hq, int hkv, int D, int F, int32_t*
 // partial/counters: workspace (counters zero before the first use; left zero).
 size_t gemm_ws_bytes(int N, int K, GemmPlan plan);
 GemmPlan gemm_plan(int N, int K);
+// Row-owned plan when N splits into equal even row blocks over enough workgroups (the weights
+// must then be packed with pack_bf16_owned and this plan's R), else the stream-K plan.
+GemmPlan gemm_plan_owned(int N, int K);
 int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const EpiParams& ep,
               GemmPlan plan, void* ws, hipStream_t st);
+// Partial sums left in ws by a gemm_bf16 call with kind EPI_PARTIAL (valid until the next GEMM
+// on the same workspace).
+PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws);
 
 // f32 path (natural [out, in] weights).  Up to 3 source matrices make the logical rows.
 struct F32Mats {
@@ -73,5 +89,8 @@ int gemm_f32(const F32Mats& W, const float* X, int N, int K, int map_kind, const
 // Pack rows row_map[i] of the virtual concatenation of up to 3 bf16 matrices into dst.
 int pack_bf16(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
               const int32_t* row_map_dev, void* dst, hipStream_t st);
+// The same rows in the row-owned layout of a plan with R rows per workgroup.
+int pack_bf16_owned(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
+                    const int32_t* row_map_dev, int R, void* dst, hipStream_t st);
 
 }  // namespace dlm

@@ -158,10 +158,16 @@ __device__ inline void epi_pair_packed(const EpiParams& e, int map, int p, int m
 }
 
 // ------------------------------------------------------------------ bf16 kernel
+// Workspace: a fixed block of per-tile counters at the start (shared by every GEMM that uses
+// the same workspace; each GEMM leaves its counters at zero), then the partial sums.
+constexpr int kMaxTiles = 4096;
+constexpr size_t kCounterBytes = kMaxTiles * 4;
+
 struct GemmP {
   const uint16_t* W;
   const uint16_t* X;
   int K, KT, tiles, NW, cmax, map;
+  int R;             // row-owned mode: rows per workgroup (0: stream-K)
   float* partial;    // [tiles][cmax][16][64]
   int* counters;     // [tiles]
   EpiParams ep;
@@ -183,16 +189,27 @@ __device__ inline void epilogue_quarter(const GemmP& p, int t, const float (&v4)
   }
 }
 
-// A workgroup is one stream-K worker: it owns the contiguous unit range [s0, s1) (at most K/16
-// units, so at most two tiles); its 4 waves take every 4th unit of it, then the wave results
-// are added in LDS (fixed order).  A tile the workgroup owns entirely gets its epilogue here;
-// otherwise the workgroup stores its partial and the last contributor of the tile adds all
-// partials in contributor order.
+// A workgroup is one stream-K worker: it owns the contiguous unit range [s0, s1), which covers
+// at most MAXSEG tile segments (first and last possibly partial); its 4 waves take every 4th
+// unit of it, each wave parks its accumulator in LDS at every tile boundary, and the wave
+// results are added in LDS in a fixed order.  Then, per segment: with deferred output the sum
+// is stored as this workgroup's partial and a later kernel adds the partials; otherwise a tile
+// the workgroup owns entirely gets its epilogue here, and a shared tile is finished by its last
+// contributor, which adds all partials in contributor order.
+constexpr int MAXSEG = 4;
+
+__device__ inline int contributors(const GemmP& p, int t, long long T, int* first) {
+  const int fo = owner_of((long long)t * p.KT, T, p.NW);
+  const int lo = owner_of((long long)(t + 1) * p.KT - 1, T, p.NW);
+  *first = fo;
+  return lo - fo + 1;
+}
+
 template <int P>
-__global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmP p) {
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmP p) {
   if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
-  __shared__ float red[4][2][16][64];
-  __shared__ int s_last[2];
+  __shared__ float red[4][MAXSEG][16][64];
+  __shared__ int s_last[MAXSEG];
   const int lane = threadIdx.x & 63;
   const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x;
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmP p) {
   int kpf = (s0 + v) % p.KT;   // step-in-tile of the next unit this wave prefetches
 #pragma unroll
   for (int u = 0; u < P; ++u) {
-    wf[u] = bload16(wr, wo + (uint32_t)(v + 4 * u) * 1024u);
+    wf[u] = bload16_nt(wr, wo + (uint32_t)(v + 4 * u) * 1024u);
     xf[u] = bload16(xr, xo + (uint32_t)kpf * 1024u);
     kpf += 4;
     if (kpf >= p.KT) kpf %= p.KT;
@@ -216,45 +233,41 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmP p) {
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  // the WG's units [0, bnd) belong to tile t0, [bnd, n) to tile t0 + 1 (a WG owns at most K/16
-  // units); this wave's first unit of tile t0 + 1 is its ring step kb
   const int t0 = s0 / p.KT;
-  const int bnd = min(n, (t0 + 1) * p.KT - s0);
-  const int kb = bnd > v ? (bnd - v + 3) / 4 : 0;
-  int seg = kb == 0 ? 1 : 0;
-  if (kb == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[v][0][r][lane] = 0.f;
-  }
+  const int nseg = (s1 - 1) / p.KT - t0 + 1;
+  int seg = 0;
+  int nextb = (t0 + 1) * p.KT - s0;   // WG-relative unit where segment seg + 1 begins
   // streaming loop: no stores to global memory inside, so the ring's memory-counter waits
-  // stay exact; the switch to the second tile parks the accumulator in LDS
+  // stay exact; a tile boundary parks the accumulator in LDS
   for (int k0 = 0; k0 < nv; k0 += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
-      if (k0 + u == kb && seg == 0) {
+      const int unit = v + 4 * (k0 + u);
+      while (unit < n && unit >= nextb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          red[v][0][r][lane] = acc[r];
+          red[v][seg][r][lane] = acc[r];
           acc[r] = 0.f;
         }
-        seg = 1;
+        ++seg;
+        nextb += p.KT;
       }
       acc = mfma32x32x16(wf[u], xf[u], acc);
-      wf[u] = bload16(wr, wo + (uint32_t)(v + 4 * (k0 + u + P)) * 1024u);
+      wf[u] = bload16_nt(wr, wo + (uint32_t)(v + 4 * (k0 + u + P)) * 1024u);
       xf[u] = bload16(xr, xo + (uint32_t)kpf * 1024u);
       kpf += 4;
       if (kpf >= p.KT) kpf %= p.KT;
     }
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    red[v][seg][r][lane] = acc[r];
-    if (seg == 0) red[v][1][r][lane] = 0.f;
-  }
+  for (int r = 0; r < 16; ++r) red[v][seg][r][lane] = acc[r];
+  for (int sg = seg + 1; sg < nseg; ++sg)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[v][sg][r][lane] = 0.f;
   __syncthreads();
-  const int nseg = bnd < n ? 2 : 1;
-  bool need[2] = {false, false};
-  int cnt[2] = {1, 1};
+  bool need[MAXSEG];
+  int cnt[MAXSEG];
+  bool any = false;
   for (int sg = 0; sg < nseg; ++sg) {
     float sums[4];
 #pragma unroll
@@ -263,21 +276,26 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmP p) {
       sums[q] = ((red[0][sg][r][lane] + red[1][sg][r][lane]) + red[2][sg][r][lane]) + red[3][sg][r][lane];
     }
     const int t = t0 + sg;
-    const int fo = owner_of((long long)t * p.KT, T, p.NW), lo = owner_of((long long)(t + 1) * p.KT - 1, T, p.NW);
-    cnt[sg] = lo - fo + 1;
-    if (cnt[sg] == 1) {
+    int fo;
+    cnt[sg] = contributors(p, t, T, &fo);
+    need[sg] = false;
+    if (p.ep.kind == EPI_PARTIAL) {
+      // [tile][contributor][m][n] with n contiguous: rows n = 8v + 4(lane/32) + q of column m
+      float* dst = p.partial + ((size_t)t * p.cmax + (g - fo)) * 1024 + (lane & 31) * 32 + 8 * v + 4 * (lane >> 5);
+      *(f32x4_t*)dst = f32x4_t{sums[0], sums[1], sums[2], sums[3]};
+    } else if (cnt[sg] == 1) {
       epilogue_quarter(p, t, sums, v, lane);
     } else {
-      need[sg] = true;
+      need[sg] = any = true;
       float* dst = p.partial + ((size_t)t * p.cmax + (g - fo)) * 1024;
 #pragma unroll
       for (int q = 0; q < 4; ++q) store_coherent(&dst[(4 * v + q) * 64 + lane], sums[q]);
     }
   }
-  if (!need[0] && !need[1]) return;
+  if (!any) return;
   wait_stores();
   __syncthreads();
-  if (threadIdx.x < 2) {
+  if (threadIdx.x < nseg) {
     const int sg = threadIdx.x;
     s_last[sg] = need[sg] ? (atomic_add_agent(&p.counters[t0 + sg], 1) == cnt[sg] - 1) : 0;
   }
@@ -295,17 +313,119 @@ __global__ __launch_bounds__(256, 3) void gemm_bf16_kernel(GemmP p) {
   }
 }
 
+// Row-owned mode: workgroup g owns R = N / NW whole output rows (packed rows [gR, gR + R)) over
+// the full K, so no tile is shared and no partial sums exist.  W is packed per workgroup:
+// block g is R x K, k-step kt (16 columns) of it is R x 16 contiguous, split into sub-tiles of
+// 32 rows (the last one holds R mod 32 rows); sub-tile s of the step is stored in matrix-core
+// operand order, lane (i + rows_s * h) holding row 32s + i, columns 16 kt + 8h .. +8.  Lanes of a
+// short sub-tile past its rows load zeros (out-of-range buffer offsets), so every workgroup
+// moves exactly R K 2 bytes of weights and one activation fragment per step feeds all NS
+// sub-tiles.  The 4 waves take every 4th step; their sums are added in LDS in fixed order.
+__device__ inline void epilogue_rows(const GemmP& p, int rowbase, int rows_s, const float (&v4)[4], int wave,
+                                     int lane) {
+  const int m = lane & 31;
+  if (m >= p.ep.M) return;
+#pragma unroll
+  for (int q = 0; q < 4; q += 2) {
+    const int r = 4 * wave + q;
+    const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+    if (row < rows_s) epi_pair_packed(p.ep, p.map, rowbase + row, m, v4[q], v4[q + 1]);
+  }
+}
+
+template <int NS, int P>
+__global__ __launch_bounds__(256, 1) void gemm_owned_kernel(GemmP p) {
+  if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
+  __shared__ float red[4][NS][16][64];
+  const int lane = threadIdx.x & 63;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.x;
+  const int R = p.R;
+  const uint32_t step_bytes = (uint32_t)R * 32u;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.W + (size_t)g * R * p.K, step_bytes * (uint32_t)p.KT);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, (uint32_t)(32 * p.K * 2));
+  uint32_t wo[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int rows_s = min(32, R - 32 * s);
+    const int i = lane & 31, h = lane >> 5;
+    wo[s] = i < rows_s ? (uint32_t)(512 * s + (i + rows_s * h) * 8) * 2u : 0x80000000u;
+  }
+  const uint32_t xo = (uint32_t)lane * 16u;
+  const int nv = (p.KT - v + 3) / 4;           // steps of this wave: v, v + 4, ...
+  u32x4_t wf[P][NS], xf[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    const uint32_t kt = (uint32_t)(v + 4 * u);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) wf[u][s] = bload16_nt(wr, wo[s] + kt * step_bytes);
+    xf[u] = bload16(xr, xo + kt * 1024u);
+  }
+  f32x16_t acc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s][r] = 0.f;
+  for (int k0 = 0; k0 < nv; k0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc[s] = mfma32x32x16(wf[u][s], xf[u], acc[s]);
+      const uint32_t kt = (uint32_t)(v + 4 * (k0 + u + P));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) wf[u][s] = bload16_nt(wr, wo[s] + kt * step_bytes);
+      xf[u] = bload16(xr, xo + kt * 1024u);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[v][s][r][lane] = acc[s][r];
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float sums[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * v + q;
+      sums[q] = ((red[0][s][r][lane] + red[1][s][r][lane]) + red[2][s][r][lane]) + red[3][s][r][lane];
+    }
+    epilogue_rows(p, g * R + 32 * s, min(32, R - 32 * s), sums, v, lane);
+  }
+}
+
+// One workgroup per compute unit: the weight stream is split into equal contiguous ranges, so
+// every CU moves the same bytes and the workgroups finish together.  A range covers at most
+// MAXSEG tile segments (n <= 3 K/16 + 1 units).
+constexpr int kNumCU = 256;
+constexpr int kMaxSub = 4;   // row-owned mode: at most 4 sub-tiles (128 rows) per workgroup
+
 GemmPlan gemm_plan(int N, int K) {
   GemmPlan pl;
-  const long long T = (long long)(N / 32) * (K / 16);
-  long long nw = T / 96;                 // about 96 KiB of weights per workgroup
-  if (nw < 256) nw = T / 48;
-  if (nw < 256) nw = 256;
-  if (nw < N / 32) nw = N / 32;          // at most K/16 units per workgroup: <= 2 tiles
+  const long long tiles = N / 32, T = tiles * (K / 16);
+  long long nw = kNumCU;
+  if (nw < (tiles + 2) / 3) nw = (tiles + 2) / 3;
   if (nw > T) nw = T;                    // every workgroup owns at least one unit
   pl.tpw = 1;
   pl.splits = (int)nw;                   // number of stream-K workgroups
+  pl.R = 0;
   return pl;
+}
+
+GemmPlan gemm_plan_owned(int N, int K) {
+  // the most workgroups (<= one per CU) that split N into equal even row counts of at most 128
+  for (int nw = kNumCU; nw >= 1; --nw) {
+    if (N % nw) continue;
+    const int R = N / nw;
+    if (R % 2 || R > 32 * kMaxSub) continue;
+    if (nw < kNumCU / 2 && N >= kNumCU) break;   // too few workgroups to stream well
+    GemmPlan pl;
+    pl.tpw = 1;
+    pl.splits = nw;
+    pl.R = R;
+    return pl;
+  }
+  return gemm_plan(N, K);
 }
 
 static int gemm_cmax(int N, int K, int nw) {
@@ -314,12 +434,18 @@ static int gemm_cmax(int N, int K, int nw) {
   return (int)((K / 16) / minsteps + 2);
 }
 
-// Workspace: a fixed block of per-tile counters at the start (shared by every GEMM that uses
-// the same workspace; each GEMM leaves its counters at zero), then the partial sums.
-constexpr int kMaxTiles = 4096;
-constexpr size_t kCounterBytes = kMaxTiles * 4;
+PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws) {
+  PartialSrc ps;
+  ps.base = (const float*)((char*)ws + kCounterBytes);
+  ps.tiles = N / 32;
+  ps.KT = K / 16;
+  ps.NW = plan.splits;
+  ps.cmax = gemm_cmax(N, K, plan.splits);
+  return ps;
+}
 
 size_t gemm_ws_bytes(int N, int K, GemmPlan plan) {
+  if (plan.R > 0) return kCounterBytes;
   const size_t part = (size_t)(N / 32) * gemm_cmax(N, K, plan.splits) * 1024 * 4;
   return kCounterBytes + align_up(part, 256);
 }
@@ -336,9 +462,23 @@ int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const Ep
   p.cmax = gemm_cmax(N, K, plan.splits);
   p.map = map_kind;
   if (p.tiles > kMaxTiles) return fail(DLM_ERR_SHAPE, "gemm: %d tiles exceed %d", p.tiles, kMaxTiles);
+  const long long T = (long long)p.tiles * p.KT;
+  if ((T + p.NW - 1) / p.NW > 3LL * p.KT + 1) return fail(DLM_ERR_SHAPE, "gemm: plan spans too many tiles");
   p.counters = (int*)ws;
   p.partial = (float*)((char*)ws + kCounterBytes);
   p.ep = ep;
+  p.R = plan.R;
+  if (plan.R > 0) {
+    if (ep.kind == EPI_PARTIAL) return fail(DLM_ERR_ARG, "gemm: row-owned plan has no partial sums");
+    if (N != plan.R * plan.splits || plan.R % 2 || plan.R > 32 * kMaxSub)
+      return fail(DLM_ERR_SHAPE, "gemm: bad row-owned plan");
+    const int ns = (plan.R + 31) / 32;
+    if (ns == 1) hipLaunchKernelGGL((gemm_owned_kernel<1, 16>), dim3(p.NW), dim3(256), 0, st, p);
+    else if (ns == 2) hipLaunchKernelGGL((gemm_owned_kernel<2, 12>), dim3(p.NW), dim3(256), 0, st, p);
+    else if (ns == 3) hipLaunchKernelGGL((gemm_owned_kernel<3, 8>), dim3(p.NW), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((gemm_owned_kernel<4, 8>), dim3(p.NW), dim3(256), 0, st, p);
+    return check_hip(hipGetLastError(), "gemm_bf16 launch");
+  }
   hipLaunchKernelGGL(gemm_bf16_kernel<8>, dim3(p.NW), dim3(256), 0, st, p);
   return check_hip(hipGetLastError(), "gemm_bf16 launch");
 }
@@ -422,6 +562,44 @@ __global__ __launch_bounds__(64) void pack_kernel(PackP p) {
   const uint16_t* s = p.src[i] + (size_t)row * p.k + kt * 16 + 8 * (lane >> 5);
   u32x4_t v = *(const u32x4_t*)s;
   *(u32x4_t*)(p.dst + ((size_t)blockIdx.x * 64 + lane) * 8) = v;
+}
+
+// Row-owned layout (see gemm_owned_kernel): 16-byte chunk c of the output decodes to
+// workgroup g, step kt, sub-tile s, row i, column half h.
+__global__ __launch_bounds__(256) void pack_owned_kernel(PackP p, int R, long long chunks) {
+  const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const long long per_g = (long long)R * p.k / 8;
+  const int g = (int)(c / per_g);
+  const int rem = (int)(c % per_g);
+  const int kt = rem / (2 * R), w = rem % (2 * R);
+  const int s = w / 64, x = w % 64;
+  const int rows_s = min(32, R - 32 * s);
+  const int i = x % rows_s, h = x / rows_s;
+  const int prow = g * R + 32 * s + i;
+  int row = p.map ? p.map[prow] : prow;
+  int src = 0;
+  while (src < p.n_src - 1 && row >= p.rows[src]) { row -= p.rows[src]; ++src; }
+  const uint16_t* sp = p.src[src] + (size_t)row * p.k + kt * 16 + 8 * h;
+  *(u32x4_t*)(p.dst + (size_t)c * 8) = *(const u32x4_t*)sp;
+}
+
+int pack_bf16_owned(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
+                    const int32_t* row_map_dev, int R, void* dst, hipStream_t st) {
+  PackP p;
+  for (int i = 0; i < 3; ++i) {
+    p.src[i] = i < n_src ? (const uint16_t*)srcs[i] : nullptr;
+    p.rows[i] = i < n_src ? src_rows[i] : 0;
+  }
+  p.n_src = n_src;
+  p.k = k;
+  p.KT = k / 16;
+  p.map = row_map_dev;
+  p.dst = (uint16_t*)dst;
+  if (R <= 0 || n_rows % R || R % 2) return fail(DLM_ERR_SHAPE, "pack: bad row-owned layout");
+  const long long chunks = (long long)n_rows * k / 8;
+  hipLaunchKernelGGL(pack_owned_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, p, R, chunks);
+  return check_hip(hipGetLastError(), "pack launch");
 }
 
 int pack_bf16(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,

@@ -7,28 +7,66 @@ namespace dlm {
 namespace {
 
 // ------------------------------------------------------------------ RMSNorm
-// one workgroup (256 threads) per row; deterministic fixed-order reduction
+// One workgroup (256 threads) per row; deterministic fixed-order reduction.  When the residual
+// stream has pending GEMM partial sums (a residual projection with deferred output), the row is
+// first completed as x + p_0 + p_1 + ... in contributor order and written back.
 struct NormP {
-  const float* x;
+  float* x;
   const void* g;
   void* out;
   int d, bf16, packed;
   float eps;
   const int32_t* cont_dev;
+  PartialSrc ps;
 };
+
+__device__ inline int owner_unit(long long s, long long T, int NW) {
+  return (int)(((s + 1) * NW - 1) / T);
+}
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
-  const float* x = p.x + (size_t)row * p.d;
+  float* x = p.x + (size_t)row * p.d;
   // every load of the row is issued before any arithmetic (d <= 4096: <= 4 float4 per thread)
-  constexpr int MAXV = 4;
+  constexpr int MAXV = 4, NPF = 6;
   f32x4_t xv[MAXV];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int c = 4 * (tid + 256 * j);
     xv[j] = c < p.d ? *(const f32x4_t*)(x + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if (p.ps.base) {
+    const long long T = (long long)p.ps.tiles * p.ps.KT;
+    int cnt[MAXV];
+    const float* src[MAXV];
+    f32x4_t pv[MAXV][NPF];
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int c = 4 * (tid + 256 * j);
+      const int t = c >> 5;
+      cnt[j] = 0;
+      src[j] = p.ps.base;
+      if (c < p.d) {
+        const int fo = owner_unit((long long)t * p.ps.KT, T, p.ps.NW);
+        cnt[j] = owner_unit((long long)(t + 1) * p.ps.KT - 1, T, p.ps.NW) - fo + 1;
+        src[j] = p.ps.base + (size_t)t * p.ps.cmax * 1024 + row * 32 + (c & 31);
+      }
+#pragma unroll
+      for (int i = 0; i < NPF; ++i)
+        pv[j][i] = i < cnt[j] ? *(const f32x4_t*)(src[j] + (size_t)i * 1024) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int c = 4 * (tid + 256 * j);
+      if (c >= p.d) continue;
+#pragma unroll
+      for (int i = 0; i < NPF; ++i)
+        if (i < cnt[j]) xv[j] += pv[j][i];
+      for (int i = NPF; i < cnt[j]; ++i) xv[j] += *(const f32x4_t*)(src[j] + (size_t)i * 1024);
+      *(f32x4_t*)(x + c) = xv[j];
+    }
   }
   float s = 0.f;
 #pragma unroll
@@ -197,9 +235,10 @@ __global__ void len_add_kernel(int32_t* len, int add) {
 
 }  // namespace
 
-int rmsnorm(const float* x, const void* g, void* out, int rows, int d, int bf16, int packed, float eps,
-            const int32_t* cont_dev, hipStream_t st) {
-  NormP p{x, g, out, d, bf16, packed, eps, cont_dev};
+int rmsnorm(float* x, const void* g, void* out, int rows, int d, int bf16, int packed, float eps,
+            const int32_t* cont_dev, hipStream_t st, const PartialSrc* ps) {
+  PartialSrc none{};
+  NormP p{x, g, out, d, bf16, packed, eps, cont_dev, ps ? *ps : none};
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, st, p);
   return check_hip(hipGetLastError(), "rmsnorm launch");
 }

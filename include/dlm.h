@@ -194,9 +194,9 @@ int dlm_pack_matrix(const void* src, int n_rows, int k, const int32_t* row_map_d
                     void* stream);
 
 /* ------------------------------------------------------------------------------------
- * dlm_linear -- y = x W^T for the block's rows with a packed bf16 weight: the skinny
- * matrix-core GEMM every projection of the round uses (same kernel, tiling and split plan
- * as inside the decode step), with a plain f32 store as its epilogue.
+ * dlm_linear -- y = x W^T for the block's rows with a packed bf16 weight: the stream-K skinny
+ * matrix-core GEMM that the round uses for its split-K projections (attention output, FFN
+ * down, self-conditioning adapter), with a plain f32 store as its epilogue.
  *   w_packed [n, k] packed by dlm_pack_matrix;  x: 32 x k bf16 in the packed activation
  *   order written by dlm_pack_activations (rows >= m are read but ignored);  y [m, n] f32.
  *   1 <= m <= 32, n % 32 == 0, k % 32 == 0.  ws: dlm_linear_ws_bytes(n, k) bytes, zeroed
@@ -256,6 +256,17 @@ size_t dlm_packed_bytes(const dlm_model_desc* desc);
 size_t dlm_pack_ws_bytes(const dlm_model_desc* desc);
 int dlm_pack_model(const dlm_model_desc* desc, const void* w_sc, const dlm_layer_weights* layers,
                    void* dst, void* row_map_ws, size_t ws_bytes, void* stream);
+
+/* One sublayer of a packed dense bf16 model on its own, with the kernel and launch plan that
+ * dlm_decode_block uses for it: layer `layer`'s FFN gate/up projection fused with SwiGLU,
+ * act = silu(x Wg^T) * (x Wu^T), for the block's rows (the FFN form of the layer that the
+ * round forwards; the largest weight stream of the round).
+ *   x_packed: bf16 32 x d and act_packed: bf16 32 x ffn, both in the packed activation order
+ *   of dlm_pack_activations.  ws: dlm_ffn_gate_up_ws_bytes(m) bytes, zeroed once before first
+ *   use.  Errors: DLM_ERR_DTYPE for f32 or MoE models, DLM_ERR_ARG for a layer out of range. */
+size_t dlm_ffn_gate_up_ws_bytes(const dlm_model* m);
+int dlm_ffn_gate_up(const dlm_model* m, int layer, const void* x_packed, void* act_packed, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * KV cache.  k[l]: device base of layer l's keys [hkv, cap, D]; v[l]: its values stored

@@ -8,7 +8,7 @@ import torch
 import synth
 import oracle
 from oracle import Prec, OracleModel, KVCache, CommitRule as OCommitRule
-from tests.gpu_util import require_gpu, storage
+from tests.gpu_util import require_gpu, storage, dev_bf16, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -206,3 +206,34 @@ def test_prefill_matches_oracle_cache():
             # value to different sides of a bf16 rounding boundary (one unit in the last place)
             ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(kv.k[0][:, :96]), 1e-30))) - 7)
             assert np.mean(np.abs(gk - kv.k[0][:, :96]) > 1.01 * ulp) < 1e-3
+
+
+def _unpack_act(bits: np.ndarray, k: int) -> np.ndarray:
+    """32 x k bf16 in the packed activation order (documented with dlm_pack_activations)
+    -> row-major float64."""
+    m = np.arange(32)[:, None]
+    c = np.arange(k)[None, :]
+    idx = ((c >> 4) * 64 + m + 32 * ((c >> 3) & 1)) * 8 + (c & 7)
+    return oracle.decode_storage(bits.reshape(-1)[idx])
+
+
+@pytest.mark.parametrize("d,ffn", [(512, 1024), (2560, 9728)])
+def test_ffn_gate_up_matches_oracle(d, ffn):
+    """The round's gate/up + SwiGLU sublayer alone (the launch plan of the decode step) against
+    the oracle's SwiGLU of the same bf16 operands, every output element."""
+    dlm = _dlm()
+    s = synth.small_shape(synth.QWEN4B, name=f"ffn-{d}", n_layers=1, d=d, hq=d // 128, hkv=max(1, d // 512),
+                          head_dim=128, ffn=ffn, vocab=1000)
+    _say(f"ffn gate/up d={d} ffn={ffn}")
+    m, w = _gpu_model(s, 1234, cap=64)
+    X = synth.stored_normal(1234, "ffn.X", (32, d), 1.0, "bf16")
+    xp = dlm.pack_activations(dev_bf16(X))
+    act = m.ffn_gate_up(0, xp)
+    act2 = m.ffn_gate_up(0, xp)
+    torch.cuda.synchronize()
+    assert torch.equal(act, act2)
+    got = _unpack_act(to_bits(act), ffn)
+    x = oracle.decode_storage(X)
+    ref = oracle.block.swiglu(x @ oracle.decode_storage(w["l0.wg"]).T, x @ oracle.decode_storage(w["l0.wu"]).T)
+    # one bf16 rounding of a float32 result: half an ulp plus the f32 accumulation error
+    np.testing.assert_allclose(got, ref, rtol=2 ** -8 + 1e-4, atol=1e-5)
