@@ -15,6 +15,8 @@
 #include "small.h"
 #include "moe.h"
 
+#include <cstddef>
+
 // ------------------------------------------------------------------ errors
 namespace dlm {
 static thread_local char g_err[512] = "";
@@ -279,9 +281,9 @@ struct dlm_model {
   const void* packed;
   // packed offsets (bytes)
   size_t off_sc;
-  std::vector<size_t> off_qkv, off_o, off_gu, off_dn;
+  std::vector<size_t> off_qkv, off_o, off_gu, off_dn, off_router, off_moe;
   size_t packed_bytes;
-  GemmPlan pl_sc, pl_qkv, pl_o, pl_gu, pl_dn;
+  GemmPlan pl_sc, pl_qkv, pl_o, pl_gu, pl_dn, pl_router;
   int n_qkv;
   std::mutex mu;
   std::map<GraphKey, hipGraphExec_t> graphs;
@@ -304,8 +306,10 @@ static int check_model_desc(const dlm_model_desc* d) {
     DLM_REQUIRE(d->dtype == DLM_BF16, DLM_ERR_DTYPE, "MoE models are bf16");
     DLM_REQUIRE(d->top_k >= 1 && d->top_k <= 8 && d->top_k <= d->n_experts && d->n_experts <= 256,
                 DLM_ERR_SHAPE, "top_k in [1, 8], n_experts <= 256");
-    DLM_REQUIRE(d->expert_ffn % 32 == 0 && d->expert_ffn > 0 && d->n_shared >= 0 && d->n_shared <= 2,
-                DLM_ERR_SHAPE, "expert_ffn %% 32 == 0, n_shared <= 2");
+    DLM_REQUIRE(d->expert_ffn % 128 == 0 && d->expert_ffn > 0 && d->n_shared >= 0 && d->n_shared <= 2,
+                DLM_ERR_SHAPE, "expert_ffn %% 128 == 0, n_shared <= 2");
+    DLM_REQUIRE(d->n_experts % 32 == 0 && d->d % 128 == 0 && d->block <= 32, DLM_ERR_SHAPE,
+                "MoE: n_experts %% 32 == 0, d %% 128 == 0, block <= 32");
   }
   if (d->dtype == DLM_F32) DLM_REQUIRE(d->d <= 256, DLM_ERR_SHAPE, "f32 models support d <= 256");
   return DLM_OK;
@@ -322,12 +326,17 @@ static void layout_packed(dlm_model* m) {
   m->off_o.resize(d.n_layers);
   m->off_gu.resize(d.n_layers);
   m->off_dn.resize(d.n_layers);
+  m->off_router.resize(d.n_layers);
+  m->off_moe.resize(d.n_layers);
   for (int l = 0; l < d.n_layers; ++l) {
     m->off_qkv[l] = take((size_t)m->n_qkv * d.d * 2);
     m->off_o[l] = take((size_t)d.d * d.hq * D * 2);
     if (d.n_experts == 0) {
       m->off_gu[l] = take((size_t)2 * d.ffn * d.d * 2);
       m->off_dn[l] = take((size_t)d.d * d.ffn * 2);
+    } else {
+      m->off_router[l] = take((size_t)d.n_experts * d.d * 2);
+      m->off_moe[l] = take(moe_layer_packed_bytes(moe_dims(d)));
     }
   }
   m->packed_bytes = d.dtype == DLM_BF16 ? off : 0;
@@ -340,6 +349,7 @@ static void layout_packed(dlm_model* m) {
   } else {
     m->pl_gu = m->pl_dn = GemmPlan{1, 1, 0};
   }
+  m->pl_router = d.n_experts ? gemm_plan(d.n_experts, d.d) : GemmPlan{1, 1, 0};
 }
 
 extern "C" size_t dlm_packed_bytes(const dlm_model_desc* d) {
@@ -421,6 +431,11 @@ extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const d
       rc = m.pl_dn.R ? pack_bf16_owned(sd, rd, 1, d->d, d->ffn, nullptr, m.pl_dn.R, out + m.off_dn[l], st)
                      : pack_bf16(sd, rd, 1, d->d, d->ffn, nullptr, out + m.off_dn[l], st);
       if (rc) return rc;
+    } else {
+      const void* sr[1] = {L.router};
+      int rr[1] = {d->n_experts};
+      if ((rc = pack_bf16(sr, rr, 1, d->n_experts, d->d, nullptr, out + m.off_router[l], st))) return rc;
+      if ((rc = moe_pack_layer(moe_dims(*d), L, out + m.off_moe[l], st))) return rc;
     }
   }
   return DLM_OK;
@@ -515,6 +530,8 @@ static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) 
     if (!d.n_experts) {
       g = std::max(g, gemm_ws_bytes(2 * d.ffn, d.d, m->pl_gu));
       g = std::max(g, gemm_ws_bytes(d.d, d.ffn, m->pl_dn));
+    } else {
+      g = std::max(g, gemm_ws_bytes(d.n_experts, d.d, m->pl_router));
     }
   }
   w.gemm_ws = take(g + 256);
@@ -556,6 +573,9 @@ extern "C" int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* 
   out->maxprob = w.maxp;
   out->argmax = w.amax;
   out->committed = w.committed;
+  out->xn = w.xn;
+  memset(&out->moe_logits, 0, sizeof(dlm_decode_views) - offsetof(dlm_decode_views, moe_logits));
+  if (m->d.n_experts) moe_views(moe_dims(m->d), w.moe_ws, out);
   return DLM_OK;
 }
 
@@ -577,7 +597,7 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     const dlm_layer_weights& L = m->layers[l];
     const bool last = l == d.n_layers - 1;
     if ((rc = rmsnorm(w.x, L.attn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st, &ps))) return rc;
-    ps.base = nullptr;
+    ps = PartialSrc{};
     EpiParams e = epi_zero();
     e.kind = EPI_QKV_ROPE;
     e.M = B;
@@ -625,9 +645,12 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     }
     if (rc) return rc;
     if ((rc = rmsnorm(w.x, L.ffn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st, &ps))) return rc;
-    ps.base = nullptr;
+    ps = PartialSrc{};
     if (d.n_experts) {
-      if ((rc = moe_ffn(d, L, w.xn, w.x, B, w.moe_ws, cont, st))) return rc;
+      // the experts' weighted outputs are added into x by the next RMSNorm, slot by slot
+      if ((rc = moe_ffn(moe_dims(d), w.xn, pk + m->off_router[l], m->pl_router, pk + m->off_moe[l], w.moe_ws,
+                        w.gemm_ws, cont, &ps, st)))
+        return rc;
       continue;
     }
     e = epi_zero();

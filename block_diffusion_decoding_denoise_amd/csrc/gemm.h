@@ -19,6 +19,10 @@ enum EpiKind {
 struct PartialSrc {
   const float* base;   // nullptr: no partials
   int tiles, KT, NW, cmax;
+  // alternatively (base == nullptr): per-row output slots, value (m, n) of slot j at
+  // slots[(m * nslot + j) * d + n], added in slot order (routed experts)
+  const float* slots;
+  int nslot;
 };
 
 // Logical row orders of the fused matrices (packed row order is described in gemm.hip):

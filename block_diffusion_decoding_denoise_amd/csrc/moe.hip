@@ -1,11 +1,548 @@
-// Routed-expert FFN with MXFP4 expert weights.
+// Routed-expert FFN of the MoE model (the FFN of every layer of the MoE configuration).
+//
+// Steps, per layer and round (all rows of the block):
+//   1. router logits r = f W_r^T (bf16 stream-K GEMM, f32 out);
+//   2. route: softmax over the E routed experts in f32, top-k by (probability desc, expert id
+//      asc), the selected probabilities are the mixing weights (not renormalised); shared
+//      experts take every row with weight 1; per-expert row lists in row order; the list of
+//      experts hit, in id order.  The same launch quantises f to MXFP8 (e4m3 codes, one e8m0
+//      scale per 32 along d);
+//   3. up: per hit expert and 64 interleaved gate/up rows, act = silu(gate) * up over its rows
+//      with v_mfma_scale_f32_16x16x128_f8f6f4 (A = MXFP4 weights, B = MXFP8 activations), the
+//      32 act values of a row quantised to MXFP8 in the epilogue;
+//   4. down: per hit expert and 64 output columns, y = act W_d^T, scaled by the row's mixing
+//      weight and stored to the row's slot; the next RMSNorm adds the slots in order.
+// Pages: [ORL-blog] "What shipped" runs routed experts in 4-bit floating point on the
+// matrix units; the MI355X form uses the OCP microscaling formats (MXFP4 weights, MXFP8
+// activations), which the scaled matrix-core instruction consumes directly.
+//
+// Packed expert matrix of R rows x K columns (R % 64 == 0, K % 128 == 0): for quad q (64 rows),
+// step s (128 columns), row group gq (16 rows) and lane l, the 16 bytes at
+// ((q S + s) 4 + gq) 1024 + 16 l hold the e2m1 codes (low nibble first) of row 64q + 16gq + l%16,
+// columns 128s + 32(l/16) .. +32, and byte ((q S + s) 4 + gq) 64 + l of the scale array holds that
+// 32-column block's e8m0.  That is the A-operand order of the scaled MFMA, so a wave loads one
+// contiguous 1 KiB (+ 64 B of scales) per row group and step.  Gate/up rows are interleaved
+// (packed row 2i = gate i, 2i + 1 = up i) so one lane holds both halves of a SwiGLU pair.
 #include "moe.h"
 
+#include <cstring>
+
 namespace dlm {
-size_t moe_ws_bytes(const dlm_model_desc& d) { (void)d; return 256; }
-int moe_ffn(const dlm_model_desc& d, const dlm_layer_weights& L, const void* xn, float* h, int rows, void* ws,
-            const int32_t* cont_dev, hipStream_t st) {
-  (void)d; (void)L; (void)xn; (void)h; (void)rows; (void)ws; (void)cont_dev; (void)st;
-  return fail(DLM_ERR_UNSUPPORTED, "MoE FFN not built yet");
+
+MoeDims moe_dims(const dlm_model_desc& d) {
+  MoeDims m;
+  m.d = d.d;
+  m.F = d.expert_ffn;
+  m.E = d.n_experts;
+  m.S = d.n_shared;
+  m.top_k = d.top_k;
+  m.NS = d.top_k + d.n_shared;
+  m.rows = d.block;
+  return m;
 }
+
+size_t moe_layer_packed_bytes(const MoeDims& m) { return (size_t)(m.E + m.S) * m.expert_bytes(); }
+
+namespace {
+
+constexpr int kMaxRows = 32;
+constexpr int kMaxExperts = 512;
+
+// -------------------------------------------------------------------- MX number formats
+// Shared exponent of a block for an element format whose largest exponent is emax:
+// floor(log2(amax)) - emax, -127 for an all-zero block (OCP MX v1.0).
+__device__ inline int mx_shared_exp(float amax, int emax) {
+  if (!(amax > 0.f)) return -127;
+  int ex;
+  frexpf(amax, &ex);                     // amax = m 2^ex, m in [0.5, 1)
+  return max(-127, min(127, ex - 1 - emax));
+}
+
+// e4m3 code (OCP: bias 7, 3 mantissa bits, largest 448, subnormal step 2^-9) of v rounded to
+// nearest, ties to even, saturating at 448.
+__device__ inline uint32_t e4m3_code(float v) {
+  const uint32_t sign = v < 0.f ? 0x80u : 0u;
+  const float a = fabsf(v);
+  float q;
+  if (a >= 448.f) {
+    q = 448.f;
+  } else {
+    int ex;
+    frexpf(a, &ex);
+    const int E = a > 0.f ? max(ex - 1, -6) : -6;
+    q = rintf(a * ldexpf(1.f, 3 - E)) * ldexpf(1.f, E - 3);    // exact power-of-two scalings
+    q = fminf(q, 448.f);
+  }
+  if (q == 0.f) return sign;
+  int ex;
+  frexpf(q, &ex);
+  const int E = ex - 1;
+  if (E < -6) return sign | (uint32_t)(q * 512.f);                                   // subnormal
+  return sign | ((uint32_t)(E + 7) << 3) | (uint32_t)(q * ldexpf(1.f, 3 - E) - 8.f);
+}
+
+__device__ inline f32x4_t mfma_mx(u32x4_t a_fp4, u32x4_t b_lo, u32x4_t b_hi, int sa, int sb, f32x4_t c) {
+  typedef int v8i_t __attribute__((ext_vector_type(8)));
+  v8i_t a, b;
+  a[0] = (int)a_fp4[0]; a[1] = (int)a_fp4[1]; a[2] = (int)a_fp4[2]; a[3] = (int)a_fp4[3];
+  a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
+  b[0] = (int)b_lo[0]; b[1] = (int)b_lo[1]; b[2] = (int)b_lo[2]; b[3] = (int)b_lo[3];
+  b[4] = (int)b_hi[0]; b[5] = (int)b_hi[1]; b[6] = (int)b_hi[2]; b[7] = (int)b_hi[3];
+  // A format 4 = e2m1 (lane l: row l%16, columns 32(l/16) .. +32), B format 0 = e4m3 (lane l:
+  // column l%16, rows 16(l/16) .. +16 then 64 + 16(l/16) .. +16); scales: lane 16b + i holds the
+  // e8m0 of row / column i, 32-element block b, in byte 0.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
+}
+
+__device__ inline uint32_t bload_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+// -------------------------------------------------------------------- packing
+struct MxPackP {
+  const uint8_t* src;         // [n_mats][R][K/2] codes, natural
+  const uint8_t* src_scale;   // [n_mats][R][K/32]
+  uint8_t* dst;
+  uint8_t* dst_scale;
+  int R, K, interleave;
+  long long chunks;           // n_mats * R * K / 32
+};
+
+__global__ __launch_bounds__(256) void mx_pack_kernel(MxPackP p) {
+  const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= p.chunks) return;
+  const long long per_mat = (long long)p.R * p.K / 32;
+  const int mat = (int)(c / per_mat);
+  int r = (int)(c % per_mat);
+  const int lane = r % 64;
+  int u = r / 64;
+  const int gq = u % 4;
+  u /= 4;
+  const int S = p.K / 128;
+  const int s = u % S, q = u / S;
+  const int prow = 64 * q + 16 * gq + (lane & 15);
+  const int srow = p.interleave ? ((prow & 1) ? p.R / 2 : 0) + prow / 2 : prow;
+  const int k0 = 128 * s + 32 * (lane >> 4);
+  const size_t so = (size_t)mat * p.R * (p.K / 2) + (size_t)srow * (p.K / 2) + k0 / 2;
+  *(u32x4_t*)(p.dst + (size_t)c * 16) = *(const u32x4_t*)(p.src + so);
+  p.dst_scale[c] = p.src_scale[(size_t)mat * p.R * (p.K / 32) + (size_t)srow * (p.K / 32) + k0 / 32];
+}
+
+// -------------------------------------------------------------------- route + quantise
+struct Lists {
+  int* cnt;        // [E + S]
+  int* tok;        // [E + S][32] rows in row order
+  int* slot;       // [E + S][32] output slot (row * NS + rank)
+  float* wgt;      // [E + S][32] mixing weight
+  int* active;     // [E + S] experts with cnt > 0, in id order
+  int* n_active;   // [1]
+};
+
+struct RouteP {
+  MoeDims m;
+  const float* logits;     // [rows][E]
+  const uint16_t* f;       // bf16 packed activations, 32 x d
+  uint8_t* xq;             // [32][d] e4m3 codes
+  uint8_t* xs;             // [32][d/32] e8m0
+  Lists li;
+  const int32_t* cont_dev;
+};
+
+__global__ __launch_bounds__(256) void moe_route_kernel(RouteP p) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  const MoeDims& m = p.m;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x < m.rows) {
+    // MXFP8 of row `row` of f: one 32-column block per thread
+    const int row = blockIdx.x;
+    for (int b = tid; b < m.d / 32; b += 256) {
+      float v[32];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const u32x4_t w = *(const u32x4_t*)(p.f + xpk_index(row, 32 * b + 8 * h));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * h + 2 * e] = lo_bf(w[e]);
+          v[8 * h + 2 * e + 1] = hi_bf(w[e]);
+        }
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int e = mx_shared_exp(amax, 8);
+      const float inv = ldexpf(1.f, -e);
+      uint32_t words[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        words[i] = e4m3_code(v[4 * i] * inv) | (e4m3_code(v[4 * i + 1] * inv) << 8) |
+                   (e4m3_code(v[4 * i + 2] * inv) << 16) | (e4m3_code(v[4 * i + 3] * inv) << 24);
+      u32x4_t* dst = (u32x4_t*)(p.xq + (size_t)row * m.d + 32 * b);
+      dst[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+      dst[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+      p.xs[(size_t)row * (m.d / 32) + b] = (uint8_t)(e + 127);
+    }
+    return;
+  }
+  // routing: wave w takes rows w, w + 4, ...; lane holds experts lane + 64 i
+  __shared__ int s_ids[kMaxRows][8];
+  __shared__ float s_w[kMaxRows][8];
+  __shared__ int s_cnt[kMaxExperts];
+  constexpr int EPL = 4;   // experts per lane (E <= 256)
+  for (int row = wave; row < m.rows; row += 4) {
+    float r[EPL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      r[i] = e < m.E ? p.logits[(size_t)row * m.E + e] : -INFINITY;
+      mx = fmaxf(mx, r[i]);
+    }
+    mx = wave_max(mx);
+    float pr[EPL], s = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      pr[i] = lane + 64 * i < m.E ? expf(r[i] - mx) : 0.f;
+      s += pr[i];
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) pr[i] = lane + 64 * i < m.E ? pr[i] / s : -1.f;
+    for (int j = 0; j < m.top_k; ++j) {
+      // largest probability, lowest id on ties
+      float bv = -2.f;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (pr[i] > bv) { bv = pr[i]; bi = lane + 64 * i; }
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i == bi) pr[i] = -1.f;
+      if (lane == 0) {
+        s_ids[row][j] = bi;
+        s_w[row][j] = bv;
+      }
+    }
+  }
+  __syncthreads();
+  const int ET = m.E + m.S;
+  for (int t = tid; t < ET; t += 256) {
+    int n = 0;
+    if (t < m.E) {
+      for (int i = 0; i < m.rows; ++i)
+        for (int j = 0; j < m.top_k; ++j)
+          if (s_ids[i][j] == t) {
+            p.li.tok[t * 32 + n] = i;
+            p.li.slot[t * 32 + n] = i * m.NS + j;
+            p.li.wgt[t * 32 + n] = s_w[i][j];
+            ++n;
+          }
+    } else {
+      for (int i = 0; i < m.rows; ++i) {
+        p.li.tok[t * 32 + i] = i;
+        p.li.slot[t * 32 + i] = i * m.NS + m.top_k + (t - m.E);
+        p.li.wgt[t * 32 + i] = 1.f;
+      }
+      n = m.rows;
+    }
+    p.li.cnt[t] = n;
+    s_cnt[t] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0;
+    for (int t = 0; t < ET; ++t)
+      if (s_cnt[t] > 0) p.li.active[a++] = t;
+    *p.li.n_active = a;
+  }
+}
+
+// -------------------------------------------------------------------- expert projections
+struct ExpP {
+  MoeDims m;
+  const uint8_t* w;        // packed codes of this layer's matrix of expert 0
+  const uint8_t* ws;       // packed scales of expert 0
+  size_t w_stride, s_stride;   // bytes per expert
+  int Q, S;                // quads (64 rows) and 128-column steps of the matrix
+  const uint8_t* bq;       // B operand codes: [rows or slots][K]
+  const uint8_t* bs;       // B operand scales: [rows or slots][K/32]
+  int b_by_slot;           // B rows are indexed by slot (down) or by row (up)
+  Lists li;
+  uint8_t* aq;             // up: act codes [32 NS][F]
+  uint8_t* as;             // up: act scales [32 NS][F/32]
+  float* y;                // down: [32 NS][d]
+  const int32_t* cont_dev;
+};
+
+// One wave per (hit expert, quad): 4 row groups x up to 2 groups of 16 rows of the block, K in
+// steps of 128, the weight steps prefetched PF at a time.
+template <int UP>
+__global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  const int item = blockIdx.x;
+  const int a = item / p.Q, q = item % p.Q;
+  if (a >= *p.li.n_active) return;
+  const int e = p.li.active[a];
+  const int n = p.li.cnt[e];
+  const int lane = threadIdx.x;
+  const int K = 128 * p.S;
+  const bool two = n > 16;
+  int col[2], brow[2];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    col[cg] = 16 * cg + (lane & 15);
+    brow[cg] = -1;
+    if (col[cg] < n) brow[cg] = p.b_by_slot ? p.li.slot[e * 32 + col[cg]] : p.li.tok[e * 32 + col[cg]];
+  }
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + e * p.w_stride + (size_t)q * p.S * 4096, (uint32_t)p.S * 4096u);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.ws + e * p.s_stride + (size_t)q * p.S * 256, (uint32_t)p.S * 256u);
+  const int n_brows = p.b_by_slot ? 32 * p.m.NS : 32;
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(p.bq, (uint32_t)(n_brows * K));
+  const __amdgpu_buffer_rsrc_t bsr = make_rsrc(p.bs, (uint32_t)(n_brows * (K / 32)));
+  uint32_t bo[2], bso[2];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    bo[cg] = brow[cg] >= 0 ? (uint32_t)(brow[cg] * K + 16 * (lane >> 4)) : 0x80000000u;
+    bso[cg] = brow[cg] >= 0 ? (uint32_t)(brow[cg] * (K / 32) + (lane >> 4)) : 0x80000000u;
+  }
+  f32x4_t acc[2][4];
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[cg][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int PF = 4;
+  u32x4_t wa[PF][4];
+  uint32_t ws[PF][4];
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      wa[u][g] = bload16_nt(wr, (uint32_t)((u * 4 + g) * 64 + lane) * 16u);
+      ws[u][g] = bload_u8(sr, (uint32_t)((u * 4 + g) * 64 + lane));
+    }
+  for (int s0 = 0; s0 < p.S; s0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int s = s0 + u;
+      if (s < p.S) {
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+          if (cg == 1 && !two) break;
+          const u32x4_t lo = bload16(br, bo[cg] + 128u * s);
+          const u32x4_t hi = bload16(br, bo[cg] + 128u * s + 64u);
+          const int sb = (int)bload_u8(bsr, bso[cg] + 4u * s);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) acc[cg][g] = mfma_mx(wa[u][g], lo, hi, (int)ws[u][g], sb, acc[cg][g]);
+        }
+      }
+      const int sn = s + PF;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        wa[u][g] = bload16_nt(wr, (uint32_t)((sn * 4 + g) * 64 + lane) * 16u);
+        ws[u][g] = bload_u8(sr, (uint32_t)((sn * 4 + g) * 64 + lane));
+      }
+    }
+  }
+  // epilogue.  acc[cg][g][r] = D[row 64q + 16g + 4(l/16) + r][column col[cg]]
+#pragma unroll
+  for (int cg = 0; cg < 2; ++cg) {
+    if (cg == 1 && !two) break;
+    const bool valid = col[cg] < n;
+    if (UP) {
+      // rows 2i / 2i + 1 are gate / up of intermediate column i = 32q + 8g + 2(l/16) + {0, 1}
+      float act[4][2];
+      float amax = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float gt = acc[cg][g][2 * h], up = acc[cg][g][2 * h + 1];
+          act[g][h] = gt / (1.0f + expf(-gt)) * up;
+          amax = fmaxf(amax, fabsf(act[g][h]));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int ex = mx_shared_exp(amax, 8);
+      const float inv = ldexpf(1.f, -ex);
+      if (valid) {
+        const int sl = p.li.slot[e * 32 + col[cg]];   // B rows are the block's rows; act goes to the slot
+        uint8_t* dst = p.aq + (size_t)sl * p.m.F + 32 * q + 2 * (lane >> 4);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(uint16_t*)(dst + 8 * g) = (uint16_t)(e4m3_code(act[g][0] * inv) | (e4m3_code(act[g][1] * inv) << 8));
+        if ((lane >> 4) == 0) p.as[(size_t)sl * (p.m.F / 32) + q] = (uint8_t)(ex + 127);
+      }
+    } else if (valid) {
+      const int sl = brow[cg];
+      const float wgt = p.li.wgt[e * 32 + col[cg]];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = wgt * acc[cg][g][r];
+        *(f32x4_t*)(p.y + (size_t)sl * p.m.d + 64 * q + 16 * g + 4 * (lane >> 4)) = o;
+      }
+    }
+  }
+}
+
+struct MoeWs {
+  float* logits;
+  uint8_t *xq, *xs, *aq, *as;
+  float* y;
+  Lists li;
+  size_t total;
+};
+
+MoeWs moe_ws_layout(const MoeDims& m, char* base) {
+  MoeWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return base ? base + o : nullptr; };
+  const int ET = m.E + m.S;
+  w.logits = (float*)take((size_t)kMaxRows * m.E * 4);
+  w.xq = (uint8_t*)take((size_t)kMaxRows * m.d);
+  w.xs = (uint8_t*)take((size_t)kMaxRows * m.d / 32);
+  w.aq = (uint8_t*)take((size_t)kMaxRows * m.NS * m.F);
+  w.as = (uint8_t*)take((size_t)kMaxRows * m.NS * m.F / 32);
+  w.y = (float*)take((size_t)kMaxRows * m.NS * m.d * 4);
+  w.li.cnt = (int*)take((size_t)ET * 4);
+  w.li.tok = (int*)take((size_t)ET * 32 * 4);
+  w.li.slot = (int*)take((size_t)ET * 32 * 4);
+  w.li.wgt = (float*)take((size_t)ET * 32 * 4);
+  w.li.active = (int*)take((size_t)ET * 4);
+  w.li.n_active = (int*)take(4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t moe_ws_bytes(const dlm_model_desc& d) {
+  if (!d.n_experts) return 0;
+  return moe_ws_layout(moe_dims(d), nullptr).total;
+}
+
+void moe_views(const MoeDims& m, void* ws, dlm_decode_views* out) {
+  MoeWs w = moe_ws_layout(m, (char*)ws);
+  out->moe_logits = w.logits;
+  out->moe_xq = w.xq;
+  out->moe_xs = w.xs;
+  out->moe_cnt = w.li.cnt;
+  out->moe_rows = w.li.tok;
+  out->moe_slots = w.li.slot;
+  out->moe_wgt = w.li.wgt;
+  out->moe_active = w.li.active;
+  out->moe_n_active = w.li.n_active;
+  out->moe_aq = w.aq;
+  out->moe_as = w.as;
+  out->moe_y = w.y;
+}
+
+int moe_pack_layer(const MoeDims& m, const dlm_layer_weights& L, void* dst, hipStream_t st) {
+  const int ET = m.E + m.S;
+  uint8_t* out = (uint8_t*)dst;
+  // per expert: w13 codes, w13 scales, w2 codes, w2 scales
+  // (packed as four arrays over all experts so each kernel sees a fixed expert stride)
+  uint8_t* w13 = out;
+  uint8_t* w13s = w13 + (size_t)ET * m.w13_bytes();
+  uint8_t* w2 = w13s + (size_t)ET * m.w13_scale_bytes();
+  uint8_t* w2s = w2 + (size_t)ET * m.w2_bytes();
+  MxPackP p;
+  p.src = (const uint8_t*)L.x_w13;
+  p.src_scale = (const uint8_t*)L.x_w13_scale;
+  p.dst = w13;
+  p.dst_scale = w13s;
+  p.R = 2 * m.F;
+  p.K = m.d;
+  p.interleave = 1;
+  p.chunks = (long long)ET * p.R * p.K / 32;
+  hipLaunchKernelGGL(mx_pack_kernel, dim3((unsigned)((p.chunks + 255) / 256)), dim3(256), 0, st, p);
+  DLM_HIP(hipGetLastError());
+  p.src = (const uint8_t*)L.x_w2;
+  p.src_scale = (const uint8_t*)L.x_w2_scale;
+  p.dst = w2;
+  p.dst_scale = w2s;
+  p.R = m.d;
+  p.K = m.F;
+  p.interleave = 0;
+  p.chunks = (long long)ET * p.R * p.K / 32;
+  hipLaunchKernelGGL(mx_pack_kernel, dim3((unsigned)((p.chunks + 255) / 256)), dim3(256), 0, st, p);
+  return check_hip(hipGetLastError(), "moe pack launch");
+}
+
+int moe_ffn(const MoeDims& m, const void* f, const void* router_packed, GemmPlan router_plan, const void* experts,
+            void* ws, void* gemm_ws, const int32_t* cont_dev, PartialSrc* out, hipStream_t st) {
+  if (m.rows > kMaxRows || m.E + m.S > kMaxExperts || m.E > 256 || m.top_k > 8)
+    return fail(DLM_ERR_SHAPE, "moe: unsupported shape");
+  MoeWs w = moe_ws_layout(m, (char*)ws);
+  const int ET = m.E + m.S;
+  // 1. router logits
+  EpiParams e;
+  memset(&e, 0, sizeof(e));
+  e.kind = EPI_STORE_F32;
+  e.M = m.rows;
+  e.bf16_out = 1;
+  e.out = w.logits;
+  e.ld_out = m.E;
+  e.cont_dev = cont_dev;
+  int rc = gemm_bf16(router_packed, f, m.E, m.d, MAP_IDENTITY, e, router_plan, gemm_ws, st);
+  if (rc) return rc;
+  // 2. route + quantise
+  RouteP rp;
+  rp.m = m;
+  rp.logits = w.logits;
+  rp.f = (const uint16_t*)f;
+  rp.xq = w.xq;
+  rp.xs = w.xs;
+  rp.li = w.li;
+  rp.cont_dev = cont_dev;
+  hipLaunchKernelGGL(moe_route_kernel, dim3(m.rows + 1), dim3(256), 0, st, rp);
+  DLM_HIP(hipGetLastError());
+  // 3. up (gate/up + SwiGLU + MXFP8 of act)
+  const uint8_t* base = (const uint8_t*)experts;
+  ExpP up;
+  up.m = m;
+  up.w = base;
+  up.ws = base + (size_t)ET * m.w13_bytes();
+  up.w_stride = m.w13_bytes();
+  up.s_stride = m.w13_scale_bytes();
+  up.Q = 2 * m.F / 64;
+  up.S = m.d / 128;
+  up.bq = w.xq;
+  up.bs = w.xs;
+  up.b_by_slot = 0;
+  up.li = w.li;
+  up.aq = w.aq;
+  up.as = w.as;
+  up.y = nullptr;
+  up.cont_dev = cont_dev;
+  hipLaunchKernelGGL(moe_expert_kernel<1>, dim3(ET * up.Q), dim3(64), 0, st, up);
+  DLM_HIP(hipGetLastError());
+  // 4. down (weighted, per slot)
+  ExpP dn = up;
+  dn.w = base + (size_t)ET * (m.w13_bytes() + m.w13_scale_bytes());
+  dn.ws = dn.w + (size_t)ET * m.w2_bytes();
+  dn.w_stride = m.w2_bytes();
+  dn.s_stride = m.w2_scale_bytes();
+  dn.Q = m.d / 64;
+  dn.S = m.F / 128;
+  dn.bq = w.aq;
+  dn.bs = w.as;
+  dn.b_by_slot = 1;
+  dn.aq = nullptr;
+  dn.as = nullptr;
+  dn.y = w.y;
+  hipLaunchKernelGGL(moe_expert_kernel<0>, dim3(ET * dn.Q), dim3(64), 0, st, dn);
+  DLM_HIP(hipGetLastError());
+  PartialSrc ps{};
+  ps.slots = w.y;
+  ps.nslot = m.NS;
+  *out = ps;
+  return DLM_OK;
+}
+
 }  // namespace dlm

@@ -68,6 +68,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
       *(f32x4_t*)(x + c) = xv[j];
     }
   }
+  if (!p.ps.base && p.ps.slots) {
+    const float* sl = p.ps.slots + (size_t)row * p.ps.nslot * p.d;
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int c = 4 * (tid + 256 * j);
+      if (c >= p.d) continue;
+      for (int i = 0; i < p.ps.nslot; ++i) xv[j] += *(const f32x4_t*)(sl + (size_t)i * p.d + c);
+      *(f32x4_t*)(x + c) = xv[j];
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < MAXV; ++j)

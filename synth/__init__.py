@@ -160,14 +160,13 @@ def encode_mxfp4(x: np.ndarray):
     e = np.clip(e, -127, 127)
     scaled = blk / np.exp2(e)[..., None]
     mag = np.minimum(np.abs(scaled), 6.0)
-    # nearest grid point, ties to the even index (even index == even mantissa bit)
-    d = np.abs(mag[..., None] - _E2M1_GRID)
-    best = d.min(axis=-1, keepdims=True)
-    cand = np.isclose(d, best, rtol=0, atol=1e-12)
-    idx_any = np.argmax(cand, axis=-1)
-    n_cand = cand.sum(axis=-1)
-    tie_even = np.where(cand & ((np.arange(8) % 2) == 0), np.arange(8), 99).min(axis=-1)
-    idx = np.where(n_cand > 1, tie_even, idx_any)
+    # nearest grid point, ties to the even index (even index == even mantissa bit): the number
+    # of midpoints below mag is the lower neighbour's index; a value exactly on a midpoint
+    # between an odd and an even index moves to the even one
+    mids = (_E2M1_GRID[1:] + _E2M1_GRID[:-1]) / 2
+    idx = np.searchsorted(mids, mag, side="left")
+    on_mid = mag == mids[np.minimum(idx, len(mids) - 1)]
+    idx = np.where(on_mid & (idx % 2 == 1), idx + 1, idx)
     sign = (scaled < 0) & (idx > 0)
     code = (sign.astype(np.uint8) << 3) | idx.astype(np.uint8)
     code = code.reshape(x.shape[:-1] + (K,))

@@ -35,3 +35,20 @@ def storage(a: np.ndarray, dtype: str):
     if dtype == "bf16":
         return dev_bf16(a)
     return dev_f32(a)
+
+
+def moe_device_weights(w):
+    """Router (bf16) and natural-layout MXFP4 expert stacks of every layer of a MoE synth model:
+    x_w13 [E+S, 2F, d/2] (gate rows then up rows), x_w2 [E+S, d, F/2], and their e8m0 scales."""
+    s = w.shape
+    out = {}
+    for i in range(s.n_layers):
+        out[f"l{i}.router"] = dev_bf16(w[f"l{i}.router"])
+        gp, gs = w.expert_stack(i, "wg")
+        up, us = w.expert_stack(i, "wu")
+        dp, ds = w.expert_stack(i, "wd")
+        for name, arr in ((f"l{i}.x_w13", np.concatenate([gp, up], axis=1)),
+                          (f"l{i}.x_w13_scale", np.concatenate([gs, us], axis=1)),
+                          (f"l{i}.x_w2", dp), (f"l{i}.x_w2_scale", ds)):
+            out[name] = torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+    return out
