@@ -73,6 +73,90 @@ def commit_pass_bytes(shape, L):
     return (s.n_layers - 1) * per_layer + last + kv
 
 
+def moe_dense_pass_bytes(s, L, with_head):
+    """Bytes of one forward of the MoE model apart from the routed experts: attention weights,
+    router, KV, and (rounds) the head and the adapter."""
+    D = s.head_dim
+    attn_w = 2 * ((s.hq + 2 * s.hkv) * D * s.d + s.d * s.hq * D)
+    per_layer = attn_w + 2 * s.n_experts * s.d + 2 * 2 * s.hkv * D * (L + s.block)
+    if with_head:
+        return s.n_layers * per_layer + 2 * s.vocab * s.d + 2 * s.d * s.d
+    last = 2 * (s.hq + 2 * s.hkv) * D * s.d
+    return (s.n_layers - 1) * per_layer + last
+
+
+def moe_expert_bytes(s):
+    F, d = s.expert_ffn, s.d
+    return 2 * F * d // 2 + 2 * F * d // 32 + d * F // 2 + d * F // 32
+
+
+def run_moe(args, torch, dlm, synth, np):
+    """The MoE configuration: bf16 attention and head, MXFP4 experts (codes drawn on the device
+    from a seeded generator: expert values do not change the work), k commits per round."""
+    s = synth.MOE16B
+    t0 = time.time()
+    w = synth.Weights(s, args.seed, cache=False)
+    dev = {}
+    for n in w.names_dense():
+        a = w[n]
+        dev[n] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed)
+    ET, F, d = s.n_experts + s.n_shared, s.expert_ffn, s.d
+    for i in range(s.n_layers):
+        for name, shp in (("x_w13", (ET, 2 * F, d // 2)), ("x_w2", (ET, d, F // 2))):
+            dev[f"l{i}.{name}"] = torch.randint(0, 256, shp, dtype=torch.uint8, device="cuda", generator=gen)
+            sshp = shp[:-1] + (shp[-1] * 2 // 32,)
+            dev[f"l{i}.{name}_scale"] = torch.randint(119, 122, sshp, dtype=torch.uint8, device="cuda", generator=gen)
+    B = s.block
+    cap = args.prompt + (args.moe_blocks + 2) * B
+    model = dlm.Model(s, dev, cap=cap)
+    for i in range(s.n_layers):          # decode reads only the packed copies
+        for name in ("x_w13", "x_w13_scale", "x_w2", "x_w2_scale"):
+            dev.pop(f"l{i}.{name}")
+    torch.cuda.empty_cache()
+    log(f"moe model built in {time.time() - t0:.1f}s")
+    prompt = torch.from_numpy(synth.prompt_ids(s, args.prompt, args.seed))
+    rule = dlm.CommitRule.fixed_k(args.k)
+    model.set_len(0)
+    model.prefill(prompt)
+    model.decode_block(rule)
+    torch.cuda.synchronize()
+    model.set_len(args.prompt)
+    hits = model.view("moe_hits", (s.n_layers,), torch.int32)
+    hits.zero_()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    host_tok = torch.empty(args.moe_blocks, B, dtype=torch.int32).pin_memory()
+    ev0.record()
+    for i in range(args.moe_blocks):
+        model.decode_block(rule)
+        host_tok[i].copy_(model.tokens, non_blocking=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3
+    R = math.ceil(B / args.k)
+    total_hits = int(hits.sum().item())
+    dense = sum(R * moe_dense_pass_bytes(s, args.prompt + B * i, True) +
+                moe_dense_pass_bytes(s, args.prompt + B * i, False) for i in range(args.moe_blocks))
+    total = dense + total_hits * moe_expert_bytes(s)
+    forwards_per_block = R * s.n_layers + (s.n_layers - 1)
+    out = {"workload": f"MoE 16B-A1B-shaped (20 layers, d 2048, 256 experts of 512 top-8 + 1 shared, MXFP4 "
+                       f"experts, MXFP8 activations), bs=1, block 32, fixed k={args.k}, prompt {args.prompt}, "
+                       f"{args.moe_blocks * B} new tokens",
+           "tok_s": args.moe_blocks * B / sec, "rounds_s": args.moe_blocks * R / sec,
+           "ms_per_block": 1e3 * sec / args.moe_blocks, "hbm_frac": total / sec / HBM_PEAK,
+           "mean_experts_hit_per_layer_forward": total_hits / (args.moe_blocks * forwards_per_block),
+           "bytes_per_block": total / args.moe_blocks}
+    log(f"moe k={args.k}: {out['tok_s']:.0f} tok/s, {out['ms_per_block']:.2f} ms/block, "
+        f"{100 * out['hbm_frac']:.1f}% of 8 TB/s, {out['mean_experts_hit_per_layer_forward']:.1f} experts/layer")
+    model.close()
+    del model, dev
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +168,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=1)
+    ap.add_argument("--moe-blocks", type=int, default=64,
+                    help="blocks of the MoE model decoded at k = --k (0 skips the MoE leg)")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel leg plus a 256 MiB device copy (for counter runs)")
     args = ap.parse_args()
@@ -201,6 +287,15 @@ def main():
         model.close()
         return
 
+    moe = None
+    if args.moe_blocks > 0:
+        model.close()
+        del model
+        dev_w.clear()
+        torch.cuda.empty_cache()
+        moe = run_moe(args, torch, dlm, synth, np)
+        model = None
+
     # ---- CPU baseline: the oracle in float32 on a bounded sample (one round + one commit pass)
     cpu = None
     if not args.no_cpu_baseline:
@@ -244,10 +339,11 @@ def main():
         "rounds_per_s": h["rounds_s"], "hbm_frac_step": h["hbm_frac"],
         "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
                   for k, r in results.items()},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "moe": moe,
     }
     print(json.dumps(line), flush=True)
-    model.close()
+    if model is not None:
+        model.close()
 
 
 if __name__ == "__main__":

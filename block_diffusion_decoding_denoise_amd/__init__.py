@@ -82,8 +82,8 @@ class KV(ctypes.Structure):
 
 class DecodeViews(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("x", "hn", "pe", "lse", "entropy", "maxprob", "argmax", "committed", "xn",
-                                               "moe_logits", "moe_xq", "moe_xs", "moe_cnt", "moe_rows", "moe_slots",
-                                               "moe_wgt", "moe_active", "moe_n_active", "moe_aq", "moe_as", "moe_y")]
+                                               "moe_logits", "moe_xq", "moe_xs", "moe_ids", "moe_wts", "moe_aq",
+                                               "moe_as", "moe_y", "moe_hits")]
 
 
 # ------------------------------------------------------------------ loading

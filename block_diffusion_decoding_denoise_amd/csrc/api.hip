@@ -308,8 +308,8 @@ static int check_model_desc(const dlm_model_desc* d) {
                 DLM_ERR_SHAPE, "top_k in [1, 8], n_experts <= 256");
     DLM_REQUIRE(d->expert_ffn % 128 == 0 && d->expert_ffn > 0 && d->n_shared >= 0 && d->n_shared <= 2,
                 DLM_ERR_SHAPE, "expert_ffn %% 128 == 0, n_shared <= 2");
-    DLM_REQUIRE(d->n_experts % 32 == 0 && d->d % 128 == 0 && d->block <= 32, DLM_ERR_SHAPE,
-                "MoE: n_experts %% 32 == 0, d %% 128 == 0, block <= 32");
+    DLM_REQUIRE(d->n_experts % 32 == 0 && d->d % 256 == 0 && d->block <= 32 && d->n_layers <= 256, DLM_ERR_SHAPE,
+                "MoE: n_experts %% 32 == 0, d %% 256 == 0, block <= 32, n_layers <= 256");
   }
   if (d->dtype == DLM_F32) DLM_REQUIRE(d->d <= 256, DLM_ERR_SHAPE, "f32 models support d <= 256");
   return DLM_OK;
@@ -349,7 +349,7 @@ static void layout_packed(dlm_model* m) {
   } else {
     m->pl_gu = m->pl_dn = GemmPlan{1, 1, 0};
   }
-  m->pl_router = d.n_experts ? gemm_plan(d.n_experts, d.d) : GemmPlan{1, 1, 0};
+  m->pl_router = d.n_experts ? gemm_plan_owned(d.n_experts, d.d) : GemmPlan{1, 1, 0};
 }
 
 extern "C" size_t dlm_packed_bytes(const dlm_model_desc* d) {
@@ -434,7 +434,10 @@ extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const d
     } else {
       const void* sr[1] = {L.router};
       int rr[1] = {d->n_experts};
-      if ((rc = pack_bf16(sr, rr, 1, d->n_experts, d->d, nullptr, out + m.off_router[l], st))) return rc;
+      rc = m.pl_router.R
+               ? pack_bf16_owned(sr, rr, 1, d->n_experts, d->d, nullptr, m.pl_router.R, out + m.off_router[l], st)
+               : pack_bf16(sr, rr, 1, d->n_experts, d->d, nullptr, out + m.off_router[l], st);
+      if (rc) return rc;
       if ((rc = moe_pack_layer(moe_dims(*d), L, out + m.off_moe[l], st))) return rc;
     }
   }
@@ -648,7 +651,7 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     ps = PartialSrc{};
     if (d.n_experts) {
       // the experts' weighted outputs are added into x by the next RMSNorm, slot by slot
-      if ((rc = moe_ffn(moe_dims(d), w.xn, pk + m->off_router[l], m->pl_router, pk + m->off_moe[l], w.moe_ws,
+      if ((rc = moe_ffn(moe_dims(d), l, w.xn, pk + m->off_router[l], m->pl_router, pk + m->off_moe[l], w.moe_ws,
                         w.gemm_ws, cont, &ps, st)))
         return rc;
       continue;

@@ -29,7 +29,8 @@ void moe_views(const MoeDims& m, void* ws, dlm_decode_views* out);
 // f: bf16 normed rows in the packed activation order; router_packed: the router matrix packed
 // for the stream-K GEMM (router_plan); experts: the layer's packed experts.  Writes each row's
 // weighted expert outputs to per-slot rows that *out describes (the next RMSNorm adds them).
-int moe_ffn(const MoeDims& m, const void* f, const void* router_packed, GemmPlan router_plan,
+// Each call adds its number of distinct experts hit to a per-layer counter in ws (statistics).
+int moe_ffn(const MoeDims& m, int layer, const void* f, const void* router_packed, GemmPlan router_plan,
             const void* experts, void* ws, void* gemm_ws, const int32_t* cont_dev, PartialSrc* out,
             hipStream_t st);
 

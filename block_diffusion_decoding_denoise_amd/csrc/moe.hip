@@ -47,6 +47,7 @@ namespace {
 
 constexpr int kMaxRows = 32;
 constexpr int kMaxExperts = 512;
+constexpr int kMaxLayers = 256;
 
 // -------------------------------------------------------------------- MX number formats
 // Shared exponent of a block for an element format whose largest exponent is emax:
@@ -129,13 +130,10 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(MxPackP p) {
 }
 
 // -------------------------------------------------------------------- route + quantise
-struct Lists {
-  int* cnt;        // [E + S]
-  int* tok;        // [E + S][32] rows in row order
-  int* slot;       // [E + S][32] output slot (row * NS + rank)
-  float* wgt;      // [E + S][32] mixing weight
-  int* active;     // [E + S] experts with cnt > 0, in id order
-  int* n_active;   // [1]
+struct Route {
+  int* ids;        // [32][top_k] expert of each rank, by (probability desc, id asc)
+  float* wts;      // [32][top_k] its probability (the mixing weight)
+  int* hits;       // [n_layers] running count of distinct experts per layer (statistics)
 };
 
 struct RouteP {
@@ -144,126 +142,83 @@ struct RouteP {
   const uint16_t* f;       // bf16 packed activations, 32 x d
   uint8_t* xq;             // [32][d] e4m3 codes
   uint8_t* xs;             // [32][d/32] e8m0
-  Lists li;
+  Route ro;
   const int32_t* cont_dev;
 };
 
+// One workgroup per row of the block: the row's MXFP8 input, then its softmax over the E
+// routed experts and the top-k by rank (rank of e = number of experts with a larger
+// probability, or an equal one and a lower id), so no serial selection loop runs.
 __global__ __launch_bounds__(256) void moe_route_kernel(RouteP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   const MoeDims& m = p.m;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if ((int)blockIdx.x < m.rows) {
-    // MXFP8 of row `row` of f: one 32-column block per thread
-    const int row = blockIdx.x;
-    for (int b = tid; b < m.d / 32; b += 256) {
-      float v[32];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ __align__(16) float s_p[256];
+  __shared__ float red[4];
+  const bool has = tid < m.E;
+  const float r = has ? p.logits[(size_t)row * m.E + tid] : -INFINITY;   // issued before the MX work
+  for (int b = tid; b < m.d / 32; b += 256) {
+    float v[32];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const u32x4_t w = *(const u32x4_t*)(p.f + xpk_index(row, 32 * b + 8 * h));
+    for (int h = 0; h < 4; ++h) {
+      const u32x4_t w = *(const u32x4_t*)(p.f + xpk_index(row, 32 * b + 8 * h));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[8 * h + 2 * e] = lo_bf(w[e]);
-          v[8 * h + 2 * e + 1] = hi_bf(w[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        v[8 * h + 2 * e] = lo_bf(w[e]);
+        v[8 * h + 2 * e + 1] = hi_bf(w[e]);
       }
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      const int e = mx_shared_exp(amax, 8);
-      const float inv = ldexpf(1.f, -e);
-      uint32_t words[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        words[i] = e4m3_code(v[4 * i] * inv) | (e4m3_code(v[4 * i + 1] * inv) << 8) |
-                   (e4m3_code(v[4 * i + 2] * inv) << 16) | (e4m3_code(v[4 * i + 3] * inv) << 24);
-      u32x4_t* dst = (u32x4_t*)(p.xq + (size_t)row * m.d + 32 * b);
-      dst[0] = u32x4_t{words[0], words[1], words[2], words[3]};
-      dst[1] = u32x4_t{words[4], words[5], words[6], words[7]};
-      p.xs[(size_t)row * (m.d / 32) + b] = (uint8_t)(e + 127);
     }
-    return;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const int e = mx_shared_exp(amax, 8);
+    const float inv = ldexpf(1.f, -e);
+    uint32_t words[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      words[i] = e4m3_code(v[4 * i] * inv) | (e4m3_code(v[4 * i + 1] * inv) << 8) |
+                 (e4m3_code(v[4 * i + 2] * inv) << 16) | (e4m3_code(v[4 * i + 3] * inv) << 24);
+    u32x4_t* dst = (u32x4_t*)(p.xq + (size_t)row * m.d + 32 * b);
+    dst[0] = u32x4_t{words[0], words[1], words[2], words[3]};
+    dst[1] = u32x4_t{words[4], words[5], words[6], words[7]};
+    p.xs[(size_t)row * (m.d / 32) + b] = (uint8_t)(e + 127);
   }
-  // routing: wave w takes rows w, w + 4, ...; lane holds experts lane + 64 i
-  __shared__ int s_ids[kMaxRows][8];
-  __shared__ float s_w[kMaxRows][8];
-  __shared__ int s_cnt[kMaxExperts];
-  constexpr int EPL = 4;   // experts per lane (E <= 256)
-  for (int row = wave; row < m.rows; row += 4) {
-    float r[EPL];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      r[i] = e < m.E ? p.logits[(size_t)row * m.E + e] : -INFINITY;
-      mx = fmaxf(mx, r[i]);
-    }
-    mx = wave_max(mx);
-    float pr[EPL], s = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      pr[i] = lane + 64 * i < m.E ? expf(r[i] - mx) : 0.f;
-      s += pr[i];
-    }
-    s = wave_sum(s);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) pr[i] = lane + 64 * i < m.E ? pr[i] / s : -1.f;
-    for (int j = 0; j < m.top_k; ++j) {
-      // largest probability, lowest id on ties
-      float bv = -2.f;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (pr[i] > bv) { bv = pr[i]; bi = lane + 64 * i; }
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + 64 * i == bi) pr[i] = -1.f;
-      if (lane == 0) {
-        s_ids[row][j] = bi;
-        s_w[row][j] = bv;
-      }
-    }
-  }
+  // softmax over the routed experts (thread t holds expert t; E <= 256)
+  float mx = wave_max(r);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  const int ET = m.E + m.S;
-  for (int t = tid; t < ET; t += 256) {
-    int n = 0;
-    if (t < m.E) {
-      for (int i = 0; i < m.rows; ++i)
-        for (int j = 0; j < m.top_k; ++j)
-          if (s_ids[i][j] == t) {
-            p.li.tok[t * 32 + n] = i;
-            p.li.slot[t * 32 + n] = i * m.NS + j;
-            p.li.wgt[t * 32 + n] = s_w[i][j];
-            ++n;
-          }
-    } else {
-      for (int i = 0; i < m.rows; ++i) {
-        p.li.tok[t * 32 + i] = i;
-        p.li.slot[t * 32 + i] = i * m.NS + m.top_k + (t - m.E);
-        p.li.wgt[t * 32 + i] = 1.f;
-      }
-      n = m.rows;
-    }
-    p.li.cnt[t] = n;
-    s_cnt[t] = n;
-  }
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    for (int t = 0; t < ET; ++t)
-      if (s_cnt[t] > 0) p.li.active[a++] = t;
-    *p.li.n_active = a;
+  const float ex = has ? expf(r - mx) : 0.f;
+  float sum = wave_sum(ex);
+  if ((tid & 63) == 0) red[tid >> 6] = sum;
+  __syncthreads();
+  sum = ((red[0] + red[1]) + red[2]) + red[3];
+  const float pr = ex / sum;
+  s_p[tid] = has ? pr : -1.f;
+  __syncthreads();
+  if (!has) return;
+  int rank = 0;
+  const f32x4_t* sp4 = (const f32x4_t*)s_p;
+#pragma unroll 8
+  for (int e4 = 0; e4 < m.E / 4; ++e4) {
+    const f32x4_t q = sp4[e4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * e4 + i;
+      rank += (q[i] > pr || (q[i] == pr && e < tid)) ? 1 : 0;
+    }
+  }
+  if (rank < m.top_k) {
+    p.ro.ids[row * m.top_k + rank] = tid;
+    p.ro.wts[row * m.top_k + rank] = pr;
   }
 }
 
 // -------------------------------------------------------------------- expert projections
 struct ExpP {
   MoeDims m;
+  int layer;
   const uint8_t* w;        // packed codes of this layer's matrix of expert 0
   const uint8_t* ws;       // packed scales of expert 0
   size_t w_stride, s_stride;   // bytes per expert
@@ -271,36 +226,75 @@ struct ExpP {
   const uint8_t* bq;       // B operand codes: [rows or slots][K]
   const uint8_t* bs;       // B operand scales: [rows or slots][K/32]
   int b_by_slot;           // B rows are indexed by slot (down) or by row (up)
-  Lists li;
+  Route ro;
   uint8_t* aq;             // up: act codes [32 NS][F]
   uint8_t* as;             // up: act scales [32 NS][F/32]
   float* y;                // down: [32 NS][d]
   const int32_t* cont_dev;
 };
 
-// One wave per (hit expert, quad): 4 row groups x up to 2 groups of 16 rows of the block, K in
-// steps of 128, the weight steps prefetched PF at a time.
+// One single-wave workgroup per (expert, quad).  The wave first finds the block's rows routed
+// to the expert (row order, from the top-k table; every row for a shared expert); a workgroup
+// whose expert no row chose exits before touching its weights.  It then runs 4 row groups x up
+// to 2 groups of 16 rows, K in steps of 128, PF weight steps in flight.
 template <int UP>
 __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
-  const int item = blockIdx.x;
-  const int a = item / p.Q, q = item % p.Q;
-  if (a >= *p.li.n_active) return;
-  const int e = p.li.active[a];
-  const int n = p.li.cnt[e];
+  const MoeDims& m = p.m;
+  const int e = blockIdx.x / p.Q, q = blockIdx.x % p.Q;
   const int lane = threadIdx.x;
+  __shared__ int s_n;
+  __shared__ int s_row[32], s_slot[32];
+  __shared__ float s_w[32];
+  {
+    int n = 0;
+    if (e >= m.E) {
+      if (lane < m.rows) {
+        s_row[lane] = lane;
+        s_slot[lane] = lane * m.NS + m.top_k + (e - m.E);
+        s_w[lane] = 1.f;
+      }
+      n = m.rows;
+    } else {
+      const int total = m.rows * m.top_k;         // <= 256 entries, row-major (row, rank)
+      for (int c = 0; c < total; c += 64) {
+        const int idx = c + lane;
+        const bool hit = idx < total && p.ro.ids[idx] == e;
+        const unsigned long long mask = __ballot(hit);
+        if (hit) {
+          const int pos = n + __popcll(mask & ((1ull << lane) - 1));
+          const int i = idx / m.top_k;
+          s_row[pos] = i;
+          s_slot[pos] = i * m.NS + idx % m.top_k;
+          s_w[pos] = p.ro.wts[idx];
+        }
+        n += __popcll(mask);
+      }
+    }
+    if (lane == 0) {
+      s_n = n;
+      if (UP && q == 0 && n > 0) atomicAdd(&p.ro.hits[p.layer], 1);
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  if (n == 0) return;
   const int K = 128 * p.S;
   const bool two = n > 16;
-  int col[2], brow[2];
+  int col[2], brow[2], slot[2];
 #pragma unroll
   for (int cg = 0; cg < 2; ++cg) {
     col[cg] = 16 * cg + (lane & 15);
     brow[cg] = -1;
-    if (col[cg] < n) brow[cg] = p.b_by_slot ? p.li.slot[e * 32 + col[cg]] : p.li.tok[e * 32 + col[cg]];
+    slot[cg] = -1;
+    if (col[cg] < n) {
+      slot[cg] = s_slot[col[cg]];
+      brow[cg] = p.b_by_slot ? slot[cg] : s_row[col[cg]];
+    }
   }
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + e * p.w_stride + (size_t)q * p.S * 4096, (uint32_t)p.S * 4096u);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.ws + e * p.s_stride + (size_t)q * p.S * 256, (uint32_t)p.S * 256u);
-  const int n_brows = p.b_by_slot ? 32 * p.m.NS : 32;
+  const int n_brows = p.b_by_slot ? 32 * m.NS : 32;
   const __amdgpu_buffer_rsrc_t br = make_rsrc(p.bq, (uint32_t)(n_brows * K));
   const __amdgpu_buffer_rsrc_t bsr = make_rsrc(p.bs, (uint32_t)(n_brows * (K / 32)));
   uint32_t bo[2], bso[2];
@@ -314,16 +308,27 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
   for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[cg][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // ring of PF steps: weights (4 row groups) and the block rows' activations (2 column groups)
   constexpr int PF = 4;
-  u32x4_t wa[PF][4];
-  uint32_t ws[PF][4];
-#pragma unroll
-  for (int u = 0; u < PF; ++u)
+  u32x4_t wa[PF][4], blo[PF][2], bhi[PF][2];
+  uint32_t wsc[PF][4], bsc[PF][2];
+  auto fetch = [&](int u, int s) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      wa[u][g] = bload16_nt(wr, (uint32_t)((u * 4 + g) * 64 + lane) * 16u);
-      ws[u][g] = bload_u8(sr, (uint32_t)((u * 4 + g) * 64 + lane));
+      wa[u][g] = bload16_nt(wr, (uint32_t)((s * 4 + g) * 64 + lane) * 16u);
+      wsc[u][g] = bload_u8(sr, (uint32_t)((s * 4 + g) * 64 + lane));
     }
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      if (cg == 1 && !two) break;
+      const uint32_t off = s < p.S ? bo[cg] + 128u * s : 0x80000000u;
+      blo[u][cg] = bload16(br, off);
+      bhi[u][cg] = bload16(br, off + 64u);
+      bsc[u][cg] = bload_u8(bsr, s < p.S ? bso[cg] + 4u * s : 0x80000000u);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < PF; ++u) fetch(u, u);
   for (int s0 = 0; s0 < p.S; s0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
@@ -332,19 +337,12 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg) {
           if (cg == 1 && !two) break;
-          const u32x4_t lo = bload16(br, bo[cg] + 128u * s);
-          const u32x4_t hi = bload16(br, bo[cg] + 128u * s + 64u);
-          const int sb = (int)bload_u8(bsr, bso[cg] + 4u * s);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) acc[cg][g] = mfma_mx(wa[u][g], lo, hi, (int)ws[u][g], sb, acc[cg][g]);
+          for (int g = 0; g < 4; ++g)
+            acc[cg][g] = mfma_mx(wa[u][g], blo[u][cg], bhi[u][cg], (int)wsc[u][g], (int)bsc[u][cg], acc[cg][g]);
         }
       }
-      const int sn = s + PF;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        wa[u][g] = bload16_nt(wr, (uint32_t)((sn * 4 + g) * 64 + lane) * 16u);
-        ws[u][g] = bload_u8(sr, (uint32_t)((sn * 4 + g) * 64 + lane));
-      }
+      fetch(u, s + PF);
     }
   }
   // epilogue.  acc[cg][g][r] = D[row 64q + 16g + 4(l/16) + r][column col[cg]]
@@ -369,22 +367,20 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
       const int ex = mx_shared_exp(amax, 8);
       const float inv = ldexpf(1.f, -ex);
       if (valid) {
-        const int sl = p.li.slot[e * 32 + col[cg]];   // B rows are the block's rows; act goes to the slot
-        uint8_t* dst = p.aq + (size_t)sl * p.m.F + 32 * q + 2 * (lane >> 4);
+        uint8_t* dst = p.aq + (size_t)slot[cg] * m.F + 32 * q + 2 * (lane >> 4);
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *(uint16_t*)(dst + 8 * g) = (uint16_t)(e4m3_code(act[g][0] * inv) | (e4m3_code(act[g][1] * inv) << 8));
-        if ((lane >> 4) == 0) p.as[(size_t)sl * (p.m.F / 32) + q] = (uint8_t)(ex + 127);
+        if ((lane >> 4) == 0) p.as[(size_t)slot[cg] * (m.F / 32) + q] = (uint8_t)(ex + 127);
       }
     } else if (valid) {
-      const int sl = brow[cg];
-      const float wgt = p.li.wgt[e * 32 + col[cg]];
+      const float wgt = s_w[col[cg]];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4_t o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[r] = wgt * acc[cg][g][r];
-        *(f32x4_t*)(p.y + (size_t)sl * p.m.d + 64 * q + 16 * g + 4 * (lane >> 4)) = o;
+        *(f32x4_t*)(p.y + (size_t)slot[cg] * m.d + 64 * q + 16 * g + 4 * (lane >> 4)) = o;
       }
     }
   }
@@ -394,7 +390,7 @@ struct MoeWs {
   float* logits;
   uint8_t *xq, *xs, *aq, *as;
   float* y;
-  Lists li;
+  Route ro;
   size_t total;
 };
 
@@ -402,19 +398,15 @@ MoeWs moe_ws_layout(const MoeDims& m, char* base) {
   MoeWs w;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return base ? base + o : nullptr; };
-  const int ET = m.E + m.S;
   w.logits = (float*)take((size_t)kMaxRows * m.E * 4);
   w.xq = (uint8_t*)take((size_t)kMaxRows * m.d);
   w.xs = (uint8_t*)take((size_t)kMaxRows * m.d / 32);
   w.aq = (uint8_t*)take((size_t)kMaxRows * m.NS * m.F);
   w.as = (uint8_t*)take((size_t)kMaxRows * m.NS * m.F / 32);
   w.y = (float*)take((size_t)kMaxRows * m.NS * m.d * 4);
-  w.li.cnt = (int*)take((size_t)ET * 4);
-  w.li.tok = (int*)take((size_t)ET * 32 * 4);
-  w.li.slot = (int*)take((size_t)ET * 32 * 4);
-  w.li.wgt = (float*)take((size_t)ET * 32 * 4);
-  w.li.active = (int*)take((size_t)ET * 4);
-  w.li.n_active = (int*)take(4);
+  w.ro.ids = (int*)take((size_t)kMaxRows * 8 * 4);
+  w.ro.wts = (float*)take((size_t)kMaxRows * 8 * 4);
+  w.ro.hits = (int*)take((size_t)kMaxLayers * 4);
   w.total = off;
   return w;
 }
@@ -431,15 +423,12 @@ void moe_views(const MoeDims& m, void* ws, dlm_decode_views* out) {
   out->moe_logits = w.logits;
   out->moe_xq = w.xq;
   out->moe_xs = w.xs;
-  out->moe_cnt = w.li.cnt;
-  out->moe_rows = w.li.tok;
-  out->moe_slots = w.li.slot;
-  out->moe_wgt = w.li.wgt;
-  out->moe_active = w.li.active;
-  out->moe_n_active = w.li.n_active;
+  out->moe_ids = w.ro.ids;
+  out->moe_wts = w.ro.wts;
   out->moe_aq = w.aq;
   out->moe_as = w.as;
   out->moe_y = w.y;
+  out->moe_hits = w.ro.hits;
 }
 
 int moe_pack_layer(const MoeDims& m, const dlm_layer_weights& L, void* dst, hipStream_t st) {
@@ -474,9 +463,9 @@ int moe_pack_layer(const MoeDims& m, const dlm_layer_weights& L, void* dst, hipS
   return check_hip(hipGetLastError(), "moe pack launch");
 }
 
-int moe_ffn(const MoeDims& m, const void* f, const void* router_packed, GemmPlan router_plan, const void* experts,
-            void* ws, void* gemm_ws, const int32_t* cont_dev, PartialSrc* out, hipStream_t st) {
-  if (m.rows > kMaxRows || m.E + m.S > kMaxExperts || m.E > 256 || m.top_k > 8)
+int moe_ffn(const MoeDims& m, int layer, const void* f, const void* router_packed, GemmPlan router_plan,
+            const void* experts, void* ws, void* gemm_ws, const int32_t* cont_dev, PartialSrc* out, hipStream_t st) {
+  if (m.rows > kMaxRows || m.E + m.S > kMaxExperts || m.E > 256 || m.top_k > 8 || layer >= kMaxLayers)
     return fail(DLM_ERR_SHAPE, "moe: unsupported shape");
   MoeWs w = moe_ws_layout(m, (char*)ws);
   const int ET = m.E + m.S;
@@ -491,21 +480,22 @@ int moe_ffn(const MoeDims& m, const void* f, const void* router_packed, GemmPlan
   e.cont_dev = cont_dev;
   int rc = gemm_bf16(router_packed, f, m.E, m.d, MAP_IDENTITY, e, router_plan, gemm_ws, st);
   if (rc) return rc;
-  // 2. route + quantise
+  // 2. route + quantise, one workgroup per row
   RouteP rp;
   rp.m = m;
   rp.logits = w.logits;
   rp.f = (const uint16_t*)f;
   rp.xq = w.xq;
   rp.xs = w.xs;
-  rp.li = w.li;
+  rp.ro = w.ro;
   rp.cont_dev = cont_dev;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(m.rows + 1), dim3(256), 0, st, rp);
+  hipLaunchKernelGGL(moe_route_kernel, dim3(m.rows), dim3(256), 0, st, rp);
   DLM_HIP(hipGetLastError());
   // 3. up (gate/up + SwiGLU + MXFP8 of act)
   const uint8_t* base = (const uint8_t*)experts;
   ExpP up;
   up.m = m;
+  up.layer = layer;
   up.w = base;
   up.ws = base + (size_t)ET * m.w13_bytes();
   up.w_stride = m.w13_bytes();
@@ -515,7 +505,7 @@ int moe_ffn(const MoeDims& m, const void* f, const void* router_packed, GemmPlan
   up.bq = w.xq;
   up.bs = w.xs;
   up.b_by_slot = 0;
-  up.li = w.li;
+  up.ro = w.ro;
   up.aq = w.aq;
   up.as = w.as;
   up.y = nullptr;

@@ -319,22 +319,20 @@ typedef struct {
                         fed a GEMM (for MoE models, the input of the last routed-expert FFN) */
   /* MoE models, state of the last routed-expert FFN that ran (NULL for dense models):
    * router logits [32][E] f32; f as MXFP8: codes [32][d] e4m3 and e8m0 scales [32][d/32];
-   * per expert (E routed then S shared): row count [E+S], rows / slots (row*NS + rank) /
-   * mixing weights [E+S][32] in row order; experts hit [E+S] in id order and their count;
-   * act as MXFP8 per slot: codes [32*NS][F], scales [32*NS][F/32]; weighted expert outputs
-   * per slot y [32*NS][d] f32 (NS = top_k + S). */
+   * each row's top-k experts by rank [32][top_k] i32 and their probabilities [32][top_k] f32;
+   * act as MXFP8 per slot (row * NS + rank, shared experts after the routed ranks): codes
+   * [32*NS][F], scales [32*NS][F/32]; weighted expert outputs per slot y [32*NS][d] f32
+   * (NS = top_k + n_shared). */
   float* moe_logits;
   uint8_t* moe_xq;
   uint8_t* moe_xs;
-  int32_t* moe_cnt;
-  int32_t* moe_rows;
-  int32_t* moe_slots;
-  float* moe_wgt;
-  int32_t* moe_active;
-  int32_t* moe_n_active;
+  int32_t* moe_ids;
+  float* moe_wts;
   uint8_t* moe_aq;
   uint8_t* moe_as;
   float* moe_y;
+  int32_t* moe_hits;   /* [n_layers]: running count, per layer, of the distinct experts (shared
+                          included) each routed-expert FFN used since the workspace was zeroed */
 } dlm_decode_views;
 int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* ws, size_t ws_bytes,
                          dlm_decode_views* out);

@@ -89,7 +89,6 @@ def test_moe_stages_one_layer():
     m.decode_round(dlm.CommitRule.fixed_k(4))
     torch.cuda.synchronize()
     B, d, E, NS, F = s.block, s.d, s.n_experts, s.top_k + s.n_shared, s.expert_ffn
-    ET = E + s.n_shared
     prec = Prec("bf16")
     om = OracleModel(s, w, prec)
     x0 = np.tile(om.get("mask_emb"), (B, 1))
@@ -109,20 +108,10 @@ def test_moe_stages_one_layer():
     g_x = (xq.reshape(B, d // 32, 32) * np.exp2(xs - 127)[..., None]).reshape(B, d)
     np.testing.assert_array_equal(g_x, oracle.mxfp8_quant_dequant(f_gpu))
     f = f_gpu
-    # routing
+    # routing: each row's top-k by rank, with its probabilities
     ids, wts, probs = oracle.router_topk(f, om.get("l0.router"), s.top_k)
-    cnt = m.view("moe_cnt", (ET,), torch.int32).cpu().numpy()
-    rows = m.view("moe_rows", (ET, 32), torch.int32).cpu().numpy()
-    slots = m.view("moe_slots", (ET, 32), torch.int32).cpu().numpy()
-    wgt = m.view("moe_wgt", (ET, 32), torch.float32).cpu().numpy()
-    g_ids = np.full((B, s.top_k), -1)
-    g_w = np.zeros((B, s.top_k))
-    for e in range(E):
-        for n in range(cnt[e]):
-            i, j = rows[e, n], slots[e, n] - rows[e, n] * NS
-            g_ids[i, j] = e
-            g_w[i, j] = wgt[e, n]
-    assert (g_ids >= 0).all()
+    g_ids = m.view("moe_ids", (32, s.top_k), torch.int32).cpu().numpy()[:B]
+    g_w = m.view("moe_wts", (32, s.top_k), torch.float32).cpu().numpy()[:B].astype(np.float64)
     # the same experts in the same ranks, except where the oracle's own probabilities are within
     # 1e-3 (relative) of each other around the difference (near ties, counted)
     near = 0
@@ -134,7 +123,7 @@ def test_moe_stages_one_layer():
         assert gaps.min() < 1e-3, f"row {i}: routing {g_ids[i]} vs {ids[i]}"
         near += 1
     assert near <= B // 4
-    np.testing.assert_allclose(g_w[g_ids == ids], wts[g_ids == ids], rtol=2e-2)
+    np.testing.assert_allclose(g_w[g_ids == ids], wts[g_ids == ids], rtol=1e-4)
     # per-slot outputs from the GPU's own MXFP8 input and routing: routed expert j of row i,
     # weighted, and the shared expert
     y = m.view("moe_y", (32 * NS, d), torch.float32).cpu().numpy()
