@@ -174,7 +174,8 @@ def _dev(t: torch.Tensor, name: str):
 def block_attn(q, k_cache, v_cache, prefix_len, out=None, prefix_len_dev=None, max_prefix_len=None,
                scale=None, ws=None):
     """o = softmax(q K^T * scale) V over the L prefix keys and the B block keys (no mask).
-    q [B, hq, D]; k_cache [hkv, cap, D]; v_cache transposed [hkv, D, cap]; returns out [B, hq, D]."""
+    q [B, hq, D]; k_cache [hkv, cap, D]; v_cache in the blocked transposed layout
+    [hkv, cap/32, D, 32] (v_cache_from_natural); returns out [B, hq, D]."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
     B, hq, D = q.shape
@@ -319,8 +320,10 @@ class Model:
         tdt = torch.bfloat16 if dt == DLM_BF16 else torch.float32
         self.cap = cap
         self.k = [torch.zeros(s.hkv, cap, s.head_dim, dtype=tdt, device=device) for _ in range(s.n_layers)]
-        # V is cached transposed, [hkv, D, cap]
-        self.v = [torch.zeros(s.hkv, s.head_dim, cap, dtype=tdt, device=device) for _ in range(s.n_layers)]
+        # V is cached transposed in 32-position blocks, [hkv, cap/32, D, 32]
+        if cap % 32:
+            raise DlmError("cap must be a multiple of 32")
+        self.v = [torch.zeros(s.hkv, cap // 32, s.head_dim, 32, dtype=tdt, device=device) for _ in range(s.n_layers)]
         self._kptrs = (ctypes.c_void_p * s.n_layers)(*[t.data_ptr() for t in self.k])
         self._vptrs = (ctypes.c_void_p * s.n_layers)(*[t.data_ptr() for t in self.v])
         self.len_dev = torch.zeros(1, dtype=torch.int32, device=device)
@@ -408,6 +411,18 @@ class Model:
             out.append(self.tokens.cpu())
             states.append(state_dict(self.state))
         return torch.cat(out), states
+
+
+def v_cache_from_natural(v):
+    """[hkv, cap, D] values -> the library's V cache layout [hkv, cap/32, D, 32] (torch)."""
+    h, cap, D = v.shape
+    return v.reshape(h, cap // 32, 32, D).transpose(2, 3).contiguous()
+
+
+def v_cache_to_natural(vc):
+    """The library's V cache [hkv, cap/32, D, 32] -> [hkv, cap, D] (torch)."""
+    h, nb, D, _ = vc.shape
+    return vc.transpose(2, 3).reshape(h, nb * 32, D)
 
 
 def weights_to_device(w, names, device="cuda"):

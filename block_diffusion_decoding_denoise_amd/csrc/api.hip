@@ -70,6 +70,7 @@ static int check_attn(const dlm_attn_desc* d) {
   DLM_REQUIRE(d, DLM_ERR_ARG, "desc is null");
   DLM_REQUIRE(d->dtype == DLM_BF16 || d->dtype == DLM_F32, DLM_ERR_DTYPE, "attn dtype %d", d->dtype);
   DLM_REQUIRE(d->hq > 0 && d->hkv > 0 && d->block > 0 && d->cap > 0, DLM_ERR_ARG, "non-positive size");
+  DLM_REQUIRE(d->cap % 32 == 0, DLM_ERR_SHAPE, "cap must be a multiple of 32 (blocked V cache)");
   DLM_REQUIRE(d->hq % d->hkv == 0, DLM_ERR_SHAPE, "hq %% hkv != 0");
   DLM_REQUIRE(d->head_dim == 64 || d->head_dim == 128, DLM_ERR_SHAPE, "head_dim must be 64 or 128");
   DLM_REQUIRE(d->block <= 32, DLM_ERR_SHAPE, "block must be <= 32");
@@ -548,6 +549,7 @@ static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) 
 static int check_kv(const dlm_model* m, const dlm_kv* kv) {
   DLM_REQUIRE(m, DLM_ERR_ARG, "model is null");
   DLM_REQUIRE(kv && kv->k && kv->v && kv->len_dev, DLM_ERR_ARG, "kv is null");
+  DLM_REQUIRE(kv->cap % 32 == 0, DLM_ERR_SHAPE, "cap must be a multiple of 32 (blocked V cache)");
   DLM_REQUIRE(kv->cap > 0 && kv->max_len >= m->d.block && kv->max_len <= kv->cap, DLM_ERR_SHAPE,
               "kv: need block <= max_len <= cap");
   for (int l = 0; l < m->d.n_layers; ++l)

@@ -2,8 +2,9 @@
 // with no mask (a denoising round predicts the block's unresolved positions together,
 // page "ORL: diffusion LLMs get a learnable 'tokens per forward'", section "What shipped").
 //
-// The V cache is stored transposed, [kv head, D, cap], so that 8 consecutive keys of one value
-// column are one 16-byte load.
+// The V cache is stored transposed in 32-key blocks, [kv head][cap/32][D][32], so that 8
+// consecutive keys of one value column are one 16-byte load and a 32-key tile of V^T is one
+// contiguous run.
 //
 // bf16 path.  One workgroup per (query head, key split).  Its 4 waves take every 4th 32-key
 // tile of the split and run independently, with no LDS in the loop: K and V^T come straight
@@ -19,18 +20,26 @@
 // splits in index order.  Deterministic throughout.
 #include "attn.h"
 
+#include <algorithm>
+
 namespace dlm {
 
 namespace {
 
+// Optional per-workgroup timestamps for kernel studies (compiled out unless defined).
+#ifndef DLM_TRACE_POINT
+#define DLM_TRACE_POINT(i)
+#endif
+
 constexpr int TK = 32;          // keys per tile
+constexpr int kMaxSplits = 32;  // key splits per kv head
 
 struct AttnP {
   const uint16_t* q;            // [B, hq, D]
   const uint16_t* k;            // [hkv, cap, D]
-  const uint16_t* v;            // V^T cache [hkv, D, cap]
+  const uint16_t* v;            // V cache, [hkv][cap/32][D][32] (vt_index)
   uint16_t* out;                // [B, hq, D]
-  float* part_o;                // [hkv][ns][G][32][D]
+  uint16_t* part_o;             // [hkv][ns][G][32][D] bf16: each split's normalised output
   float* part_ml;               // [hkv][ns][G][32][2]
   int hq, hkv, B, cap, chunk, nsplit_max, out_packed;
   float scale_log2;             // softmax scale * log2(e)
@@ -39,38 +48,95 @@ struct AttnP {
   const int32_t* cont_dev;
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
+// Keys per split for N keys over at most nsplit_max splits: the smallest multiple of one
+// pass (PT tiles of 32 keys) that needs no more splits, so short prefixes use few splits and
+// long ones spread over all of them.
+constexpr int PT = 2;           // tiles per pass
+__device__ inline int split_chunk(int N, int nsplit_max) {
+  const int unit = PT * TK;
+  return ((N + nsplit_max * unit - 1) / (nsplit_max * unit)) * unit;
+}
+
+// One workgroup per (kv head, group of WPG query heads, key split); wave w serves query head
+// WPG hg + w of the group.  The split is processed in passes of PT 32-key tiles: the tiles'
+// K and V^T are loaded once per workgroup (non-temporal buffer loads into registers, then LDS,
+// double-buffered, the next pass in flight while this one is computed) and shared by the
+// waves.  Per pass each wave forms the scores of all PT tiles (independent MFMA chains), takes
+// one online-softmax step over the pass and adds P V.
+template <int D, int WPG>
+__global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
+  DLM_TRACE_POINT(0);
   if (p.cont_dev && *p.cont_dev == 0) return;
   constexpr int DS = D / 32;    // d-steps of the score MFMA
   constexpr int DB = D / 16;    // dv blocks of the output
-  __shared__ float red_o[4][D][33];
-  __shared__ float wm[4][32], wl[4][32];
+  constexpr int NT = 64 * WPG;
+  // LDS tile: K rows of 2D bytes padded by 16 (the rows a lane group reads land on distinct
+  // banks), V^T rows of 32 keys (64 bytes) padded by 16
+  constexpr int KROW = 2 * D + 16, VROW = 64 + 16;
+  constexpr int KBYTES = TK * KROW, VBYTES = D * VROW, TBYTES = KBYTES + VBYTES;
+  constexpr int KC = TK * D / 8 / NT, VC = D * 4 / NT;     // 16-byte chunks per thread and tile
+  static_assert(KC >= 1 && VC >= 1 && KC * NT == TK * D / 8 && VC * NT == D * 4, "tile split");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][PT][TBYTES];
   const int L = p.len_dev ? *p.len_dev : p.len_host;
   const int N = min(L + p.B, p.cap);
-  const int nsplit = min((N + p.chunk - 1) / p.chunk, p.nsplit_max);
+  const int chunk = split_chunk(N, p.nsplit_max);
+  const int nsplit = (N + chunk - 1) / chunk;
   const int G = p.hq / p.hkv;
-  // workgroup -> (kv head g, split s, query head hh in the group); the G query heads of one
-  // (g, s) share an XCD (workgroup ids are dealt round-robin to the 8 XCDs)
-  int g, s, hh;
-  {
-    const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
-    hh = j % G;
-    const int u = (j / G) * 8 + xcd;
-    g = u / p.nsplit_max;
-    s = u % p.nsplit_max;
-    if (g >= p.hkv) return;
-  }
+  const int HG = G / WPG;
+  const int s = blockIdx.x % p.nsplit_max, gh = blockIdx.x / p.nsplit_max;
+  const int g = gh / HG, hg = gh % HG;
   if (s >= nsplit) return;
-  const int head = g * G + hh;
+  DLM_TRACE_POINT(1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c0 = s * p.chunk, c1 = min(N, c0 + p.chunk);
-  // buffer descriptors: K rows past c1 read as zeros; V^T reads stay inside this head's
-  // [D][cap] block (the keys past c1 inside it are masked after the load)
+  const int hl = WPG * hg + w;                // query head within the kv head's group
+  const int head = g * G + hl;
+  const int c0 = s * chunk, c1 = min(N, c0 + chunk);
+  const int npass = (c1 - c0 + PT * TK - 1) / (PT * TK);
+  // buffer descriptors: K rows past c1 read as zeros; V^T tiles stay inside this head's
+  // [cap/32][D][32] block (a tile wholly past c1 is not loaded; keys past c1 inside a tile are
+  // masked after the LDS read)
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + (size_t)g * p.cap * D, (uint32_t)c1 * D * 2u);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + (size_t)g * D * p.cap, (uint32_t)D * p.cap * 2u);
   const int lg = lane >> 4;                                // lane group: keys 8lg .. 8lg+7
+
+  // global -> register staging of one pass (PT tiles; KC + VC 16-byte chunks per thread each)
+  u32x4_t stk[PT][KC], stv[PT][VC];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int tu = t0 + u * TK;
+      const bool in = tu < c1;
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int c = tid + NT * j, key = c / (D / 8), col = c % (D / 8);
+        stk[u][j] = bload16_nt(kr, in ? (uint32_t)((tu + key) * D * 2 + col * 16) : 0x80000000u);
+      }
+#pragma unroll
+      for (int j = 0; j < VC; ++j) {
+        const int c = tid + NT * j, dv = c >> 2, part = c & 3;
+        stv[u][j] = bload16_nt(vr, in ? (uint32_t)((((tu >> 5) * D + dv) * 32) * 2 + part * 16) : 0x80000000u);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      uint8_t* sk = smem[buf][u];
+      uint8_t* sv = smem[buf][u] + KBYTES;
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const int c = tid + NT * j, key = c / (D / 8), col = c % (D / 8);
+        *(u32x4_t*)(sk + key * KROW + col * 16) = stk[u][j];
+      }
+#pragma unroll
+      for (int j = 0; j < VC; ++j) {
+        const int c = tid + NT * j, dv = c >> 2, part = c & 3;
+        *(u32x4_t*)(sv + dv * VROW + part * 16) = stv[u][j];
+      }
+    }
+  };
+  fetch(c0);
 
   // Q fragments (B operand): lane l: query 16qb + l%16, d = 32ds + 8(l/16) .. +8
   u32x4_t qf[2][DS];
@@ -87,77 +153,74 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
   for (int b = 0; b < DB; ++b) o[b][0] = o[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
 
-  // K rows for score block kb: MFMA row i (= lane % 16) takes key 8(i/4) + 4kb + i%4, so the
-  // result rows 4(l/16) + r of block kb are keys 8(l/16) + 4kb + r.  V^T fragments (A operand
-  // of O^T = V^T P^T): lane l: column dv = 16b + l%16, keys 8lg .. +8.  The next tile of this
-  // wave is loaded while the current one is computed (buffer loads: past the ends they read
-  // zeros or in-bounds data that is masked).
-  u32x4_t kf[2][DS], vf[DB];
-  auto load_tile = [&](int t0, u32x4_t (&kt)[2][DS], u32x4_t (&vt)[DB]) {
+  stash(0);
+  if (npass > 1) fetch(c0 + PT * TK);
+  __syncthreads();
+  for (int ip = 0; ip < npass; ++ip) {
+    const int p0 = c0 + ip * PT * TK;
+    // scores of every tile of the pass.  K rows for score block kb: MFMA row i (= lane % 16)
+    // takes key 8(i/4) + 4kb + i%4, so the result rows 4(l/16) + r of block kb are keys
+    // 8(l/16) + 4kb + r; lane l ends up holding query 16qb + l%16.
+    f32x4_t sc[PT][2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int i = lane & 15;
-      const int key = t0 + 8 * (i >> 2) + 4 * kb + (i & 3);
+    for (int u = 0; u < PT; ++u) {
+      const uint8_t* sk = smem[ip & 1][u];
+      u32x4_t kc[2][DS];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kt[kb][ds] = bload16(kr, (uint32_t)(key * D + 32 * ds + 8 * (lane >> 4)) * 2u);
-    }
+      for (int kb = 0; kb < 2; ++kb) {
+        const int i = lane & 15;
+        const int key = 8 * (i >> 2) + 4 * kb + (i & 3);
 #pragma unroll
-    for (int b = 0; b < DB; ++b) vt[b] = bload16(vr, (uint32_t)((16 * b + (lane & 15)) * p.cap + t0 + 8 * lg) * 2u);
-  };
-  load_tile(c0 + w * TK, kf, vf);
-  for (int t0 = c0 + w * TK; t0 < c1; t0 += 4 * TK) {
-    u32x4_t kn[2][DS], vn[DB];
-    load_tile(t0 + 4 * TK, kn, vn);
-    // keys kv0 .. kv0+7 past c1 are zeroed (their probabilities are zero too, but stale cache
-    // contents could be non-finite): a per-lane mask of the valid 16-bit halves
-    const int kv0 = t0 + 8 * lg;
-    const int nvalid = min(8, max(0, c1 - kv0));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t msk = (2 * j < nvalid ? 0x0000ffffu : 0u) | (2 * j + 1 < nvalid ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int b = 0; b < DB; ++b) vf[b][j] &= msk;
-    }
-    // scores S^T[kb][qb]: lane l holds keys 8(l/16) + 4kb + r for query 16qb + l%16
-    f32x4_t sc[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) a = mfma16x16x32(kf[kb][ds], qf[qb][ds], a);
-        sc[kb][qb] = a;
+        for (int ds = 0; ds < DS; ++ds) kc[kb][ds] = *(const u32x4_t*)(sk + key * KROW + (32 * ds + 8 * lg) * 2);
       }
-    // online softmax per query (lane-resident), in log2 units
-    u32x4_t pf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds) a = mfma16x16x32(kc[kb][ds], qf[qb][ds], a);
+          sc[u][kb][qb] = a;
+        }
+    }
+    // one online-softmax step over the pass, per query (lane-resident), in log2 units
+    u32x4_t pf[PT][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int u = 0; u < PT; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = t0 + 8 * lg + 4 * kb + r;
-          float v = sc[kb][qb][r] * p.scale_log2;
-          v = key < c1 ? v : -INFINITY;
-          sc[kb][qb][r] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = p0 + u * TK + 8 * lg + 4 * kb + r;
+            float v = sc[u][kb][qb][r] * p.scale_log2;
+            v = key < c1 ? v : -INFINITY;
+            sc[u][kb][qb][r] = v;
+            mx = fmaxf(mx, v);
+          }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mnew = fmaxf(mrow[qb], mx);
-      const float alpha = exp2f(mrow[qb] - mnew);
-      float pv[8];
+      const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - mnew);
       float sum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int u = 0; u < PT; ++u) {
+        float pv[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = exp2f(sc[kb][qb][r] - mnew);
-          pv[4 * kb + r] = e;     // k-slot 4kb + r of lane group lg is key 8lg + 4kb + r
-          sum += e;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = __builtin_amdgcn_exp2f(sc[u][kb][qb][r] - mnew);
+            pv[4 * kb + r] = e;     // k-slot 4kb + r of lane group lg is key 8lg + 4kb + r
+            sum += e;
+          }
+        u32x4_t pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = pack2bf(pv[2 * i], pv[2 * i + 1]);
+        pf[u][qb] = pk;
+      }
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
       lrow[qb] = lrow[qb] * alpha + sum;
@@ -166,98 +229,98 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnP p) {
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[b][qb][r] *= alpha;
-      u32x4_t pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = (uint32_t)f2bf(pv[2 * i]) | ((uint32_t)f2bf(pv[2 * i + 1]) << 16);
-      pf[qb] = pk;
     }
-    // O^T[b][qb] += V^T[16b.., keys] P^T[keys, q]
+    // O^T[b][qb] += V^T[16b.., keys] P^T[keys, q]; V^T fragments (A operand): lane l: column
+    // dv = 16b + l%16, keys 8lg .. +8 (keys past c1 zeroed: stale cache contents could be
+    // non-finite)
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int u = 0; u < PT; ++u) {
+      const uint8_t* sv = smem[ip & 1][u] + KBYTES;
+      const int nvalid = min(8, max(0, c1 - (p0 + u * TK + 8 * lg)));
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) o[b][qb] = mfma16x16x32(vf[b], pf[qb], o[b][qb]);
+      for (int b = 0; b < DB; ++b) {
+        u32x4_t vc = *(const u32x4_t*)(sv + (16 * b + (lane & 15)) * VROW + 16 * lg);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int jj = 0; jj < 4; ++jj)
+          vc[jj] &= (2 * jj < nvalid ? 0x0000ffffu : 0u) | (2 * jj + 1 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kf[kb][ds] = kn[kb][ds];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) vf[b] = vn[b];
-  }
-  // merge the 4 waves: common max per query, each wave's O rescaled to it and published in
-  // LDS, then every output summed over the waves in wave order
-  if (lane < 16) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      wm[w][16 * qb + lane] = mrow[qb];
-      wl[w][16 * qb + lane] = lrow[qb];
+        for (int qb = 0; qb < 2; ++qb) o[b][qb] = mfma16x16x32(vc, pf[u][qb], o[b][qb]);
+      }
     }
+    if (ip == 0) DLM_TRACE_POINT(2);
+    // the next pass's registers go to the other buffer (last read in the previous pass, which
+    // every wave has finished), then the pass after it is requested
+    if (ip + 1 < npass) {
+      stash((ip + 1) & 1);
+      if (ip + 2 < npass) fetch(p0 + 2 * PT * TK);
+    }
+    __syncthreads();
   }
-  __syncthreads();
+  DLM_TRACE_POINT(3);
+  // o[b][qb][r] = O^T[dv = 16b + 4(l/16) + r][query 16qb + l%16]
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = 16 * qb + (lane & 15);
-    const float M = fmaxf(fmaxf(wm[0][qi], wm[1][qi]), fmaxf(wm[2][qi], wm[3][qi]));
-    const float sw = mrow[qb] == -INFINITY ? 0.f : exp2f(mrow[qb] - M);
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[w][16 * b + 4 * (lane >> 4) + r][qi] = o[b][qb][r] * sw;
-  }
-  __syncthreads();
-  // thread -> (query, 8 consecutive value columns)
-  for (int e = tid; e < 32 * (D / 8); e += 256) {
-    const int qi = e % 32, dv0 = (e / 32) * 8;
     if (qi >= p.B) continue;
-    const float M = fmaxf(fmaxf(wm[0][qi], wm[1][qi]), fmaxf(wm[2][qi], wm[3][qi]));
-    float Ls = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) Ls += wm[ww][qi] == -INFINITY ? 0.f : wl[ww][qi] * exp2f(wm[ww][qi] - M);
-    float val[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      val[j] = ((red_o[0][dv0 + j][qi] + red_o[1][dv0 + j][qi]) + red_o[2][dv0 + j][qi]) + red_o[3][dv0 + j][qi];
+    const float inv = 1.0f / lrow[qb];
     if (nsplit == 1) {
-      const float inv = 1.0f / Ls;
-      u32x4_t pk;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pk[j] = (uint32_t)f2bf(val[2 * j] * inv) | ((uint32_t)f2bf(val[2 * j + 1] * inv) << 16);
-      const size_t oi = p.out_packed ? xpk_index(qi, head * D + dv0) : ((size_t)qi * p.hq + head) * D + dv0;
-      *(u32x4_t*)(p.out + oi) = pk;   // 8 consecutive columns are 16 contiguous bytes in both layouts
+      for (int b = 0; b < DB; ++b) {
+        const int dv = 16 * b + 4 * (lane >> 4);
+        u32x2_t pk;
+        pk[0] = pack2bf(o[b][qb][0] * inv, o[b][qb][1] * inv);
+        pk[1] = pack2bf(o[b][qb][2] * inv, o[b][qb][3] * inv);
+        // 4 consecutive columns are 8 contiguous bytes in both layouts
+        const size_t oi = p.out_packed ? xpk_index(qi, head * D + dv) : ((size_t)qi * p.hq + head) * D + dv;
+        *(u32x2_t*)(p.out + oi) = pk;
+      }
     } else {
-      const size_t row = (((size_t)g * p.nsplit_max + s) * G + hh) * 32 + qi;
+      // the split's normalised output (bf16) and its (max, sum)
+      const size_t row = (((size_t)g * p.nsplit_max + s) * G + hl) * 32 + qi;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p.part_o[row * D + dv0 + j] = val[j];
-      if (dv0 == 0) {
-        p.part_ml[row * 2 + 0] = M;
-        p.part_ml[row * 2 + 1] = Ls;
+      for (int b = 0; b < DB; ++b) {
+        u32x2_t pk;
+        pk[0] = pack2bf(o[b][qb][0] * inv, o[b][qb][1] * inv);
+        pk[1] = pack2bf(o[b][qb][2] * inv, o[b][qb][3] * inv);
+        *(u32x2_t*)(p.part_o + row * D + 16 * b + 4 * (lane >> 4)) = pk;
+      }
+      if ((lane >> 4) == 0) {
+        p.part_ml[row * 2 + 0] = mrow[qb];
+        p.part_ml[row * 2 + 1] = lrow[qb];
       }
     }
   }
+  DLM_TRACE_POINT(4);
 }
 
 // merge the splits of (head, query): one workgroup per (head, query), D threads; all partial
-// loads are issued before the arithmetic (at most 16 splits)
+// loads are issued before the arithmetic (at most kMaxSplits splits); splits added in index order
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   const int L = p.len_dev ? *p.len_dev : p.len_host;
   const int N = min(L + p.B, p.cap);
-  const int nsplit = min((N + p.chunk - 1) / p.chunk, p.nsplit_max);
+  const int chunk = split_chunk(N, p.nsplit_max);
+  const int nsplit = (N + chunk - 1) / chunk;
   if (nsplit <= 1) return;      // the attention kernel wrote the output itself
   const int head = blockIdx.x / p.B, qi = blockIdx.x % p.B;
   const int G = p.hq / p.hkv;
   const int g = head / G, hh = head % G;
   const int dv = threadIdx.x;
-  constexpr int MAXS = 16;
+  constexpr int MAXS = kMaxSplits;
+  // branch-free loads: split slots past nsplit use out-of-range buffer offsets (zeros)
+  const size_t nrow = (size_t)p.hkv * p.nsplit_max * G * 32;
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(p.part_ml, (uint32_t)(nrow * 8));
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.part_o, (uint32_t)(nrow * D * 2));
   float mv[MAXS], lv[MAXS], ov[MAXS];
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
     const size_t row = (((size_t)g * p.nsplit_max + s) * G + hh) * 32 + qi;
     const bool ok = s < nsplit;
-    mv[s] = ok ? p.part_ml[row * 2] : -INFINITY;
-    lv[s] = ok ? p.part_ml[row * 2 + 1] : 0.f;
-    ov[s] = ok ? p.part_o[row * D + dv] : 0.f;
+    const u32x2_t mlv = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(mr, ok ? (int)(row * 8) : (int)0x80000000, 0, 0));
+    mv[s] = ok ? __uint_as_float(mlv[0]) : -INFINITY;
+    lv[s] = __uint_as_float(mlv[1]);
+    ov[s] = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(orr, ok ? (int)((row * D + dv) * 2) : (int)0x80000000, 0, 0));
   }
   float M = -INFINITY;
 #pragma unroll
@@ -265,9 +328,9 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnP p) {
   float num = 0.f, den = 0.f;
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
-    const float f = mv[s] == -INFINITY ? 0.f : exp2f(mv[s] - M);
+    const float f = mv[s] == -INFINITY ? 0.f : lv[s] * exp2f(mv[s] - M);   // split weight
     num += f * ov[s];
-    den += f * lv[s];
+    den += f;
   }
   const size_t o = p.out_packed ? xpk_index(qi, head * D + dv) : ((size_t)qi * p.hq + head) * D + dv;
   p.out[o] = f2bf(num / den);
@@ -295,7 +358,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnF32P p) {
   const int g = head / (p.hq / p.hkv);
   const float* q = p.q + ((size_t)qi * p.hq + head) * p.D;
   const float* kb = p.k + (size_t)g * p.cap * p.D;
-  const float* vb = p.v + (size_t)g * p.D * p.cap;   // V^T: [D][cap]
+  const float* vb = p.v + (size_t)g * p.D * p.cap;   // this head's blocked V^T
   const int lane = threadIdx.x;
   float mx = -INFINITY;
   for (int j = lane; j < N; j += 64) {
@@ -312,7 +375,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnF32P p) {
     for (int t = 0; t < p.D; ++t) s = fmaf(q[t], kb[(size_t)j * p.D + t], s);
     const float e = expf(s * p.scale - mx);
     den += e;
-    for (int t = 0; t < p.D; ++t) acc[t] = fmaf(e, vb[(size_t)t * p.cap + j], acc[t]);
+    for (int t = 0; t < p.D; ++t) acc[t] = fmaf(e, vb[vt_index(0, p.D, p.cap, j, t)], acc[t]);
   }
   den = wave_sum(den);
   for (int t = 0; t < p.D; ++t) {
@@ -324,22 +387,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnF32P p) {
 }  // namespace
 
 AttnPlan attn_plan(int hq, int hkv, int D, int B, int max_len) {
-  (void)hq; (void)D; (void)B;
+  (void)hq; (void)hkv; (void)D;
   AttnPlan pl;
+  // the launch covers up to kMaxSplits splits of at least one pass; the kernels choose the
+  // split length from the prefix length they read at run time
   const int N = max_len + B;
-  // chunk: multiple of 32 keys, at least 256, at most 32 splits per kv head
-  // chunk: a multiple of 4 tiles of 32 keys (one tile per wave and round), at most 16 splits
-  int chunk = 128;
-  while ((N + chunk - 1) / chunk > 16) chunk += 128;
-  pl.chunk = chunk;
-  pl.nsplit_max = (N + chunk - 1) / chunk;
-  (void)hkv;
+  pl.chunk = PT * TK;
+  pl.nsplit_max = std::min(kMaxSplits, std::max(1, (N + PT * TK - 1) / (PT * TK)));
   return pl;
 }
 
 size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl) {
   const int G = hq / hkv;
-  const size_t po = (size_t)hkv * pl.nsplit_max * G * 32 * D * 4;
+  const size_t po = (size_t)hkv * pl.nsplit_max * G * 32 * D * 2;
   const size_t pm = (size_t)hkv * pl.nsplit_max * G * 32 * 2 * 4;
   return align_up(po, 256) + align_up(pm, 256);
 }
@@ -354,8 +414,8 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
   p.v = (const uint16_t*)v;
   p.out = (uint16_t*)out;
   const int G = hq / hkv;
-  const size_t po = (size_t)hkv * pl.nsplit_max * G * 32 * D * 4;
-  p.part_o = (float*)ws;
+  const size_t po = (size_t)hkv * pl.nsplit_max * G * 32 * D * 2;
+  p.part_o = (uint16_t*)ws;
   p.part_ml = (float*)((char*)ws + align_up(po, 256));
   p.hq = hq;
   p.hkv = hkv;
@@ -367,13 +427,20 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
   p.len_dev = len_dev;
   p.len_host = len_host;
   p.cont_dev = cont_dev;
-  const int units = hkv * pl.nsplit_max;
-  const int grid = ((units + 7) / 8) * 8 * G;
+  const int WPG = G < 4 ? G : 4;
+  if (G % WPG || (WPG != 1 && WPG != 2 && WPG != 4))
+    return fail(DLM_ERR_SHAPE, "attention: query heads per kv head must be 1, 2 or a multiple of 4");
+  const int grid = hkv * (G / WPG) * pl.nsplit_max;
+  auto launch = [&](auto kern, int threads) { hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, p); };
   if (D == 128) {
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(grid), dim3(256), 0, st, p);
+    if (WPG == 4) launch(attn_bf16_kernel<128, 4>, 256);
+    else if (WPG == 2) launch(attn_bf16_kernel<128, 2>, 128);
+    else launch(attn_bf16_kernel<128, 1>, 64);
     hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(hq * B), dim3(128), 0, st, p);
   } else {
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(grid), dim3(256), 0, st, p);
+    if (WPG == 4) launch(attn_bf16_kernel<64, 4>, 256);
+    else if (WPG == 2) launch(attn_bf16_kernel<64, 2>, 128);
+    else launch(attn_bf16_kernel<64, 1>, 64);
     hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(hq * B), dim3(64), 0, st, p);
   }
   return check_hip(hipGetLastError(), "attn_bf16 launch");

@@ -20,12 +20,13 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------- bf16 <-> f32
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// round-to-nearest-even; NaN stays NaN (quiet bit forced)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// round-to-nearest-even (the hardware conversion, v_cvt_pk_bf16_f32); NaN stays NaN
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values, a in the low half
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
@@ -108,6 +109,14 @@ __device__ __forceinline__ float wave_max(float v) {
 // run.  Element (m, k) of the 32-row block lives at this index.
 __host__ __device__ __forceinline__ size_t xpk_index(int m, int k) {
   return ((size_t)(k >> 4) * 64 + m + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
+}
+
+// ---------------------------------------------------------------- V cache layout
+// The V cache of a kv head is stored transposed in 32-key blocks: [cap / 32][D][32], so that
+// a 32-key tile of V^T (the A operand of the attention's P V product, keys contiguous) is one
+// contiguous D x 64-byte run.  Element (key t, column j) of kv head h:
+__host__ __device__ __forceinline__ size_t vt_index(int h, int D, int cap, int t, int j) {
+  return (((size_t)h * (cap >> 5) + (t >> 5)) * D + j) * 32 + (t & 31);
 }
 
 // ---------------------------------------------------------------- host side

@@ -19,6 +19,7 @@ enum EpiKind {
 struct PartialSrc {
   const float* base;   // nullptr: no partials
   int tiles, KT, NW, cmax;
+  size_t bytes;        // size of the partial area
   // alternatively (base == nullptr): per-row output slots, value (m, n) of slot j at
   // slots[(m * nslot + j) * d + n], added in slot order (routed experts)
   const float* slots;

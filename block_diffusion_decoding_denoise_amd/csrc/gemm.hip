@@ -123,12 +123,12 @@ __device__ inline void epi_qk_rope(const EpiParams& e, int m, int part, int head
   }
 }
 
-// the V cache is stored transposed, [kv head, D, cap]
+// the V cache is stored transposed in 32-key blocks (vt_index)
 __device__ inline void epi_v(const EpiParams& e, int m, int rel, float v) {
   const int L = prefix_len(e);
   if (L + m >= e.cap) return;
   const int head = rel / e.D, j = rel % e.D;
-  store_act(e.v_cache, ((size_t)head * e.D + j) * e.cap + (L + m), v, e.bf16_out);
+  store_act(e.v_cache, vt_index(head, e.D, e.cap, L + m, j), v, e.bf16_out);
 }
 
 __device__ inline void epi_swiglu(const EpiParams& e, int m, int j, float g, float u) {
@@ -441,6 +441,9 @@ PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws) {
   ps.KT = K / 16;
   ps.NW = plan.splits;
   ps.cmax = gemm_cmax(N, K, plan.splits);
+  ps.bytes = (size_t)ps.tiles * ps.cmax * 1024 * 4;
+  ps.slots = nullptr;
+  ps.nslot = 0;
   return ps;
 }
 

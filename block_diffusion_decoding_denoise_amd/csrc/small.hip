@@ -29,60 +29,78 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   float* x = p.x + (size_t)row * p.d;
-  // every load of the row is issued before any arithmetic (d <= 4096: <= 4 float4 per thread)
+  // every load of the row (x, gains, pending partial sums) is issued, unconditionally, before
+  // any arithmetic: addresses of columns past d are clamped to column 0 and their values
+  // ignored, and partial slots past a tile's contributor count use out-of-range buffer
+  // offsets, which read zeros (d <= 4096: <= 4 float4 per thread)
   constexpr int MAXV = 4, NPF = 6;
+  int cc[MAXV];
+  bool valid[MAXV];
   f32x4_t xv[MAXV];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int c = 4 * (tid + 256 * j);
-    xv[j] = c < p.d ? *(const f32x4_t*)(x + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    valid[j] = c < p.d;
+    cc[j] = valid[j] ? c : 0;
+    xv[j] = *(const f32x4_t*)(x + cc[j]);
+  }
+  u32x2_t gb[MAXV];
+  f32x4_t gf[MAXV];
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    if (p.bf16) gb[j] = *(const u32x2_t*)((const uint16_t*)p.g + cc[j]);
+    else gf[j] = *(const f32x4_t*)((const float*)p.g + cc[j]);
   }
   if (p.ps.base) {
     const long long T = (long long)p.ps.tiles * p.ps.KT;
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(p.ps.base, (uint32_t)p.ps.bytes);
     int cnt[MAXV];
-    const float* src[MAXV];
+    uint32_t off[MAXV];
     f32x4_t pv[MAXV][NPF];
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
-      const int c = 4 * (tid + 256 * j);
-      const int t = c >> 5;
-      cnt[j] = 0;
-      src[j] = p.ps.base;
-      if (c < p.d) {
-        const int fo = owner_unit((long long)t * p.ps.KT, T, p.ps.NW);
-        cnt[j] = owner_unit((long long)(t + 1) * p.ps.KT - 1, T, p.ps.NW) - fo + 1;
-        src[j] = p.ps.base + (size_t)t * p.ps.cmax * 1024 + row * 32 + (c & 31);
-      }
+      const int t = cc[j] >> 5;
+      const int fo = owner_unit((long long)t * p.ps.KT, T, p.ps.NW);
+      cnt[j] = valid[j] ? owner_unit((long long)(t + 1) * p.ps.KT - 1, T, p.ps.NW) - fo + 1 : 0;
+      off[j] = (uint32_t)((((size_t)t * p.ps.cmax) * 1024 + row * 32 + (cc[j] & 31)) * 4);
 #pragma unroll
       for (int i = 0; i < NPF; ++i)
-        pv[j][i] = i < cnt[j] ? *(const f32x4_t*)(src[j] + (size_t)i * 1024) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pv[j][i] = __builtin_bit_cast(f32x4_t, bload16(pr, i < cnt[j] ? off[j] + (uint32_t)i * 4096u : 0x80000000u));
     }
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
-      const int c = 4 * (tid + 256 * j);
-      if (c >= p.d) continue;
 #pragma unroll
-      for (int i = 0; i < NPF; ++i)
-        if (i < cnt[j]) xv[j] += pv[j][i];
-      for (int i = NPF; i < cnt[j]; ++i) xv[j] += *(const f32x4_t*)(src[j] + (size_t)i * 1024);
-      *(f32x4_t*)(x + c) = xv[j];
+      for (int i = 0; i < NPF; ++i) xv[j] += pv[j][i];      // slots past cnt read zeros
+      for (int i = NPF; i < cnt[j]; ++i)
+        xv[j] += __builtin_bit_cast(f32x4_t, bload16(pr, off[j] + (uint32_t)i * 4096u));
     }
+  } else if (p.ps.slots) {
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.ps.slots + (size_t)row * p.ps.nslot * p.d,
+                                                (uint32_t)(p.ps.nslot * p.d * 4));
+    constexpr int MAXSL = 10;
+    f32x4_t sv[MAXV][MAXSL];
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j)
+#pragma unroll
+      for (int i = 0; i < MAXSL; ++i)
+        sv[j][i] = __builtin_bit_cast(
+            f32x4_t, bload16(sr, valid[j] && i < p.ps.nslot ? (uint32_t)((i * p.d + cc[j]) * 4) : 0x80000000u));
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j)
+#pragma unroll
+      for (int i = 0; i < MAXSL; ++i) xv[j] += sv[j][i];
   }
-  if (!p.ps.base && p.ps.slots) {
-    const float* sl = p.ps.slots + (size_t)row * p.ps.nslot * p.d;
+  if (p.ps.base || p.ps.slots) {
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      const int c = 4 * (tid + 256 * j);
-      if (c >= p.d) continue;
-      for (int i = 0; i < p.ps.nslot; ++i) xv[j] += *(const f32x4_t*)(sl + (size_t)i * p.d + c);
-      *(f32x4_t*)(x + c) = xv[j];
-    }
+    for (int j = 0; j < MAXV; ++j)
+      if (valid[j]) *(f32x4_t*)(x + cc[j]) = xv[j];
   }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < MAXV; ++j)
+    if (valid[j])
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s = fmaf(xv[j][e], xv[j][e], s);
+      for (int e = 0; e < 4; ++e) s = fmaf(xv[j][e], xv[j][e], s);
   s = wave_sum(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
@@ -90,21 +108,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
   const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
-    const int c = 4 * (tid + 256 * j);
-    if (c >= p.d) continue;
+    if (!valid[j]) continue;
+    const int c = cc[j];
     if (p.bf16) {
-      const uint2 gw = *(const uint2*)((const uint16_t*)p.g + c);
-      const float g4[4] = {lo_bf(gw.x), hi_bf(gw.x), lo_bf(gw.y), hi_bf(gw.y)};
+      const float g4[4] = {lo_bf(gb[j][0]), hi_bf(gb[j][0]), lo_bf(gb[j][1]), hi_bf(gb[j][1])};
       uint2 ow;
-      ow.x = (uint32_t)f2bf(xv[j][0] * r * g4[0]) | ((uint32_t)f2bf(xv[j][1] * r * g4[1]) << 16);
-      ow.y = (uint32_t)f2bf(xv[j][2] * r * g4[2]) | ((uint32_t)f2bf(xv[j][3] * r * g4[3]) << 16);
+      ow.x = pack2bf(xv[j][0] * r * g4[0], xv[j][1] * r * g4[1]);
+      ow.y = pack2bf(xv[j][2] * r * g4[2], xv[j][3] * r * g4[3]);
       // 4 consecutive columns stay contiguous in the packed operand order
       *(uint2*)((uint16_t*)p.out + (p.packed ? xpk_index(row, c) : (size_t)row * p.d + c)) = ow;
     } else {
-      const f32x4_t g4 = *(const f32x4_t*)((const float*)p.g + c);
       f32x4_t o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = xv[j][e] * r * g4[e];
+      for (int e = 0; e < 4; ++e) o[e] = xv[j][e] * r * gf[j][e];
       *(f32x4_t*)((float*)p.out + (size_t)row * p.d + c) = o;
     }
   }

@@ -72,9 +72,11 @@ const char* dlm_last_error(void);
  *
  *   q        [B, hq, D]     query rows, RoPE already applied.
  *   k_cache  [hkv, cap, D]  keys; rows [0, L) are the prefix, [L, L+B) the block.
- *   v_cache  [hkv, D, cap]  values, stored transposed (column j of key position t at
- *                           v_cache[h][j][t]) so that consecutive keys of one value column
- *                           are contiguous; positions as for k_cache.
+ *   v_cache  [hkv, cap/32, D, 32]  values, stored transposed in blocks of 32 key positions:
+ *                           column j of key position t of kv head h is
+ *                           v_cache[h][t / 32][j][t % 32], so consecutive keys of one value
+ *                           column are contiguous and a 32-key block is one contiguous run;
+ *                           positions as for k_cache.  cap % 32 == 0.
  *   out      [B, hq, D]     o = softmax(scale * q k^T) v, same dtype as q.
  *   L is desc->prefix_len, or *desc->prefix_len_dev when that device pointer is non-null
  *   (so a captured graph can replay with a growing prefix).  Shapes: D in {64, 128},
@@ -270,7 +272,8 @@ int dlm_ffn_gate_up(const dlm_model* m, int layer, const void* x_packed, void* a
 
 /* ------------------------------------------------------------------------------------
  * KV cache.  k[l]: device base of layer l's keys [hkv, cap, D]; v[l]: its values stored
- * transposed, [hkv, D, cap] (model dtype).
+ * transposed in 32-position blocks, [hkv, cap/32, D, 32] (as for dlm_block_attn); model
+ * dtype; cap % 32 == 0.
  * len_dev: device int32 holding the committed prefix length L.
  * ------------------------------------------------------------------------------------ */
 typedef struct {

@@ -76,7 +76,7 @@ def test_tiny_fp32_fixed_k_and_determinism():
     n = len(prompt) + 64
     for l in range(s.n_layers):
         np.testing.assert_allclose(m.k[l][:, :n].cpu().numpy(), kv.k[l][:, :n], atol=2e-5, rtol=1e-4)
-        np.testing.assert_allclose(m.v[l].transpose(1, 2)[:, :n].cpu().numpy(), kv.v[l][:, :n], atol=2e-5, rtol=1e-4)
+        np.testing.assert_allclose(dlm.v_cache_to_natural(m.v[l])[:, :n].cpu().numpy(), kv.v[l][:, :n], atol=2e-5, rtol=1e-4)
 
 
 def _valid_commit(rule_args, maxprob, open_rows, chosen):
@@ -130,7 +130,7 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1):
             pe_prev = m.view("pe", (B, d), torch.float32).cpu().numpy().astype(np.float64)
             L = int(m.len_dev.item())
             kv = KVCache([t.float().cpu().numpy().astype(np.float64) for t in m.k],
-                         [t.transpose(1, 2).float().cpu().numpy().astype(np.float64) for t in m.v], L)
+                         [dlm.v_cache_to_natural(t).float().cpu().numpy().astype(np.float64) for t in m.v], L)
             m.decode_round(rule)
             torch.cuda.synchronize()
             if r % check_every == 0:
@@ -197,7 +197,7 @@ def test_prefill_matches_oracle_cache():
     oracle.prefill(om, kv, prompt, Prec("bf16"))
     for l in range(s.n_layers):
         gk = m.k[l][:, :96].float().cpu().numpy()
-        gv = m.v[l].transpose(1, 2)[:, :96].float().cpu().numpy()
+        gv = _dlm().v_cache_to_natural(m.v[l])[:, :96].float().cpu().numpy()
         # bf16 storage: at most a few units in the last place where a rounding boundary is crossed
         np.testing.assert_allclose(gk, kv.k[l][:, :96], atol=3e-2, rtol=2e-2)
         np.testing.assert_allclose(gv, kv.v[l][:, :96], atol=3e-2, rtol=2e-2)

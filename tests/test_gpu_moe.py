@@ -53,7 +53,7 @@ def _round0_residual(shape, seed, prompt_len):
     torch.cuda.synchronize()
     L = int(m.len_dev.item())
     kv = KVCache([t.float().cpu().numpy().astype(np.float64) for t in m.k],
-                 [t.transpose(1, 2).float().cpu().numpy().astype(np.float64) for t in m.v], L)
+                 [dlm.v_cache_to_natural(t).float().cpu().numpy().astype(np.float64) for t in m.v], L)
     m.decode_round(dlm.CommitRule.fixed_k(4))
     torch.cuda.synchronize()
     gx = m.view("x", (shape.block, shape.d), torch.float32).cpu().numpy()
@@ -85,7 +85,7 @@ def test_moe_stages_one_layer():
     torch.cuda.synchronize()
     L = int(m.len_dev.item())
     kv = KVCache([t.float().cpu().numpy().astype(np.float64) for t in m.k],
-                 [t.transpose(1, 2).float().cpu().numpy().astype(np.float64) for t in m.v], L)
+                 [dlm.v_cache_to_natural(t).float().cpu().numpy().astype(np.float64) for t in m.v], L)
     m.decode_round(dlm.CommitRule.fixed_k(4))
     torch.cuda.synchronize()
     B, d, E, NS, F = s.block, s.d, s.n_experts, s.top_k + s.n_shared, s.expert_ffn

@@ -78,7 +78,8 @@ def _attn_case(dtype, hq, hkv, D, B, L, cap, seed):
     q = synth.stored_normal(seed, "attn.q", (B, hq, D), 1.0, dtype)
     k = synth.stored_normal(seed, "attn.k", (hkv, cap, D), 1.0, dtype)
     v = synth.stored_normal(seed, "attn.v", (hkv, cap, D), 1.0, dtype)
-    vt = np.ascontiguousarray(np.swapaxes(v, 1, 2))       # the library's V cache is [hkv, D, cap]
+    # the library's V cache is transposed in 32-position blocks, [hkv, cap/32, D, 32]
+    vt = np.ascontiguousarray(v.reshape(hkv, cap // 32, 32, D).transpose(0, 1, 3, 2))
     out = dlm.block_attn(storage(q, dtype), storage(k, dtype), storage(vt, dtype), L)
     torch.cuda.synchronize()
     qf, kf, vf = (oracle.decode_storage(a) for a in (q, k, v))
@@ -99,7 +100,7 @@ def test_attn_bf16_small(L):
 @pytest.mark.parametrize("L,B,hq,hkv,D", [(0, 1, 4, 2, 64), (17, 7, 8, 8, 128), (1000, 32, 16, 4, 128),
                                           (64, 32, 4, 1, 64)])
 def test_attn_bf16_shapes(L, B, hq, hkv, D):
-    _attn_case("bf16", hq, hkv, D, B, L, L + B + 5, 1236)
+    _attn_case("bf16", hq, hkv, D, B, L, (L + B + 5 + 31) // 32 * 32, 1236)
 
 
 @pytest.mark.parametrize("L", [0, 64, 150])
