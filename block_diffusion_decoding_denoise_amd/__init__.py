@@ -123,6 +123,7 @@ def lib():
         "dlm_pack_model": (i, [P(ModelDesc), vp, P(LayerWeights), vp, vp, sz, vp]),
         "dlm_decode_ws_bytes": (sz, [vp, P(KV)]),
         "dlm_decode_block": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, sz, vp]),
+        "dlm_decode_block_pipelined": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, vp, sz, vp]),
         "dlm_prefill": (i, [vp, vp, i, P(KV), vp, sz, vp]),
         "dlm_decode_views_get": (i, [vp, P(KV), vp, sz, P(DecodeViews)]),
         "dlm_decode_round": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, sz, vp]),
@@ -387,6 +388,17 @@ class Model:
                                       _ptr(state), _ptr(self.ws), self.ws.numel(), _stream()), "dlm_decode_block")
         return tokens
 
+    def decode_block_pipelined(self, rule: CommitRule, prev_tokens, tokens, state=None):
+        """Decode one block into `tokens`, first completing the pending commit pass of the
+        previous block (prev_tokens, or None); this block's commit pass is left pending
+        (dlm_decode_block_pipelined)."""
+        state = self.state if state is None else state
+        _check(lib().dlm_decode_block_pipelined(self.handle, ctypes.byref(rule), ctypes.byref(self.kv),
+                                                None if prev_tokens is None else _ptr(prev_tokens), _ptr(tokens),
+                                                _ptr(state), _ptr(self.ws), self.ws.numel(), _stream()),
+               "dlm_decode_block_pipelined")
+        return tokens
+
     def decode_begin(self):
         _check(lib().dlm_decode_begin(self.handle, ctypes.byref(self.kv), _ptr(self.tokens), _ptr(self.state),
                                       _ptr(self.ws), self.ws.numel(), _stream()), "dlm_decode_begin")
@@ -400,16 +412,30 @@ class Model:
         _check(lib().dlm_commit_pass(self.handle, ctypes.byref(self.kv), _ptr(tokens), _ptr(self.ws), self.ws.numel(),
                                      _stream()), "dlm_commit_pass")
 
-    def generate(self, prompt_ids, n_blocks, rule: CommitRule):
+    def generate(self, prompt_ids, n_blocks, rule: CommitRule, pipelined=False):
         """Prefill, then decode n_blocks blocks (one token readback per block).
-        Returns (token ids [n_blocks * B], list of per-block round states)."""
+        Returns (token ids [n_blocks * B], list of per-block round states).  pipelined: each
+        block's commit pass rides along with the next block's round 0 (the last one runs on
+        its own), with the same result."""
         self.set_len(0)
         self.prefill(prompt_ids)
         out, states = [], []
-        for _ in range(n_blocks):
-            self.decode_block(rule)
-            out.append(self.tokens.cpu())
+        if not pipelined:
+            for _ in range(n_blocks):
+                self.decode_block(rule)
+                out.append(self.tokens.cpu())
+                states.append(state_dict(self.state))
+            return torch.cat(out), states
+        bufs = [torch.zeros_like(self.tokens), torch.zeros_like(self.tokens)]
+        prev = None
+        for b in range(n_blocks):
+            cur = bufs[b % 2]
+            self.decode_block_pipelined(rule, prev, cur)
+            out.append(cur.cpu())
             states.append(state_dict(self.state))
+            prev = cur
+        if prev is not None:
+            self.commit_pass(prev)
         return torch.cat(out), states
 
 

@@ -102,7 +102,7 @@ extern "C" int dlm_block_attn(const dlm_attn_desc* d, const void* q, const void*
     return attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, d->hq, d->hkv, d->head_dim,
                     d->block, d->cap, d->softmax_scale, d->prefix_len_dev, d->prefix_len, nullptr, st);
   const int maxL = d->prefix_len_dev ? d->max_prefix_len : d->prefix_len;
-  return attn_bf16(q, k, v, out, d->hq, d->hkv, d->head_dim, d->block, d->cap, d->softmax_scale,
+  return attn_bf16(q, k, v, out, d->hq, d->hkv, d->head_dim, d->block, 1, d->cap, d->softmax_scale,
                    d->prefix_len_dev, d->prefix_len, nullptr,
                    attn_plan(d->hq, d->hkv, d->head_dim, d->block, maxL), ws, /*out_packed=*/0, st);
 }
@@ -268,7 +268,9 @@ extern "C" int dlm_pack_activations(const void* x, int rows, int k, void* x_pack
 
 // ------------------------------------------------------------------ model
 struct GraphKey {
-  std::tuple<int, float, int, int, int, const void*, const void*, const void*, const void*, const void*, const void*> t;
+  std::tuple<int, float, int, int, int, const void*, const void*, const void*, const void*, const void*, const void*,
+             int, const void*>
+      t;
   bool operator<(const GraphKey& o) const { return t < o.t; }
 };
 
@@ -504,20 +506,29 @@ static AttnPlan model_attn_plan(const dlm_model* m, const dlm_kv* kv) {
   return attn_plan(m->d.hq, m->d.hkv, m->d.head_dim, m->d.block, kv->max_len - m->d.block);
 }
 
+// A round fused with the previous block's commit pass runs 64 rows through the layers: the
+// dense bf16 models with 32-row blocks do so.
+static bool fusable(const dlm_model* m) {
+  return m->d.dtype == DLM_BF16 && !m->d.n_experts && m->d.block == 32;
+}
+
 static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) {
   const dlm_model_desc& d = m->d;
   const size_t el = d.dtype == DLM_BF16 ? 2 : 4;
-  const int B = 32;  // buffers always hold 32 rows (the GEMM B operand reads 32)
+  // buffers hold 32 rows (the GEMM B operand reads 32), the layer buffers 64 when a round can
+  // carry the previous block's commit rows
+  const int B = 32;
+  const int BL = fusable(m) ? 64 : 32;
   const int qd = d.hq * d.head_dim;
   const int F = d.n_experts ? d.expert_ffn : d.ffn;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return base + o; };
   DecodeWs w;
-  w.x = (float*)take((size_t)B * d.d * 4);
-  w.xn = take((size_t)B * d.d * el);
-  w.q = take((size_t)B * qd * el);
-  w.o = take((size_t)B * qd * el);
-  w.act = take((size_t)B * F * el);
+  w.x = (float*)take((size_t)BL * d.d * 4);
+  w.xn = take((size_t)BL * d.d * el);
+  w.q = take((size_t)BL * qd * el);
+  w.o = take((size_t)BL * qd * el);
+  w.act = take((size_t)BL * F * el);
   w.xsc = take((size_t)B * d.d * el);
   w.hn = take((size_t)B * d.d * el);
   w.pe = (float*)take((size_t)B * d.d * 4);
@@ -530,16 +541,17 @@ static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) 
   if (d.dtype == DLM_BF16) {
     g = std::max(g, gemm_ws_bytes(d.d, d.d, m->pl_sc));
     g = std::max(g, gemm_ws_bytes(m->n_qkv, d.d, m->pl_qkv));
-    g = std::max(g, gemm_ws_bytes(d.d, qd, m->pl_o));
+    g = std::max(g, gemm_ws_bytes(d.d, qd, m->pl_o, BL));
     if (!d.n_experts) {
       g = std::max(g, gemm_ws_bytes(2 * d.ffn, d.d, m->pl_gu));
-      g = std::max(g, gemm_ws_bytes(d.d, d.ffn, m->pl_dn));
+      g = std::max(g, gemm_ws_bytes(d.d, d.ffn, m->pl_dn, BL));
     } else {
       g = std::max(g, gemm_ws_bytes(d.n_experts, d.d, m->pl_router));
     }
   }
   w.gemm_ws = take(g + 256);
-  w.attn_ws = take(d.dtype == DLM_BF16 ? attn_ws_bytes(d.hq, d.hkv, d.head_dim, model_attn_plan(m, kv)) : 256);
+  w.attn_ws = take(d.dtype == DLM_BF16 ? attn_ws_bytes(d.hq, d.hkv, d.head_dim, model_attn_plan(m, kv), BL / 32)
+                                       : 256);
   w.head_ws = take(head_ws_bytes(d.dtype, d.block, d.d, d.vocab));
   w.moe_ws = take(d.n_experts ? moe_ws_bytes(d) : 0);
   w.total = off;
@@ -585,16 +597,19 @@ extern "C" int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* 
 }
 
 // ------------------------------------------------------------------ the forward pass
-// Runs the block's residual stream x through every layer.  last_kv_only: the last layer
-// stops after its K/V are written (commit pass).
+// Runs the residual stream x through every layer.  last_kv_only: the last layer stops after
+// its K/V are written (commit pass).  nqb = 2 (bf16, block 32): x holds 64 rows, the previous
+// block's committed rows (positions L .. L + 31, whose K/V this pass appends) and then the
+// current block's rows (positions L + 32 ..), which also attend to the first 32.
 // The bf16 residual projections (attention output, FFN down) leave their sums as deferred
 // GEMM partials, which the next RMSNorm adds into the residual stream; *pending describes the
 // partials still to be added after the last layer (base == nullptr: none).
 static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& w, const int32_t* cont,
-                          bool last_kv_only, hipStream_t st, PartialSrc* pending) {
+                          bool last_kv_only, hipStream_t st, PartialSrc* pending, int nqb = 1) {
   const dlm_model_desc& d = m->d;
   const int bf = d.dtype == DLM_BF16;
-  const int B = d.block, D = d.head_dim, qd = d.hq * D;
+  const int D = d.head_dim, qd = d.hq * D;
+  const int B = nqb == 1 ? d.block : 64;   // rows through the GEMMs and norms
   const char* pk = (const char*)m->packed;
   int rc;
   PartialSrc ps{};
@@ -628,8 +643,8 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     if (rc) return rc;
     if (last && last_kv_only) break;
     const float scale = 1.0f / sqrtf((float)D);
-    if (bf) rc = attn_bf16(w.q, kv->k[l], kv->v[l], w.o, d.hq, d.hkv, D, B, kv->cap, scale, kv->len_dev, 0, cont,
-                           model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st);
+    if (bf) rc = attn_bf16(w.q, kv->k[l], kv->v[l], w.o, d.hq, d.hkv, D, d.block, nqb, kv->cap, scale, kv->len_dev,
+                           0, cont, model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st);
     else rc = attn_f32((const float*)w.q, (const float*)kv->k[l], (const float*)kv->v[l], (float*)w.o, d.hq, d.hkv,
                        D, B, kv->cap, scale, kv->len_dev, 0, cont, st);
     if (rc) return rc;
@@ -642,7 +657,7 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     e.cont_dev = cont;
     if (bf) {
       rc = gemm_bf16(pk + m->off_o[l], w.o, d.d, qd, MAP_IDENTITY, e, m->pl_o, w.gemm_ws, st);
-      if (!m->pl_o.R) ps = gemm_partials(d.d, qd, m->pl_o, w.gemm_ws);
+      if (!m->pl_o.R) ps = gemm_partials(d.d, qd, m->pl_o, w.gemm_ws, B);
     } else {
       F32Mats W{};
       W.w[0] = (const float*)L.wo; W.rows[0] = d.d;
@@ -682,7 +697,7 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     e.cont_dev = cont;
     if (bf) {
       rc = gemm_bf16(pk + m->off_dn[l], w.act, d.d, d.ffn, MAP_IDENTITY, e, m->pl_dn, w.gemm_ws, st);
-      if (!m->pl_dn.R) ps = gemm_partials(d.d, d.ffn, m->pl_dn, w.gemm_ws);
+      if (!m->pl_dn.R) ps = gemm_partials(d.d, d.ffn, m->pl_dn, w.gemm_ws, B);
     } else {
       F32Mats W{};
       W.w[0] = (const float*)L.wd; W.rows[0] = d.d;
@@ -746,6 +761,46 @@ static int enqueue_commit_pass(const dlm_model* m, const dlm_kv* kv, const int32
   return len_add(kv->len_dev, d.block, st);
 }
 
+// Round 0 of a block fused with the commit pass of the previous block (prev_tokens, whose K/V
+// are not yet in the cache): one 64-row pass whose first 32 rows are the previous block's
+// committed tokens at positions L .. L + 31 and whose last 32 rows are round 0 of this block
+// at L + 32 .., which attend to the prefix, to the previous block and to each other.  Every
+// row computes what the separate commit pass and round would; the weights stream once.
+static int enqueue_fused_round0(const dlm_model* m, const dlm_commit_rule& rule, const dlm_kv* kv,
+                                const int32_t* prev_tokens, int32_t* tokens, dlm_round_state* state,
+                                const DecodeWs& w, hipStream_t st) {
+  const dlm_model_desc& d = m->d;
+  const int B = d.block;
+  const int32_t* cont = rule.mode == DLM_COMMIT_FIXED_K ? nullptr : &state->cont;
+  int rc;
+  float* x_round = w.x + (size_t)B * d.d;
+  if ((rc = embed(prev_tokens, m->emb, w.x, B, d.d, d.vocab, 1, st))) return rc;
+  if ((rc = selfcond_prep(w.pe, w.committed, w.xsc, B, d.d, 1, nullptr, st))) return rc;
+  EpiParams e = epi_zero();
+  e.kind = EPI_SELFCOND;
+  e.M = B;
+  e.bf16_out = 1;
+  e.out = x_round;
+  e.ld_out = d.d;
+  e.mask_emb = m->mask_emb;
+  e.emb = m->emb;
+  e.tokens = tokens;
+  e.committed = w.committed;
+  e.vocab = d.vocab;
+  if ((rc = gemm_bf16((const char*)m->packed + m->off_sc, w.xsc, d.d, d.d, MAP_IDENTITY, e, m->pl_sc, w.gemm_ws,
+                      st)))
+    return rc;
+  PartialSrc ps{};
+  if ((rc = enqueue_layers(m, kv, w, nullptr, false, st, &ps, /*nqb=*/2))) return rc;
+  ps.row0 = B;   // the final norm serves the round's rows only
+  if ((rc = rmsnorm(x_round, m->final_norm, w.hn, B, d.d, 1, 0, d.eps, nullptr, st, &ps))) return rc;
+  if ((rc = len_add(kv->len_dev, B, st))) return rc;   // the previous block is now in the cache
+  if ((rc = head_launch(d.dtype, w.hn, m->emb, w.committed, B, d.d, d.vocab, w.lse, w.ent, w.maxp, w.amax, w.pe,
+                        nullptr, w.head_ws, cont, st)))
+    return rc;
+  return commit_launch(rule, B, w.maxp, w.amax, w.lse, w.ent, w.committed, tokens, state, st);
+}
+
 static int n_rounds(const dlm_model* m, const dlm_commit_rule& r) {
   if (r.mode == DLM_COMMIT_FIXED_K) {
     const int n = (m->d.block + r.k - 1) / r.k;
@@ -762,6 +817,27 @@ static int enqueue_block(const dlm_model* m, const dlm_commit_rule& rule, const 
   for (int r = 0; r < R; ++r)
     if ((rc = enqueue_round(m, rule, kv, tokens, state, w, st))) return rc;
   return enqueue_commit_pass(m, kv, tokens, w, st);
+}
+
+// A block whose own commit pass is left to the next block (or to dlm_commit_pass): the
+// previous block's pending commit pass runs fused into round 0 when the model allows it, else
+// on its own before round 0.
+static int enqueue_block_pipelined(const dlm_model* m, const dlm_commit_rule& rule, const dlm_kv* kv,
+                                   const int32_t* prev_tokens, int32_t* tokens, dlm_round_state* state,
+                                   const DecodeWs& w, hipStream_t st) {
+  int rc;
+  if ((rc = block_reset(m->d.block, w.committed, tokens, state, w.pe, 32 * m->d.d, st))) return rc;
+  const int R = n_rounds(m, rule);
+  int r = 0;
+  if (prev_tokens && fusable(m)) {
+    if ((rc = enqueue_fused_round0(m, rule, kv, prev_tokens, tokens, state, w, st))) return rc;
+    r = 1;
+  } else if (prev_tokens) {
+    if ((rc = enqueue_commit_pass(m, kv, prev_tokens, w, st))) return rc;
+  }
+  for (; r < R; ++r)
+    if ((rc = enqueue_round(m, rule, kv, tokens, state, w, st))) return rc;
+  return DLM_OK;
 }
 
 static int check_decode(const dlm_model* m, const dlm_kv* kv, void* ws, size_t ws_bytes) {
@@ -796,26 +872,24 @@ extern "C" int dlm_ffn_gate_up(const dlm_model* m, int layer, const void* x_pack
                    ws, (hipStream_t)stream);
 }
 
-extern "C" int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv, int32_t* tokens,
-                                dlm_round_state* state, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_decode(m, kv, ws, ws_bytes);
-  if (rc) return rc;
-  if ((rc = check_rule(rule))) return rc;
-  DLM_REQUIRE(tokens && state, DLM_ERR_ARG, "null pointer");
-  DLM_DEVICE_CHECK();
+// Captures (once per key) and launches the graph of one block.
+static int launch_block_graph(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                              const int32_t* prev_tokens, int pipelined, int32_t* tokens, dlm_round_state* state,
+                              void* ws, hipStream_t st) {
   dlm_model* mm = const_cast<dlm_model*>(m);
   DecodeWs w = decode_layout(m, kv, (char*)ws);
-  hipStream_t st = (hipStream_t)stream;
   GraphKey key;
   const void* kv0 = kv->k[0];
   key.t = std::make_tuple(rule->mode, rule->tau, rule->k, rule->forced_top1, rule->max_rounds, (const void*)tokens,
-                          (const void*)state, ws, kv0, (const void*)kv->len_dev, (const void*)kv->v[0]);
+                          (const void*)state, ws, kv0, (const void*)kv->len_dev, (const void*)kv->v[0], pipelined,
+                          (const void*)prev_tokens);
   std::lock_guard<std::mutex> lock(mm->mu);
   auto it = mm->graphs.find(key);
   if (it == mm->graphs.end()) {
     if (!mm->cap_stream) DLM_HIP(hipStreamCreateWithFlags(&mm->cap_stream, hipStreamNonBlocking));
     DLM_HIP(hipStreamBeginCapture(mm->cap_stream, hipStreamCaptureModeThreadLocal));
-    rc = enqueue_block(m, *rule, kv, tokens, state, w, mm->cap_stream);
+    int rc = pipelined ? enqueue_block_pipelined(m, *rule, kv, prev_tokens, tokens, state, w, mm->cap_stream)
+                       : enqueue_block(m, *rule, kv, tokens, state, w, mm->cap_stream);
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(mm->cap_stream, &g);
     if (rc) {
@@ -833,6 +907,28 @@ extern "C" int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule,
     it = mm->graphs.emplace(key, ex).first;
   }
   return check_hip(hipGraphLaunch(it->second, st), "hipGraphLaunch");
+}
+
+extern "C" int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv, int32_t* tokens,
+                                dlm_round_state* state, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_rule(rule))) return rc;
+  DLM_REQUIRE(tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_DEVICE_CHECK();
+  return launch_block_graph(m, rule, kv, nullptr, 0, tokens, state, ws, (hipStream_t)stream);
+}
+
+extern "C" int dlm_decode_block_pipelined(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                                          const int32_t* prev_tokens, int32_t* tokens, dlm_round_state* state,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_rule(rule))) return rc;
+  DLM_REQUIRE(tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(prev_tokens != tokens, DLM_ERR_ARG, "prev_tokens and tokens must be distinct buffers");
+  DLM_DEVICE_CHECK();
+  return launch_block_graph(m, rule, kv, prev_tokens, 1, tokens, state, ws, (hipStream_t)stream);
 }
 
 extern "C" int dlm_decode_begin(const dlm_model* m, const dlm_kv* kv, int32_t* tokens, dlm_round_state* state,

@@ -10,9 +10,11 @@ struct AttnPlan {
 };
 
 AttnPlan attn_plan(int hq, int hkv, int D, int B, int max_len);
-size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl);
+// nqb query blocks (1, or 2 of B = 32 rows: the second block also attends to the first's keys,
+// which sit at L .. L + 31; see attn.hip)
+size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl, int nqb = 1);
 int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, int hkv, int D,
-              int B, int cap, float scale, const int32_t* len_dev, int len_host,
+              int B, int nqb, int cap, float scale, const int32_t* len_dev, int len_host,
               const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st);
 int attn_f32(const float* q, const float* k, const float* v, float* out, int hq, int hkv, int D,
              int B, int cap, float scale, const int32_t* len_dev, int len_host,

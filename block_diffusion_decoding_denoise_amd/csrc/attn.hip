@@ -34,14 +34,17 @@ namespace {
 constexpr int TK = 32;          // keys per tile
 constexpr int kMaxSplits = 32;  // key splits per kv head
 
+// Query block j (of nqb; j > 0 only with B = 32) holds rows 32 j .. 32 j + B - 1 of q and out,
+// sits at positions L + 32 j .. and attends to keys [0, L + 32 j + B): with two blocks, the
+// first is a committed block whose keys the second one also sees.
 struct AttnP {
-  const uint16_t* q;            // [B, hq, D]
+  const uint16_t* q;            // [nqb 32, hq, D]
   const uint16_t* k;            // [hkv, cap, D]
   const uint16_t* v;            // V cache, [hkv][cap/32][D][32] (vt_index)
-  uint16_t* out;                // [B, hq, D]
-  uint16_t* part_o;             // [hkv][ns][G][32][D] bf16: each split's normalised output
-  float* part_ml;               // [hkv][ns][G][32][2]
-  int hq, hkv, B, cap, chunk, nsplit_max, out_packed;
+  uint16_t* out;                // [nqb 32, hq, D] (or packed, 32-row panels)
+  uint16_t* part_o;             // [nqb][hkv][ns][G][32][D] bf16: each split's normalised output
+  float* part_ml;               // [nqb][hkv][ns][G][32][2]
+  int hq, hkv, B, nqb, cap, chunk, nsplit_max, out_packed;
   float scale_log2;             // softmax scale * log2(e)
   const int32_t* len_dev;
   int len_host;
@@ -77,13 +80,15 @@ __global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
   constexpr int KC = TK * D / 8 / NT, VC = D * 4 / NT;     // 16-byte chunks per thread and tile
   static_assert(KC >= 1 && VC >= 1 && KC * NT == TK * D / 8 && VC * NT == D * 4, "tile split");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][PT][TBYTES];
-  const int L = p.len_dev ? *p.len_dev : p.len_host;
+  const int G = p.hq / p.hkv;
+  const int HG = G / WPG;
+  const int per_qb = p.hkv * HG * p.nsplit_max;
+  const int qblk = blockIdx.x / per_qb, bx = blockIdx.x % per_qb;
+  const int L = (p.len_dev ? *p.len_dev : p.len_host) + 32 * qblk;
   const int N = min(L + p.B, p.cap);
   const int chunk = split_chunk(N, p.nsplit_max);
   const int nsplit = (N + chunk - 1) / chunk;
-  const int G = p.hq / p.hkv;
-  const int HG = G / WPG;
-  const int s = blockIdx.x % p.nsplit_max, gh = blockIdx.x / p.nsplit_max;
+  const int s = bx % p.nsplit_max, gh = bx / p.nsplit_max;
   const int g = gh / HG, hg = gh % HG;
   if (s >= nsplit) return;
   DLM_TRACE_POINT(1);
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
     const int qi = 16 * qb + (lane & 15);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
-      qf[qb][ds] = qi < p.B ? ld16(p.q + ((size_t)qi * p.hq + head) * D + 32 * ds + 8 * (lane >> 4))
+      qf[qb][ds] = qi < p.B ? ld16(p.q + ((size_t)(32 * qblk + qi) * p.hq + head) * D + 32 * ds + 8 * (lane >> 4))
                             : u32x4_t{0u, 0u, 0u, 0u};
   }
   f32x4_t o[DB][2];
@@ -271,12 +276,13 @@ __global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
         pk[0] = pack2bf(o[b][qb][0] * inv, o[b][qb][1] * inv);
         pk[1] = pack2bf(o[b][qb][2] * inv, o[b][qb][3] * inv);
         // 4 consecutive columns are 8 contiguous bytes in both layouts
-        const size_t oi = p.out_packed ? xpk_index(qi, head * D + dv) : ((size_t)qi * p.hq + head) * D + dv;
+        const int qr = 32 * qblk + qi;
+        const size_t oi = p.out_packed ? xpk_index_m(qr, head * D + dv, p.hq * D) : ((size_t)qr * p.hq + head) * D + dv;
         *(u32x2_t*)(p.out + oi) = pk;
       }
     } else {
       // the split's normalised output (bf16) and its (max, sum)
-      const size_t row = (((size_t)g * p.nsplit_max + s) * G + hl) * 32 + qi;
+      const size_t row = ((((size_t)qblk * p.hkv + g) * p.nsplit_max + s) * G + hl) * 32 + qi;
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
         u32x2_t pk;
@@ -293,29 +299,31 @@ __global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
   DLM_TRACE_POINT(4);
 }
 
-// merge the splits of (head, query): one workgroup per (head, query), D threads; all partial
-// loads are issued before the arithmetic (at most kMaxSplits splits); splits added in index order
+// merge the splits of (head, query): one workgroup per (query block, head, query), D threads;
+// all partial loads are issued before the arithmetic (at most kMaxSplits splits); splits added
+// in index order
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
-  const int L = p.len_dev ? *p.len_dev : p.len_host;
+  const int qblk = blockIdx.x / (p.hq * p.B), bx = blockIdx.x % (p.hq * p.B);
+  const int L = (p.len_dev ? *p.len_dev : p.len_host) + 32 * qblk;
   const int N = min(L + p.B, p.cap);
   const int chunk = split_chunk(N, p.nsplit_max);
   const int nsplit = (N + chunk - 1) / chunk;
   if (nsplit <= 1) return;      // the attention kernel wrote the output itself
-  const int head = blockIdx.x / p.B, qi = blockIdx.x % p.B;
+  const int head = bx / p.B, qi = bx % p.B;
   const int G = p.hq / p.hkv;
   const int g = head / G, hh = head % G;
   const int dv = threadIdx.x;
   constexpr int MAXS = kMaxSplits;
   // branch-free loads: split slots past nsplit use out-of-range buffer offsets (zeros)
-  const size_t nrow = (size_t)p.hkv * p.nsplit_max * G * 32;
+  const size_t nrow = (size_t)p.nqb * p.hkv * p.nsplit_max * G * 32;
   const __amdgpu_buffer_rsrc_t mr = make_rsrc(p.part_ml, (uint32_t)(nrow * 8));
   const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.part_o, (uint32_t)(nrow * D * 2));
   float mv[MAXS], lv[MAXS], ov[MAXS];
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
-    const size_t row = (((size_t)g * p.nsplit_max + s) * G + hh) * 32 + qi;
+    const size_t row = ((((size_t)qblk * p.hkv + g) * p.nsplit_max + s) * G + hh) * 32 + qi;
     const bool ok = s < nsplit;
     const u32x2_t mlv = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(mr, ok ? (int)(row * 8) : (int)0x80000000, 0, 0));
     mv[s] = ok ? __uint_as_float(mlv[0]) : -INFINITY;
@@ -332,7 +340,8 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnP p) {
     num += f * ov[s];
     den += f;
   }
-  const size_t o = p.out_packed ? xpk_index(qi, head * D + dv) : ((size_t)qi * p.hq + head) * D + dv;
+  const int qr = 32 * qblk + qi;
+  const size_t o = p.out_packed ? xpk_index_m(qr, head * D + dv, p.hq * D) : ((size_t)qr * p.hq + head) * D + dv;
   p.out[o] = f2bf(num / den);
 }
 
@@ -397,16 +406,18 @@ AttnPlan attn_plan(int hq, int hkv, int D, int B, int max_len) {
   return pl;
 }
 
-size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl) {
+size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl, int nqb) {
   const int G = hq / hkv;
-  const size_t po = (size_t)hkv * pl.nsplit_max * G * 32 * D * 2;
-  const size_t pm = (size_t)hkv * pl.nsplit_max * G * 32 * 2 * 4;
+  const size_t po = (size_t)nqb * hkv * pl.nsplit_max * G * 32 * D * 2;
+  const size_t pm = (size_t)nqb * hkv * pl.nsplit_max * G * 32 * 2 * 4;
   return align_up(po, 256) + align_up(pm, 256);
 }
 
 int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, int hkv, int D,
-              int B, int cap, float scale, const int32_t* len_dev, int len_host,
+              int B, int nqb, int cap, float scale, const int32_t* len_dev, int len_host,
               const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st) {
+  if (nqb < 1 || nqb > 2 || (nqb == 2 && B != 32))
+    return fail(DLM_ERR_SHAPE, "attention: one query block, or two of 32 rows");
   AttnP p;
   p.out_packed = out_packed;
   p.q = (const uint16_t*)q;
@@ -414,12 +425,13 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
   p.v = (const uint16_t*)v;
   p.out = (uint16_t*)out;
   const int G = hq / hkv;
-  const size_t po = (size_t)hkv * pl.nsplit_max * G * 32 * D * 2;
+  const size_t po = (size_t)nqb * hkv * pl.nsplit_max * G * 32 * D * 2;
   p.part_o = (uint16_t*)ws;
   p.part_ml = (float*)((char*)ws + align_up(po, 256));
   p.hq = hq;
   p.hkv = hkv;
   p.B = B;
+  p.nqb = nqb;
   p.cap = cap;
   p.chunk = pl.chunk;
   p.nsplit_max = pl.nsplit_max;
@@ -430,18 +442,18 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
   const int WPG = G < 4 ? G : 4;
   if (G % WPG || (WPG != 1 && WPG != 2 && WPG != 4))
     return fail(DLM_ERR_SHAPE, "attention: query heads per kv head must be 1, 2 or a multiple of 4");
-  const int grid = hkv * (G / WPG) * pl.nsplit_max;
+  const int grid = nqb * hkv * (G / WPG) * pl.nsplit_max;
   auto launch = [&](auto kern, int threads) { hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, p); };
   if (D == 128) {
     if (WPG == 4) launch(attn_bf16_kernel<128, 4>, 256);
     else if (WPG == 2) launch(attn_bf16_kernel<128, 2>, 128);
     else launch(attn_bf16_kernel<128, 1>, 64);
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(hq * B), dim3(128), 0, st, p);
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(nqb * hq * B), dim3(128), 0, st, p);
   } else {
     if (WPG == 4) launch(attn_bf16_kernel<64, 4>, 256);
     else if (WPG == 2) launch(attn_bf16_kernel<64, 2>, 128);
     else launch(attn_bf16_kernel<64, 1>, 64);
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(hq * B), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(nqb * hq * B), dim3(64), 0, st, p);
   }
   return check_hip(hipGetLastError(), "attn_bf16 launch");
 }

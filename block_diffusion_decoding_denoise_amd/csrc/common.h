@@ -110,6 +110,10 @@ __device__ __forceinline__ float wave_max(float v) {
 __host__ __device__ __forceinline__ size_t xpk_index(int m, int k) {
   return ((size_t)(k >> 4) * 64 + m + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
 }
+// More than 32 rows (K columns) are stored as consecutive 32-row panels of that order.
+__host__ __device__ __forceinline__ size_t xpk_index_m(int m, int k, int K) {
+  return (size_t)(m >> 5) * 32 * K + xpk_index(m & 31, k);
+}
 
 // ---------------------------------------------------------------- V cache layout
 // The V cache of a kv head is stored transposed in 32-key blocks: [cap / 32][D][32], so that

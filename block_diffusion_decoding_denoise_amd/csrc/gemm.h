@@ -1,4 +1,4 @@
-// Skinny GEMM (M = block rows <= 32) with fused epilogues -- internal interface.
+// Skinny GEMM (M <= 64 block rows) with fused epilogues -- internal interface.
 #pragma once
 #include "common.h"
 
@@ -15,10 +15,12 @@ enum EpiKind {
 
 // Where a deferred GEMM left its partial sums: tile t (32 output columns) has contributors
 // c = 0 .. cnt(t)-1, with cnt(t) from the stream-K split (see contributors()), and value
-// (m, n) of contributor c at base[(t * cmax + c) * 1024 + m * 32 + n % 32].
+// (m, n) of contributor c at base[(t * cmax + c) * mstride + m * 32 + n % 32], where
+// mstride = 32 x (the GEMM's row count rounded up to 32).  A consumer that works on rows
+// row0 .. of the GEMM's rows reads its row r as GEMM row row0 + r.
 struct PartialSrc {
   const float* base;   // nullptr: no partials
-  int tiles, KT, NW, cmax;
+  int tiles, KT, NW, cmax, mstride, row0;
   size_t bytes;        // size of the partial area
   // alternatively (base == nullptr): per-row output slots, value (m, n) of slot j at
   // slots[(m * nslot + j) * d + n], added in slot order (routed experts)
@@ -33,7 +35,8 @@ enum RowMapKind { MAP_IDENTITY = 0, MAP_QKV = 1, MAP_GU = 2 };
 
 struct EpiParams {
   int kind;
-  int M;                  // valid activation rows
+  int M;                  // valid activation rows (<= 64; more than 32 only for the row-owned
+                          // kinds and EPI_PARTIAL)
   int bf16_out;           // activations / caches are bf16 (else f32)
   // f32 outputs
   float* out;             // STORE_F32 / RESID / SELFCOND: [M, ld_out]
@@ -68,11 +71,13 @@ struct GemmPlan {
 // Packed-row -> logical-row map used when packing (host side).
 void build_row_map(int kind, int n_rows, int hq, int hkv, int D, int F, int32_t* out);
 
-// bf16 path.  W: packed [N, K] (N % 32 == 0, K % 16 == 0); X: bf16 32 x K in the packed
-// operand order (xpk_index; rows >= M are read but ignored).  The SwiGLU epilogue writes its
-// bf16 output in the same packed order (it feeds the down projection).
-// partial/counters: workspace (counters zero before the first use; left zero).
-size_t gemm_ws_bytes(int N, int K, GemmPlan plan);
+// bf16 path.  W: packed [N, K] (N % 32 == 0, K % 16 == 0); X: bf16, M <= 32 rows as one
+// 32 x K panel in the packed operand order (xpk_index; rows >= M are read but ignored), or
+// 32 < M <= 64 rows as two such panels (xpk_index_m).  The SwiGLU epilogue writes its bf16
+// output in the same packed order (it feeds the down projection).
+// partial/counters: workspace (counters zero before the first use; left zero); mrows: the
+// largest M the workspace serves.
+size_t gemm_ws_bytes(int N, int K, GemmPlan plan, int mrows = 32);
 GemmPlan gemm_plan(int N, int K);
 // Row-owned plan when N splits into equal even row blocks over enough workgroups (the weights
 // must then be packed with pack_bf16_owned and this plan's R), else the stream-K plan.
@@ -81,7 +86,7 @@ int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const Ep
               GemmPlan plan, void* ws, hipStream_t st);
 // Partial sums left in ws by a gemm_bf16 call with kind EPI_PARTIAL (valid until the next GEMM
 // on the same workspace).
-PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws);
+PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws, int M = 32);
 
 // f32 path (natural [out, in] weights).  Up to 3 source matrices make the logical rows.
 struct F32Mats {

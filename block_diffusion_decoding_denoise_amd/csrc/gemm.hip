@@ -1,6 +1,7 @@
 // Skinny GEMMs of the denoising round: C[m][n] = sum_k X[m][k] W[n][k] for the block's
-// M <= 32 rows, with the consumer of C fused into the epilogue (RoPE + KV-cache write,
-// SwiGLU, residual add, self-conditioning input).
+// M <= 32 rows (or 64: a round fused with the previous block's commit pass), with the consumer
+// of C fused into the epilogue (RoPE + KV-cache write, SwiGLU, residual add, self-conditioning
+// input).
 //
 // bf16 path (matrix cores).  W is packed once at model load: 32-row tile t, 16-column step
 // kt is one contiguous 1 KiB run in which lane l's 16 bytes are
@@ -10,8 +11,10 @@
 // [w T / NW, (w+1) T / NW) of the T = tiles x steps units, so every worker streams the same
 // number of bytes with 1 KiB loads and no tile-count tail.  Each wave keeps a ring of P
 // steps in flight (buffer loads, which return zeros past the range, so the ring runs without
-// branches); the block's activations (bf16, 32 x K, L2-resident) are the B operand (32 rows
-// in one MFMA), stored in the packed operand order so each fragment is one contiguous 1 KiB.  When a worker finishes a tile segment it runs the epilogue straight from its
+// branches); the block's activations (bf16, 32 x K per panel, L2-resident) are the B operand
+// (32 rows in one MFMA; a second panel of 32 rows reuses each weight fragment for a second
+// product), stored in the packed operand order so each fragment is one contiguous 1 KiB.
+// When a worker finishes a tile segment it runs the epilogue straight from its
 // accumulator registers if it owned the whole tile, else it stores a partial and the last
 // contributor of the tile (agent-scope counter) adds the partials in contributor order, so
 // results are deterministic.  Partials are handed over with coherent stores and loads, never
@@ -23,6 +26,11 @@
 //        accumulators held by one lane; v rows keep their order.
 //   GU:  p = 2i -> gate row 16t + i, p = 2i+1 -> up row 16t + i, so SwiGLU takes a pair.
 #include "gemm.h"
+
+// Optional per-workgroup timestamps for kernel studies (compiled out unless defined).
+#ifndef DLM_TRACE_POINT
+#define DLM_TRACE_POINT(i)
+#endif
 
 #include <vector>
 
@@ -133,7 +141,7 @@ __device__ inline void epi_v(const EpiParams& e, int m, int rel, float v) {
 
 __device__ inline void epi_swiglu(const EpiParams& e, int m, int j, float g, float u) {
   const float s = g / (1.0f + expf(-g));
-  store_act(e.act_out, e.bf16_out ? xpk_index(m, j) : (size_t)m * e.F + j, s * u, e.bf16_out);
+  store_act(e.act_out, e.bf16_out ? xpk_index_m(m, j, e.F) : (size_t)m * e.F + j, s * u, e.bf16_out);
 }
 
 // pair of packed rows (p, p+1), p even
@@ -168,7 +176,7 @@ struct GemmP {
   const uint16_t* X;
   int K, KT, tiles, NW, cmax, map;
   int R;             // row-owned mode: rows per workgroup (0: stream-K)
-  float* partial;    // [tiles][cmax][16][64]
+  float* partial;    // [tiles][cmax][16][64] (fixup) or [tiles][cmax][32 MB][32] (deferred)
   int* counters;     // [tiles]
   EpiParams ep;
 };
@@ -205,10 +213,11 @@ __device__ inline int contributors(const GemmP& p, int t, long long T, int* firs
   return lo - fo + 1;
 }
 
-template <int P>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmP p) {
+// MB: activation panels of 32 rows (2 only with deferred output).
+template <int P, int MB>
+__global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void gemm_bf16_kernel(GemmP p) {
   if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
-  __shared__ float red[4][MAXSEG][16][64];
+  __shared__ float red[4][MAXSEG][MB][16][64];
   __shared__ int s_last[MAXSEG];
   const int lane = threadIdx.x & 63;
   const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -218,21 +227,25 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmP p) {
   const int n = s1 - s0;
   const int nv = (n - v + 3) / 4;             // units of this wave: WG units v, v+4, ...
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.W + (size_t)s0 * 512, (uint32_t)n * 1024u);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, (uint32_t)(32 * p.K * 2));
+  const uint32_t xpanel = (uint32_t)(32 * p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, MB * xpanel);
   const uint32_t wo = (uint32_t)lane * 16u;
   const uint32_t xo = (uint32_t)lane * 16u;
-  u32x4_t wf[P], xf[P];
+  u32x4_t wf[P], xf[P][MB];
   int kpf = (s0 + v) % p.KT;   // step-in-tile of the next unit this wave prefetches
 #pragma unroll
   for (int u = 0; u < P; ++u) {
     wf[u] = bload16_nt(wr, wo + (uint32_t)(v + 4 * u) * 1024u);
-    xf[u] = bload16(xr, xo + (uint32_t)kpf * 1024u);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) xf[u][mb] = bload16(xr, xo + (uint32_t)kpf * 1024u + mb * xpanel);
     kpf += 4;
     if (kpf >= p.KT) kpf %= p.KT;
   }
-  f32x16_t acc;
+  f32x16_t acc[MB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   const int t0 = s0 / p.KT;
   const int nseg = (s1 - 1) / p.KT - t0 + 1;
   int seg = 0;
@@ -245,71 +258,88 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmP p) {
       const int unit = v + 4 * (k0 + u);
       while (unit < n && unit >= nextb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          red[v][seg][r][lane] = acc[r];
-          acc[r] = 0.f;
-        }
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            red[v][seg][mb][r][lane] = acc[mb][r];
+            acc[mb][r] = 0.f;
+          }
         ++seg;
         nextb += p.KT;
       }
-      acc = mfma32x32x16(wf[u], xf[u], acc);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32x32x16(wf[u], xf[u][mb], acc[mb]);
       wf[u] = bload16_nt(wr, wo + (uint32_t)(v + 4 * (k0 + u + P)) * 1024u);
-      xf[u] = bload16(xr, xo + (uint32_t)kpf * 1024u);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xf[u][mb] = bload16(xr, xo + (uint32_t)kpf * 1024u + mb * xpanel);
       kpf += 4;
       if (kpf >= p.KT) kpf %= p.KT;
     }
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[v][seg][r][lane] = acc[r];
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[v][seg][mb][r][lane] = acc[mb][r];
   for (int sg = seg + 1; sg < nseg; ++sg)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[v][sg][r][lane] = 0.f;
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[v][sg][mb][r][lane] = 0.f;
   __syncthreads();
   bool need[MAXSEG];
   int cnt[MAXSEG];
   bool any = false;
   for (int sg = 0; sg < nseg; ++sg) {
-    float sums[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 4 * v + q;
-      sums[q] = ((red[0][sg][r][lane] + red[1][sg][r][lane]) + red[2][sg][r][lane]) + red[3][sg][r][lane];
-    }
     const int t = t0 + sg;
     int fo;
     cnt[sg] = contributors(p, t, T, &fo);
     need[sg] = false;
-    if (p.ep.kind == EPI_PARTIAL) {
-      // [tile][contributor][m][n] with n contiguous: rows n = 8v + 4(lane/32) + q of column m
-      float* dst = p.partial + ((size_t)t * p.cmax + (g - fo)) * 1024 + (lane & 31) * 32 + 8 * v + 4 * (lane >> 5);
-      *(f32x4_t*)dst = f32x4_t{sums[0], sums[1], sums[2], sums[3]};
-    } else if (cnt[sg] == 1) {
-      epilogue_quarter(p, t, sums, v, lane);
-    } else {
-      need[sg] = any = true;
-      float* dst = p.partial + ((size_t)t * p.cmax + (g - fo)) * 1024;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) store_coherent(&dst[(4 * v + q) * 64 + lane], sums[q]);
+    for (int mb = 0; mb < MB; ++mb) {
+      float sums[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * v + q;
+        sums[q] = ((red[0][sg][mb][r][lane] + red[1][sg][mb][r][lane]) + red[2][sg][mb][r][lane]) +
+                  red[3][sg][mb][r][lane];
+      }
+      if (p.ep.kind == EPI_PARTIAL) {
+        // [tile][contributor][m][n] with n contiguous: rows n = 8v + 4(lane/32) + q of column m
+        float* dst = p.partial + ((size_t)t * p.cmax + (g - fo)) * (1024 * MB) + (32 * mb + (lane & 31)) * 32 +
+                     8 * v + 4 * (lane >> 5);
+        *(f32x4_t*)dst = f32x4_t{sums[0], sums[1], sums[2], sums[3]};
+      } else if constexpr (MB == 1) {
+        if (cnt[sg] == 1) {
+          epilogue_quarter(p, t, sums, v, lane);
+        } else {
+          need[sg] = any = true;
+          float* dst = p.partial + ((size_t)t * p.cmax + (g - fo)) * 1024;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) store_coherent(&dst[(4 * v + q) * 64 + lane], sums[q]);
+        }
+      }
     }
   }
-  if (!any) return;
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x < nseg) {
-    const int sg = threadIdx.x;
-    s_last[sg] = need[sg] ? (atomic_add_agent(&p.counters[t0 + sg], 1) == cnt[sg] - 1) : 0;
-  }
-  __syncthreads();
-  for (int sg = 0; sg < nseg; ++sg) {
-    if (!s_last[sg]) continue;
-    const int t = t0 + sg;
-    const float* base = p.partial + (size_t)t * p.cmax * 1024;
-    float tot[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < cnt[sg]; ++j)
+  if constexpr (MB == 1) {
+    if (!any) return;
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x < nseg) {
+      const int sg = threadIdx.x;
+      s_last[sg] = need[sg] ? (atomic_add_agent(&p.counters[t0 + sg], 1) == cnt[sg] - 1) : 0;
+    }
+    __syncthreads();
+    for (int sg = 0; sg < nseg; ++sg) {
+      if (!s_last[sg]) continue;
+      const int t = t0 + sg;
+      const float* base = p.partial + (size_t)t * p.cmax * 1024;
+      float tot[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < cnt[sg]; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tot[q] += load_coherent(&base[(size_t)j * 1024 + (4 * v + q) * 64 + lane]);
-    if (threadIdx.x == 0) store_agent(&p.counters[t], 0);
-    epilogue_quarter(p, t, tot, v, lane);
+        for (int q = 0; q < 4; ++q) tot[q] += load_coherent(&base[(size_t)j * 1024 + (4 * v + q) * 64 + lane]);
+      if (threadIdx.x == 0) store_agent(&p.counters[t], 0);
+      epilogue_quarter(p, t, tot, v, lane);
+    }
   }
 }
 
@@ -322,8 +352,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmP p) {
 // moves exactly R K 2 bytes of weights and one activation fragment per step feeds all NS
 // sub-tiles.  The 4 waves take every 4th step; their sums are added in LDS in fixed order.
 __device__ inline void epilogue_rows(const GemmP& p, int rowbase, int rows_s, const float (&v4)[4], int wave,
-                                     int lane) {
-  const int m = lane & 31;
+                                     int lane, int mb) {
+  const int m = 32 * mb + (lane & 31);
   if (m >= p.ep.M) return;
 #pragma unroll
   for (int q = 0; q < 4; q += 2) {
@@ -333,17 +363,20 @@ __device__ inline void epilogue_rows(const GemmP& p, int rowbase, int rows_s, co
   }
 }
 
-template <int NS, int P>
+// MB: activation panels of 32 rows; one weight fragment feeds NS x MB products.
+template <int NS, int P, int MB>
 __global__ __launch_bounds__(256, 1) void gemm_owned_kernel(GemmP p) {
+  DLM_TRACE_POINT(0);
   if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
-  __shared__ float red[4][NS][16][64];
+  __shared__ float red[4][NS][MB][16][64];
   const int lane = threadIdx.x & 63;
   const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x;
   const int R = p.R;
   const uint32_t step_bytes = (uint32_t)R * 32u;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.W + (size_t)g * R * p.K, step_bytes * (uint32_t)p.KT);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, (uint32_t)(32 * p.K * 2));
+  const uint32_t xpanel = (uint32_t)(32 * p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, MB * xpanel);
   uint32_t wo[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -353,45 +386,81 @@ __global__ __launch_bounds__(256, 1) void gemm_owned_kernel(GemmP p) {
   }
   const uint32_t xo = (uint32_t)lane * 16u;
   const int nv = (p.KT - v + 3) / 4;           // steps of this wave: v, v + 4, ...
-  u32x4_t wf[P][NS], xf[P];
+  // With several row sub-tiles per step (gate/up), workgroups start at different column
+  // steps (rotated by g KT / NW) so that the activation block, freshly written by the
+  // previous kernel, is not requested by every workgroup at the same address at the same
+  // time; measured, this helps the long gate/up stream and slightly slows the single-sub-tile
+  // QKV, which keeps the natural order.  A wave's i-th step is (v + 4 i + kofs) mod KT; steps
+  // past the wave's count read zeros (offsets at or above 2^31 are past every range).
+  const int kofs = NS >= 2 ? (int)(((long long)g * p.KT) / p.NW) : 0;
+  auto step_of = [&](int i) -> int {
+    const int k = v + 4 * i;
+    if (k >= p.KT) return -1;
+    return k + kofs >= p.KT ? k + kofs - p.KT : k + kofs;
+  };
+  auto w_off = [&](int i, int s) -> uint32_t {
+    const int r = step_of(i);
+    return r < 0 ? 0x80000000u : wo[s] + (uint32_t)r * step_bytes;
+  };
+  auto x_off = [&](int i) -> uint32_t {
+    const int r = step_of(i);
+    return r < 0 ? 0x80000000u : xo + (uint32_t)r * 1024u;
+  };
+  u32x4_t wf[P][NS], xf[P][MB];
 #pragma unroll
   for (int u = 0; u < P; ++u) {
-    const uint32_t kt = (uint32_t)(v + 4 * u);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) wf[u][s] = bload16_nt(wr, wo[s] + kt * step_bytes);
-    xf[u] = bload16(xr, xo + kt * 1024u);
+    for (int s = 0; s < NS; ++s) wf[u][s] = bload16_nt(wr, w_off(u, s));
+    const uint32_t xa = x_off(u);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) xf[u][mb] = bload16(xr, xa + mb * xpanel);
   }
-  f32x16_t acc[NS];
+  f32x16_t acc[NS][MB];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[s][r] = 0.f;
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[s][mb][r] = 0.f;
   for (int k0 = 0; k0 < nv; k0 += P) {
+    if (k0 == P) DLM_TRACE_POINT(1);
 #pragma unroll
     for (int u = 0; u < P; ++u) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) acc[s] = mfma32x32x16(wf[u][s], xf[u], acc[s]);
-      const uint32_t kt = (uint32_t)(v + 4 * (k0 + u + P));
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) wf[u][s] = bload16_nt(wr, wo[s] + kt * step_bytes);
-      xf[u] = bload16(xr, xo + kt * 1024u);
+        for (int mb = 0; mb < MB; ++mb) acc[s][mb] = mfma32x32x16(wf[u][s], xf[u][mb], acc[s][mb]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) wf[u][s] = bload16_nt(wr, w_off(k0 + u + P, s));
+      const uint32_t xa = x_off(k0 + u + P);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xf[u][mb] = bload16(xr, xa + mb * xpanel);
     }
   }
+  DLM_TRACE_POINT(2);
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[v][s][r][lane] = acc[s][r];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[v][s][mb][r][lane] = acc[s][mb][r];
   __syncthreads();
+  DLM_TRACE_POINT(3);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    float sums[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 4 * v + q;
-      sums[q] = ((red[0][s][r][lane] + red[1][s][r][lane]) + red[2][s][r][lane]) + red[3][s][r][lane];
+    for (int mb = 0; mb < MB; ++mb) {
+      float sums[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * v + q;
+        sums[q] = ((red[0][s][mb][r][lane] + red[1][s][mb][r][lane]) + red[2][s][mb][r][lane]) +
+                  red[3][s][mb][r][lane];
+      }
+      epilogue_rows(p, g * R + 32 * s, min(32, R - 32 * s), sums, v, lane, mb);
     }
-    epilogue_rows(p, g * R + 32 * s, min(32, R - 32 * s), sums, v, lane);
   }
+  DLM_TRACE_POINT(4);
 }
 
 // One workgroup per compute unit: the weight stream is split into equal contiguous ranges, so
@@ -434,22 +503,26 @@ static int gemm_cmax(int N, int K, int nw) {
   return (int)((K / 16) / minsteps + 2);
 }
 
-PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws) {
+static int panels(int M) { return M > 32 ? 2 : 1; }
+
+PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws, int M) {
   PartialSrc ps;
   ps.base = (const float*)((char*)ws + kCounterBytes);
   ps.tiles = N / 32;
   ps.KT = K / 16;
   ps.NW = plan.splits;
   ps.cmax = gemm_cmax(N, K, plan.splits);
-  ps.bytes = (size_t)ps.tiles * ps.cmax * 1024 * 4;
+  ps.mstride = 1024 * panels(M);
+  ps.row0 = 0;
+  ps.bytes = (size_t)ps.tiles * ps.cmax * ps.mstride * 4;
   ps.slots = nullptr;
   ps.nslot = 0;
   return ps;
 }
 
-size_t gemm_ws_bytes(int N, int K, GemmPlan plan) {
+size_t gemm_ws_bytes(int N, int K, GemmPlan plan, int mrows) {
   if (plan.R > 0) return kCounterBytes;
-  const size_t part = (size_t)(N / 32) * gemm_cmax(N, K, plan.splits) * 1024 * 4;
+  const size_t part = (size_t)(N / 32) * gemm_cmax(N, K, plan.splits) * 1024 * panels(mrows) * 4;
   return kCounterBytes + align_up(part, 256);
 }
 
@@ -471,18 +544,31 @@ int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const Ep
   p.partial = (float*)((char*)ws + kCounterBytes);
   p.ep = ep;
   p.R = plan.R;
+  if (ep.M < 1 || ep.M > 64) return fail(DLM_ERR_SHAPE, "gemm: %d rows (1..64 supported)", ep.M);
+  const int mb = panels(ep.M);
+  auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(p.NW), dim3(256), 0, st, p); };
   if (plan.R > 0) {
     if (ep.kind == EPI_PARTIAL) return fail(DLM_ERR_ARG, "gemm: row-owned plan has no partial sums");
     if (N != plan.R * plan.splits || plan.R % 2 || plan.R > 32 * kMaxSub)
       return fail(DLM_ERR_SHAPE, "gemm: bad row-owned plan");
     const int ns = (plan.R + 31) / 32;
-    if (ns == 1) hipLaunchKernelGGL((gemm_owned_kernel<1, 16>), dim3(p.NW), dim3(256), 0, st, p);
-    else if (ns == 2) hipLaunchKernelGGL((gemm_owned_kernel<2, 12>), dim3(p.NW), dim3(256), 0, st, p);
-    else if (ns == 3) hipLaunchKernelGGL((gemm_owned_kernel<3, 8>), dim3(p.NW), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((gemm_owned_kernel<4, 8>), dim3(p.NW), dim3(256), 0, st, p);
+    if (mb == 1) {
+      if (ns == 1) launch(gemm_owned_kernel<1, 16, 1>);
+      else if (ns == 2) launch(gemm_owned_kernel<2, 12, 1>);
+      else if (ns == 3) launch(gemm_owned_kernel<3, 8, 1>);
+      else launch(gemm_owned_kernel<4, 8, 1>);
+    } else {
+      if (ns == 1) launch(gemm_owned_kernel<1, 16, 2>);
+      else if (ns == 2) launch(gemm_owned_kernel<2, 12, 2>);
+      else if (ns == 3) launch(gemm_owned_kernel<3, 8, 2>);
+      else launch(gemm_owned_kernel<4, 8, 2>);
+    }
     return check_hip(hipGetLastError(), "gemm_bf16 launch");
   }
-  hipLaunchKernelGGL(gemm_bf16_kernel<8>, dim3(p.NW), dim3(256), 0, st, p);
+  if (mb == 2 && ep.kind != EPI_PARTIAL)
+    return fail(DLM_ERR_ARG, "gemm: more than 32 rows need a row-owned plan or deferred output");
+  if (mb == 1) launch(gemm_bf16_kernel<8, 1>);
+  else launch(gemm_bf16_kernel<8, 2>);
   return check_hip(hipGetLastError(), "gemm_bf16 launch");
 }
 

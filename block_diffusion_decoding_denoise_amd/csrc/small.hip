@@ -62,20 +62,21 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
       const int t = cc[j] >> 5;
       const int fo = owner_unit((long long)t * p.ps.KT, T, p.ps.NW);
       cnt[j] = valid[j] ? owner_unit((long long)(t + 1) * p.ps.KT - 1, T, p.ps.NW) - fo + 1 : 0;
-      off[j] = (uint32_t)((((size_t)t * p.ps.cmax) * 1024 + row * 32 + (cc[j] & 31)) * 4);
+      off[j] = (uint32_t)((((size_t)t * p.ps.cmax) * p.ps.mstride + (row + p.ps.row0) * 32 + (cc[j] & 31)) * 4);
+      const uint32_t cstep = (uint32_t)p.ps.mstride * 4u;    // bytes between contributors
 #pragma unroll
       for (int i = 0; i < NPF; ++i)
-        pv[j][i] = __builtin_bit_cast(f32x4_t, bload16(pr, i < cnt[j] ? off[j] + (uint32_t)i * 4096u : 0x80000000u));
+        pv[j][i] = __builtin_bit_cast(f32x4_t, bload16(pr, i < cnt[j] ? off[j] + (uint32_t)i * cstep : 0x80000000u));
     }
 #pragma unroll
     for (int j = 0; j < MAXV; ++j) {
 #pragma unroll
       for (int i = 0; i < NPF; ++i) xv[j] += pv[j][i];      // slots past cnt read zeros
       for (int i = NPF; i < cnt[j]; ++i)
-        xv[j] += __builtin_bit_cast(f32x4_t, bload16(pr, off[j] + (uint32_t)i * 4096u));
+        xv[j] += __builtin_bit_cast(f32x4_t, bload16(pr, off[j] + (uint32_t)i * (uint32_t)p.ps.mstride * 4u));
     }
   } else if (p.ps.slots) {
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.ps.slots + (size_t)row * p.ps.nslot * p.d,
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.ps.slots + (size_t)(row + p.ps.row0) * p.ps.nslot * p.d,
                                                 (uint32_t)(p.ps.nslot * p.d * 4));
     constexpr int MAXSL = 10;
     f32x4_t sv[MAXV][MAXSL];
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
       ow.x = pack2bf(xv[j][0] * r * g4[0], xv[j][1] * r * g4[1]);
       ow.y = pack2bf(xv[j][2] * r * g4[2], xv[j][3] * r * g4[3]);
       // 4 consecutive columns stay contiguous in the packed operand order
-      *(uint2*)((uint16_t*)p.out + (p.packed ? xpk_index(row, c) : (size_t)row * p.d + c)) = ow;
+      *(uint2*)((uint16_t*)p.out + (p.packed ? xpk_index_m(row, c, p.d) : (size_t)row * p.d + c)) = ow;
     } else {
       f32x4_t o;
 #pragma unroll

@@ -303,6 +303,30 @@ int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_
                      int32_t* tokens, dlm_round_state* state, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* dlm_decode_block_pipelined -- dlm_decode_block with the block's own commit pass left
+ * pending, so that the next block can carry it.  The call decodes the block in `tokens`
+ * exactly as dlm_decode_block does, but first completes the PREVIOUS block's pending commit
+ * pass (prev_tokens: that block's committed tokens [block] i32, device; NULL when no block is
+ * pending) and ends without appending this block's K/V: after it, L has grown by the previous
+ * block only, and this block is pending.  A run of blocks is therefore
+ *   pipelined(prev = NULL, t0), pipelined(t0, t1), ..., pipelined(t_{n-2}, t_{n-1}),
+ *   dlm_commit_pass(t_{n-1})
+ * and produces the same tokens and cache as dlm_decode_block on each block in turn: the commit
+ * pass is the forward of the clean block whose K/V the next block attends to ([ORL-blog]
+ * "What shipped"), and nothing in round 0 of the next block depends on it other than those
+ * K/V.  For dense bf16 models with block = 32 the commit rows ride along with round 0 as one
+ * 64-row forward (rows 0..31: the previous block at positions L .. L + 31; rows 32..63: round
+ * 0 at L + 32 .., attending to the prefix, the previous block and each other), so the layer
+ * weights stream once for both; other models run the commit pass on its own first.
+ *   prev_tokens must not alias tokens and must hold the previous block's final tokens until
+ *   the call's work has run.  The cache must have room for both blocks: L + 2 block <=
+ *   max_len at the call (the kernels write no K/V at or past cap).  Other arguments and
+ *   errors as dlm_decode_block; DLM_ERR_ARG when prev_tokens == tokens.
+ *   The debug views' x after a pipelined round 0 holds the 64 rows of the fused forward. */
+int dlm_decode_block_pipelined(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                               const int32_t* prev_tokens, int32_t* tokens, dlm_round_state* state,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* Commit passes over n / block consecutive prompt blocks (n % block == 0): forwards each
  * block of ids (device int32 [n]) and appends its K/V; L += n. */
 int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
@@ -310,7 +334,8 @@ int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv,
 
 /* Debug/test hooks on the decode workspace (device pointers into ws; NULL if absent). */
 typedef struct {
-  float* x;          /* [block, d] residual stream of the last forward */
+  float* x;          /* [block, d] residual stream of the last forward ([64, d] after a fused
+                        round 0 of dlm_decode_block_pipelined) */
   void* hn;          /* [block, d] final-normed rows (model dtype) */
   float* pe;         /* [block, d] p.E of the last round */
   float* lse;        /* [block] */

@@ -1,0 +1,113 @@
+"""GPU: a block's commit pass carried by the next block's round 0 (dlm_decode_block_pipelined).
+
+The pipelined sequence must give the same tokens, round states and KV cache as decoding each
+block with its own commit pass.  For dense bf16 models with 32-row blocks the commit rows and
+round 0 share one 64-row forward; every row of it runs the same arithmetic in the same order
+as in the separate passes (each row's GEMM outputs come from their own matrix-core columns
+with the same contraction order, the attention of each query block sees the same keys and
+splits), so the comparison is bitwise.  The f32 model runs the commit pass on its own and is
+compared with the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from oracle import Prec, OracleModel, CommitRule as OCommitRule
+from tests.gpu_util import require_gpu, storage
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dlm():
+    require_gpu()
+    import block_diffusion_decoding_denoise_amd as dlm
+    dlm.lib()
+    return dlm
+
+
+def _model(shape, seed, cap):
+    dlm = _dlm()
+    w = synth.Weights(shape, seed)
+    up = {n: storage(w[n], shape.dtype) for n in w.names_dense()}
+    return dlm.Model(shape, up, cap=cap), w
+
+
+def _run(dlm, m, prompt, n_blocks, rule, pipelined):
+    toks, states = m.generate(torch.from_numpy(prompt), n_blocks, rule, pipelined=pipelined)
+    torch.cuda.synchronize()
+    n = len(prompt) + 32 * n_blocks
+    assert int(m.len_dev.item()) == n
+    k = [x[:, :n].clone() for x in m.k]
+    v = [dlm.v_cache_to_natural(x)[:, :n].clone() for x in m.v]
+    return toks, states, k, v
+
+
+SMALL = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
+                          vocab=3001)
+# the 4B layer shapes (row-owned gate/up with 3 sub-tiles, QKV with 24 rows per workgroup,
+# stream-K attention-output and down projections with their real partial counts)
+QWEN4B_2L = synth.small_shape(synth.QWEN4B, name="qwen4b-2-layers", n_layers=2)
+
+
+@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args", [
+    (SMALL, 1234, 64, 3, ("fixed_k", 6)),
+    (SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32)),
+    (SMALL, 1236, 96, 2, ("fixed_k", 32)),
+    (QWEN4B_2L, 1234, 256, 3, ("fixed_k", 6)),
+], ids=["small-k6", "small-threshold", "small-k32", "qwen4b-2l-k6"])
+def test_pipelined_bitexact_bf16(shape, seed, prompt_len, n_blocks, rule_args):
+    dlm = _dlm()
+    _say(f"pipelined vs separate commit passes: {shape.name} seed {seed} prompt {prompt_len} "
+         f"blocks {n_blocks} rule {rule_args}")
+    m, _ = _model(shape, seed, cap=prompt_len + 32 * n_blocks)
+    rule = getattr(dlm.CommitRule, rule_args[0])(*rule_args[1:])
+    prompt = synth.prompt_ids(shape, prompt_len, seed)
+    t0, s0, k0, v0 = _run(dlm, m, prompt, n_blocks, rule, pipelined=False)
+    t1, s1, k1, v1 = _run(dlm, m, prompt, n_blocks, rule, pipelined=True)
+    assert s0 == s1
+    assert torch.equal(t0, t1)
+    for l in range(shape.n_layers):
+        assert torch.equal(k0[l], k1[l]), f"layer {l} keys"
+        assert torch.equal(v0[l], v1[l]), f"layer {l} values"
+    # replaying the captured graphs gives the same again
+    t2, s2, k2, _ = _run(dlm, m, prompt, n_blocks, rule, pipelined=True)
+    assert torch.equal(t1, t2) and s1 == s2
+    assert all(torch.equal(a, b) for a, b in zip(k1, k2))
+
+
+def test_pipelined_tiny_fp32_matches_oracle():
+    """f32: the pending commit pass runs on its own; tokens and rounds bit-exact with the
+    oracle's block loop, and the final cache equal to the oracle's."""
+    dlm = _dlm()
+    s = synth.TINY
+    _say("pipelined tiny fp32, seed 1234")
+    m, w = _model(s, 1234, cap=64 + 4 * 32)
+    prompt = synth.prompt_ids(s, 64, 1234)
+    rule = dlm.CommitRule.threshold(0.9, True, 32)
+    toks, states, k, v = _run(dlm, m, prompt, 4, rule, pipelined=True)
+    om = OracleModel(s, w, Prec("f32"))
+    ref, blocks, kv = oracle.generate(om, prompt, 4, OCommitRule(0, 0.9, 1, True, 32), Prec("f32"))
+    np.testing.assert_array_equal(toks.numpy(), ref)
+    for b, (st, br) in enumerate(zip(states, blocks)):
+        assert st["round"] == br.rounds and st["n_new"] == br.n_new and st["flags"] == br.flags, f"block {b}"
+    n = 64 + 4 * 32
+    for l in range(s.n_layers):
+        np.testing.assert_allclose(k[l].cpu().numpy(), kv.k[l][:, :n], atol=2e-5, rtol=1e-4)
+        np.testing.assert_allclose(v[l].cpu().numpy(), kv.v[l][:, :n], atol=2e-5, rtol=1e-4)
+
+
+def test_pipelined_rejects_aliased_tokens():
+    dlm = _dlm()
+    m, _ = _model(SMALL, 1234, cap=128)
+    rule = dlm.CommitRule.fixed_k(6)
+    with pytest.raises(dlm.DlmError):
+        m.decode_block_pipelined(rule, m.tokens, m.tokens)
