@@ -43,19 +43,23 @@ struct HeadP {
   const int32_t* cont_dev;
 };
 
+// open rows of the block (rows <= 64) as a bit mask: one flag load per lane, then a wave
+// ballot (every wave computes the same mask)
+__device__ inline unsigned long long open_mask(const uint8_t* committed, int rows) {
+  const int lane = threadIdx.x & 63;
+  bool open = false;
+  if (lane < rows) open = committed == nullptr || committed[lane] == 0;
+  return __ballot(open);
+}
+
 // open-row compaction shared by all kernels: returns n_open, and fills idx[k] = row of the
-// k-th open row (idx in LDS, size >= 64); thread-count independent.
+// k-th open row (idx in LDS, size >= 64); any multiple of 64 threads.
 __device__ inline int compact_open(const uint8_t* committed, int rows, int* idx) {
-  int n = 0;
-  for (int i = 0; i < rows; ++i) {
-    const bool open = committed == nullptr || committed[i] == 0;
-    if (open) {
-      if (threadIdx.x == 0) idx[n] = i;
-      ++n;
-    }
-  }
+  const unsigned long long mask = open_mask(committed, rows);
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64 && ((mask >> lane) & 1ull)) idx[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
   __syncthreads();
-  return n;
+  return __popcll(mask);
 }
 
 // bf16 path: 256 workgroups = 8 XCDs x 32 slots; the n_groups row groups of a chunk share
@@ -67,7 +71,10 @@ __device__ inline int n_chunks_for(int n_groups, int chunks_fixed) {
 // statistics layout per (chunk, open row): m, s, T, best value, best index (as float bits)
 enum { ST_M = 0, ST_S = 1, ST_T = 2, ST_BV = 3, ST_BI = 4 };
 
-template <int MAXK, int NW>
+// Loads are branch-free (rows, vocabulary entries and d-steps out of range use out-of-range
+// buffer offsets, which read zeros), so the next tile's loads stay in flight while a tile is
+// processed.  DBG: also store every logit (tests).
+template <int MAXK, int NW, bool DBG>
 __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   __shared__ int s_idx[DLM_MAX_ROWS];
@@ -100,10 +107,11 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
     const int k = 16 * grp + (lane & 15);
     const bool ok = k < n_open;
     const int row = ok ? s_idx[k] : 0;
+    const __amdgpu_buffer_rsrc_t hr = make_rsrc(p.h, (uint32_t)(p.rows * p.d * 2));
 #pragma unroll
     for (int u = 0; u < MAXK; ++u)
-      hf[u] = (ok && u < nk) ? ld16(p.h + (size_t)row * p.d + (kw0 + u) * 32 + 8 * (lane >> 4))
-                             : u32x4_t{0u, 0u, 0u, 0u};
+      hf[u] = bload16(hr, (ok && u < nk) ? (uint32_t)((row * p.d + (kw0 + u) * 32 + 8 * (lane >> 4)) * 2)
+                                         : 0x80000000u);
   }
   f32x4_t acc[MAXK][2];
 #pragma unroll
@@ -114,36 +122,35 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
   int bi = 0x7fffffff;
   const int my_row = tid >> 4, my_v = tid & 15;
 
+  // E rows as a buffer (the host keeps V d 2 < 2^31)
+  const __amdgpu_buffer_rsrc_t er = make_rsrc(p.E, (uint32_t)((size_t)p.V * p.d * 2));
   auto load_tile = [&](int t, u32x4_t* ef) {
     const int v = t * 16 + (lane & 15);
-    const bool ok = v < p.V;
+    const bool ok = v < p.V && t < t1;
+    const uint32_t base = ((uint32_t)v * (uint32_t)p.d + (uint32_t)(kw0 * 32 + 8 * (lane >> 4))) * 2u;
 #pragma unroll
-    for (int u = 0; u < MAXK; ++u)
-      ef[u] = (ok && u < nk) ? ld16(p.E + (size_t)v * p.d + (kw0 + u) * 32 + 8 * (lane >> 4))
-                             : u32x4_t{0u, 0u, 0u, 0u};
+    for (int u = 0; u < MAXK; ++u) ef[u] = bload16(er, (ok && u < nk) ? base + (uint32_t)u * 64u : 0x80000000u);
   };
   u32x4_t ef[MAXK], en[MAXK];
-  if (t0 < t1) load_tile(t0, ef);
+  load_tile(t0, ef);
   for (int t = t0; t < t1; ++t) {
-    if (t + 1 < t1) load_tile(t + 1, en);
-    // (1) partial logits over this wave's d-slice: L^T[v][row]
+    load_tile(t + 1, en);     // past t1: zeros, no traffic
+    // (1) partial logits over this wave's d-slice: L^T[v][row] (d-steps past nk are zeros)
     f32x4_t lp = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < MAXK; ++u)
-      if (u < nk) lp = mfma16x16x32(ef[u], hf[u], lp);
+    for (int u = 0; u < MAXK; ++u) lp = mfma16x16x32(ef[u], hf[u], lp);
 #pragma unroll
     for (int r = 0; r < 4; ++r) lpart[w][4 * (lane >> 4) + r][lane & 15] = lp[r];
     // keep this wave's E slice, transposed, for the p.E product
 #pragma unroll
-    for (int u = 0; u < MAXK; ++u)
-      if (u < nk) {
+    for (int u = 0; u < MAXK; ++u) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int dl = u * 32 + 8 * (lane >> 4) + 2 * i;
-          Et[w][dl][lane & 15] = (uint16_t)(ef[u][i] & 0xffffu);
-          Et[w][dl + 1][lane & 15] = (uint16_t)(ef[u][i] >> 16);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int dl = u * 32 + 8 * (lane >> 4) + 2 * i;
+        Et[w][dl][lane & 15] = (uint16_t)(ef[u][i] & 0xffffu);
+        Et[w][dl + 1][lane & 15] = (uint16_t)(ef[u][i] >> 16);
       }
+    }
     __syncthreads();
     // (2) reduce partials, update the statistics of row my_row (threads 0..255)
     if (tid < 256) {
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
       const bool valid = vg < p.V;
       if (!valid) l = -INFINITY;
       const int k = 16 * grp + my_row;
-      if (p.logits_dbg && valid && k < n_open) p.logits_dbg[(size_t)s_idx[k] * p.V + vg] = l;
+      if (DBG && valid && k < n_open) p.logits_dbg[(size_t)s_idx[k] * p.V + vg] = l;
       float tm = l;
       for (int o = 1; o < 16; o <<= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
       // tile argmax (lowest id among equal values)
@@ -188,22 +195,19 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) al4[r] = alpha_s[4 * (lane >> 4) + r];
 #pragma unroll
-      for (int u = 0; u < MAXK; ++u)
-        if (u < nk) {
+      for (int u = 0; u < MAXK; ++u) {
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const u32x2_t eb = *(const u32x2_t*)&Et[w][u * 32 + 16 * hb + (lane & 15)][4 * (lane >> 4)];
-            f32x4_t a = acc[u][hb];
+        for (int hb = 0; hb < 2; ++hb) {
+          const u32x2_t eb = *(const u32x2_t*)&Et[w][u * 32 + 16 * hb + (lane & 15)][4 * (lane >> 4)];
+          f32x4_t a = acc[u][hb];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] *= al4[r];
-            acc[u][hb] = mfma16x16x16(pa, eb, a);
-          }
+          for (int r = 0; r < 4; ++r) a[r] *= al4[r];
+          acc[u][hb] = mfma16x16x16(pa, eb, a);
         }
+      }
     }
-    if (t + 1 < t1) {
 #pragma unroll
-      for (int u = 0; u < MAXK; ++u) ef[u] = en[u];
-    }
+    for (int u = 0; u < MAXK; ++u) ef[u] = en[u];
   }
   // partial outputs for rows k = 16grp + r
   if (tid < 256 && my_v == 0) {
@@ -354,8 +358,7 @@ __global__ __launch_bounds__(256) void head_combine_kernel(HeadP p, int bf16_pat
     if (p.pe && dcol < p.d) p.pe[(size_t)row * p.d + dcol] = 0.f;
     return;
   }
-  int k = 0;
-  for (int i = 0; i < row; ++i) k += (p.committed == nullptr || p.committed[i] == 0) ? 1 : 0;
+  const int k = __popcll(open_mask(p.committed, p.rows) & ((1ull << row) - 1ull));   // open rows before row
   const int n_groups = (n_open + 15) / 16;
   const int CH = bf16_path ? n_chunks_for(n_groups, 0) : p.chunks_fixed;
   float cm = -INFINITY, cs = 0.f, ct = 0.f, cbv = -INFINITY;
@@ -442,11 +445,17 @@ int head_launch(int dtype, const void* h, const void* E, const uint8_t* committe
   p.pe = pe;
   p.cont_dev = cont_dev;
   if (dtype == DLM_BF16) {
+    if ((size_t)V * d * 2 >= (1ull << 31)) return fail(DLM_ERR_SHAPE, "head: embedding of %d x %d too large", V, d);
     const int grid = 256;   // n_groups * chunks <= 256, extra workgroups exit
     const int k8 = (d / 32 + 7) / 8;     // k-steps per wave with 8 waves
+    const bool dbg = logits_dbg != nullptr;
     if (k8 <= 10) {
       switch (k8) {
-#define HEAD_CASE(K) case K: hipLaunchKernelGGL((head_bf16_kernel<K, 8>), dim3(grid), dim3(512), 0, st, p); break;
+#define HEAD_CASE(K)                                                                                    \
+  case K:                                                                                               \
+    if (dbg) hipLaunchKernelGGL((head_bf16_kernel<K, 8, true>), dim3(grid), dim3(512), 0, st, p);       \
+    else hipLaunchKernelGGL((head_bf16_kernel<K, 8, false>), dim3(grid), dim3(512), 0, st, p);          \
+    break;
         HEAD_CASE(1) HEAD_CASE(2) HEAD_CASE(3) HEAD_CASE(4) HEAD_CASE(5) HEAD_CASE(6) HEAD_CASE(7)
         HEAD_CASE(8) HEAD_CASE(9) HEAD_CASE(10)
 #undef HEAD_CASE
@@ -455,7 +464,8 @@ int head_launch(int dtype, const void* h, const void* E, const uint8_t* committe
     } else {
       const int k16 = (d / 32 + 15) / 16;
       if (k16 > 8) return fail(DLM_ERR_SHAPE, "head: d=%d too large", d);
-      hipLaunchKernelGGL((head_bf16_kernel<8, 16>), dim3(grid), dim3(1024), 0, st, p);
+      if (dbg) hipLaunchKernelGGL((head_bf16_kernel<8, 16, true>), dim3(grid), dim3(1024), 0, st, p);
+      else hipLaunchKernelGGL((head_bf16_kernel<8, 16, false>), dim3(grid), dim3(1024), 0, st, p);
     }
   } else {
     hipLaunchKernelGGL(head_f32_kernel, dim3(rows * 16), dim3(256), 0, st, p);
