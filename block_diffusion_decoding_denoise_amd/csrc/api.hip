@@ -343,7 +343,7 @@ static void layout_packed(dlm_model* m) {
     }
   }
   m->packed_bytes = d.dtype == DLM_BF16 ? off : 0;
-  m->pl_sc = gemm_plan(d.d, d.d);
+  m->pl_sc = gemm_plan_owned(d.d, d.d);
   m->pl_qkv = gemm_plan_owned(m->n_qkv, d.d);
   m->pl_o = gemm_plan(d.d, d.hq * D);
   if (d.n_experts == 0) {
@@ -408,7 +408,8 @@ extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const d
   {
     const void* s[1] = {w_sc};
     int r[1] = {d->d};
-    rc = pack_bf16(s, r, 1, d->d, d->d, nullptr, out + m.off_sc, st);
+    rc = m.pl_sc.R ? pack_bf16_owned(s, r, 1, d->d, d->d, nullptr, m.pl_sc.R, out + m.off_sc, st)
+                   : pack_bf16(s, r, 1, d->d, d->d, nullptr, out + m.off_sc, st);
     if (rc) return rc;
   }
   for (int l = 0; l < d->n_layers; ++l) {

@@ -84,18 +84,31 @@ __global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
   const int HG = G / WPG;
   const int per_qb = p.hkv * HG * p.nsplit_max;
   const int qblk = blockIdx.x / per_qb, bx = blockIdx.x % per_qb;
-  const int L = (p.len_dev ? *p.len_dev : p.len_host) + 32 * qblk;
-  const int N = min(L + p.B, p.cap);
-  const int chunk = split_chunk(N, p.nsplit_max);
-  const int nsplit = (N + chunk - 1) / chunk;
   const int s = bx % p.nsplit_max, gh = bx / p.nsplit_max;
   const int g = gh / HG, hg = gh % HG;
-  if (s >= nsplit) return;
-  DLM_TRACE_POINT(1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = WPG * hg + w;                // query head within the kv head's group
   const int head = g * G + hl;
+  // Q fragments (B operand): lane l: query 16qb + l%16, d = 32ds + 8(l/16) .. +8; requested
+  // before the prefix length is known (queries past B read zeros)
+  u32x4_t qf[2][DS];
+  {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.q, (uint32_t)(32 * p.nqb * p.hq * D * 2));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qi = 16 * qb + (lane & 15);
+      const uint32_t qo = (uint32_t)((((32 * qblk + qi) * p.hq + head) * D + 8 * (lane >> 4)) * 2);
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) qf[qb][ds] = bload16(qr, qi < p.B ? qo + (uint32_t)ds * 64u : 0x80000000u);
+    }
+  }
+  const int L = (p.len_dev ? *p.len_dev : p.len_host) + 32 * qblk;
+  const int N = min(L + p.B, p.cap);
+  const int chunk = split_chunk(N, p.nsplit_max);
+  const int nsplit = (N + chunk - 1) / chunk;
+  if (s >= nsplit) return;
+  DLM_TRACE_POINT(1);
   const int c0 = s * chunk, c1 = min(N, c0 + chunk);
   const int npass = (c1 - c0 + PT * TK - 1) / (PT * TK);
   // buffer descriptors: K rows past c1 read as zeros; V^T tiles stay inside this head's
@@ -143,16 +156,6 @@ __global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
   };
   fetch(c0);
 
-  // Q fragments (B operand): lane l: query 16qb + l%16, d = 32ds + 8(l/16) .. +8
-  u32x4_t qf[2][DS];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = 16 * qb + (lane & 15);
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qf[qb][ds] = qi < p.B ? ld16(p.q + ((size_t)(32 * qblk + qi) * p.hq + head) * D + 32 * ds + 8 * (lane >> 4))
-                            : u32x4_t{0u, 0u, 0u, 0u};
-  }
   f32x4_t o[DB][2];
 #pragma unroll
   for (int b = 0; b < DB; ++b) o[b][0] = o[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};

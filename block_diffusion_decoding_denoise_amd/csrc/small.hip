@@ -142,61 +142,54 @@ struct CommitP {
 
 __device__ inline float rank_key(float v) { return v != v ? -INFINITY : v; }
 
-// single wave; lane 0 runs the (tiny) selection so the tie-breaks read like the definition
+// One wave, lane i = row i (rows <= 64): every row's statistics are loaded at once, and the
+// selection is taken through wave ballots.  An open row's rank is the number of open rows
+// ranked before it (larger max-prob first, NaN as -inf, lower index first among equals), so
+// "rank < k" picks exactly the k rows that k successive picks of the best remaining row take.
 __global__ __launch_bounds__(64) void commit_kernel(CommitP p) {
-  if (threadIdx.x != 0) return;
   dlm_round_state* st = p.st;
   if (st->cont == 0) return;
   const int round = st->round;
-  uint64_t open = 0;
-  int n_open = 0, flags = 0;
-  for (int i = 0; i < p.rows; ++i)
-    if (!p.committed[i]) {
-      open |= 1ull << i;
-      ++n_open;
-      const bool fin = isfinite(p.maxp[i]) && (!p.lse || isfinite(p.lse[i])) && (!p.ent || isfinite(p.ent[i]));
-      if (!fin) flags |= DLM_FLAG_NONFINITE;
-    }
-  uint64_t sel = 0;
-  auto best_of = [&](uint64_t cand) {
-    int b = -1;
-    float bv = 0.f;
-    for (int i = 0; i < p.rows; ++i)
-      if (cand >> i & 1ull) {
-        const float v = rank_key(p.maxp[i]);
-        if (b < 0 || v > bv) { b = i; bv = v; }
-      }
-    return b;
-  };
+  const int lane = threadIdx.x;
+  const bool in = lane < p.rows;
+  const int i = in ? lane : 0;                 // rows >= 1: lanes past the block re-read row 0
+  const bool is_open = in && !p.committed[i];
+  const float mp = p.maxp[i];
+  const float ls = p.lse ? p.lse[i] : 0.f;
+  const float en = p.ent ? p.ent[i] : 0.f;
+  const int32_t am = p.amax[i];
+  const uint64_t open = __ballot(is_open);
+  const int n_open = __popcll(open);
+  int flags = __ballot(is_open && !(isfinite(mp) && isfinite(ls) && isfinite(en))) ? DLM_FLAG_NONFINITE : 0;
+  const float key = rank_key(mp);
+  int rank = 0;
+  for (int j = 0; j < p.rows; ++j) {
+    const float kj = __shfl(key, j, 64);
+    rank += ((open >> j) & 1ull) && (kj > key || (kj == key && j < lane)) ? 1 : 0;
+  }
+  uint64_t sel;
   if (p.rule.mode == DLM_COMMIT_THRESHOLD) {
-    for (int i = 0; i < p.rows; ++i)
-      if ((open >> i & 1ull) && p.maxp[i] >= p.rule.tau) sel |= 1ull << i;
-    if (p.rule.forced_top1 && n_open > 0) sel |= 1ull << best_of(open);
+    sel = __ballot(is_open && mp >= p.rule.tau);
+    if (p.rule.forced_top1 && n_open > 0) sel |= __ballot(is_open && rank == 0);
   } else {
-    const int k = min(p.rule.k, n_open);
-    uint64_t cand = open;
-    for (int j = 0; j < k; ++j) {
-      const int b = best_of(cand);
-      sel |= 1ull << b;
-      cand &= ~(1ull << b);
-    }
+    sel = __ballot(is_open && rank < min(p.rule.k, n_open));
   }
   if (round >= p.rule.max_rounds - 1) {
     if (open & ~sel) flags |= DLM_FLAG_HIT_MAX_ROUNDS;
     sel = open;
   }
-  int n_new = 0;
-  for (int i = 0; i < p.rows; ++i)
-    if (sel >> i & 1ull) {
-      p.tokens[i] = p.amax[i];
-      p.committed[i] = 1;
-      ++n_new;
-    }
-  if (round < DLM_MAX_ROUNDS) st->n_new[round] = n_new;
-  st->round = round + 1;
-  st->n_open = n_open - n_new;
-  st->flags |= flags;
-  st->cont = (st->n_open > 0 && round + 1 < p.rule.max_rounds) ? 1 : 0;
+  if (in && ((sel >> lane) & 1ull)) {
+    p.tokens[lane] = am;
+    p.committed[lane] = 1;
+  }
+  if (lane == 0) {
+    const int n_new = __popcll(sel);
+    if (round < DLM_MAX_ROUNDS) st->n_new[round] = n_new;
+    st->round = round + 1;
+    st->n_open = n_open - n_new;
+    st->flags |= flags;
+    st->cont = (st->n_open > 0 && round + 1 < p.rule.max_rounds) ? 1 : 0;
+  }
 }
 
 // ------------------------------------------------------------------ block reset
