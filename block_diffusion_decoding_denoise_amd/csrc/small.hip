@@ -7,7 +7,7 @@ namespace dlm {
 namespace {
 
 // ------------------------------------------------------------------ RMSNorm
-// One workgroup (256 threads) per row; deterministic fixed-order reduction.  When the residual
+// One workgroup (NTH threads, 1024 as launched) per row; deterministic fixed-order reduction.  When the residual
 // stream has pending GEMM partial sums (a residual projection with deferred output), the row is
 // first completed as x + p_0 + p_1 + ... in contributor order and written back.
 struct NormP {
@@ -24,22 +24,24 @@ __device__ inline int owner_unit(long long s, long long T, int NW) {
   return (int)(((s + 1) * NW - 1) / T);
 }
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
+template <int NTH>
+__global__ __launch_bounds__(NTH) void rmsnorm_kernel(NormP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
-  __shared__ float red[4];
+  constexpr int NWV = NTH / 64;
+  __shared__ float red[NWV];
   const int row = blockIdx.x, tid = threadIdx.x;
   float* x = p.x + (size_t)row * p.d;
   // every load of the row (x, gains, pending partial sums) is issued, unconditionally, before
   // any arithmetic: addresses of columns past d are clamped to column 0 and their values
   // ignored, and partial slots past a tile's contributor count use out-of-range buffer
-  // offsets, which read zeros (d <= 4096: <= 4 float4 per thread)
-  constexpr int MAXV = 4, NPF = 6;
+  // offsets, which read zeros (d <= 4096: <= 4096 / (4 NTH) float4 per thread)
+  constexpr int MAXV = 4096 / 4 / NTH, NPF = 6;
   int cc[MAXV];
   bool valid[MAXV];
   f32x4_t xv[MAXV];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
-    const int c = 4 * (tid + 256 * j);
+    const int c = 4 * (tid + NTH * j);
     valid[j] = c < p.d;
     cc[j] = valid[j] ? c : 0;
     xv[j] = *(const f32x4_t*)(x + cc[j]);
@@ -105,7 +107,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(NormP p) {
   s = wave_sum(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
-  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) tot += red[i];
   const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
@@ -259,7 +263,7 @@ int rmsnorm(float* x, const void* g, void* out, int rows, int d, int bf16, int p
             const int32_t* cont_dev, hipStream_t st, const PartialSrc* ps) {
   PartialSrc none{};
   NormP p{x, g, out, d, bf16, packed, eps, cont_dev, ps ? *ps : none};
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(rmsnorm_kernel<1024>, dim3(rows), dim3(1024), 0, st, p);
   return check_hip(hipGetLastError(), "rmsnorm launch");
 }
 
