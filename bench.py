@@ -304,7 +304,7 @@ def main():
     gemm_bytes = 2 * (2 * s.ffn * s.d) + 2 * 32 * s.d + 2 * 32 * s.ffn
     roofline = {"bound": "hbm", "achieved": gemm_bytes / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": gemm_bytes / t_launch / HBM_PEAK, "traffic": counter_traffic(),
-                "kernel": "gemm_owned_kernel<3, 8> (FFN gate/up + SwiGLU, N=19456, K=2560, M=32)",
+                "kernel": "gemm_owned_kernel<3, 8, 1> (FFN gate/up + SwiGLU, N=19456, K=2560, M=32)",
                 "bytes_per_launch": gemm_bytes, "us_per_launch": t_launch * 1e6, "launches": n_launch}
     log(f"gate/up + SwiGLU: {t_launch * 1e6:.1f} us/launch, {roofline['achieved']:.0f} GB/s")
 
