@@ -552,16 +552,18 @@ int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const Ep
     if (N != plan.R * plan.splits || plan.R % 2 || plan.R > 32 * kMaxSub)
       return fail(DLM_ERR_SHAPE, "gemm: bad row-owned plan");
     const int ns = (plan.R + 31) / 32;
+    // ring depths from sweeps at the 4B shapes (QKV: 8 beat 6, 12, 16 and 20 steps; gate/up
+    // with two panels: 4 beat 6 and 8)
     if (mb == 1) {
-      if (ns == 1) launch(gemm_owned_kernel<1, 16, 1>);
+      if (ns == 1) launch(gemm_owned_kernel<1, 8, 1>);
       else if (ns == 2) launch(gemm_owned_kernel<2, 12, 1>);
       else if (ns == 3) launch(gemm_owned_kernel<3, 8, 1>);
       else launch(gemm_owned_kernel<4, 8, 1>);
     } else {
-      if (ns == 1) launch(gemm_owned_kernel<1, 16, 2>);
-      else if (ns == 2) launch(gemm_owned_kernel<2, 12, 2>);
-      else if (ns == 3) launch(gemm_owned_kernel<3, 8, 2>);
-      else launch(gemm_owned_kernel<4, 8, 2>);
+      if (ns == 1) launch(gemm_owned_kernel<1, 8, 2>);
+      else if (ns == 2) launch(gemm_owned_kernel<2, 8, 2>);
+      else if (ns == 3) launch(gemm_owned_kernel<3, 4, 2>);
+      else launch(gemm_owned_kernel<4, 4, 2>);
     }
     return check_hip(hipGetLastError(), "gemm_bf16 launch");
   }
