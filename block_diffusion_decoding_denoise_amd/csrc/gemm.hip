@@ -570,7 +570,7 @@ int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const Ep
   if (mb == 2 && ep.kind != EPI_PARTIAL)
     return fail(DLM_ERR_ARG, "gemm: more than 32 rows need a row-owned plan or deferred output");
   if (mb == 1) launch(gemm_bf16_kernel<8, 1>);
-  else launch(gemm_bf16_kernel<8, 2>);
+  else launch(gemm_bf16_kernel<4, 2>);   // two panels: a 4-unit ring measured faster than 6 or 8
   return check_hip(hipGetLastError(), "gemm_bf16 launch");
 }
 
