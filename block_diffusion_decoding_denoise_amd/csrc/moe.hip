@@ -157,31 +157,31 @@ __global__ __launch_bounds__(256) void moe_route_kernel(RouteP p) {
   __shared__ float red[4];
   const bool has = tid < m.E;
   const float r = has ? p.logits[(size_t)row * m.E + tid] : -INFINITY;   // issued before the MX work
-  for (int b = tid; b < m.d / 32; b += 256) {
-    float v[32];
+  // MXFP8 of the row: four threads per 32-element block, 8 elements (one 16-byte packed run)
+  // each; the block maximum is taken over the four lanes
+  for (int b = tid >> 2; b < m.d / 32; b += 64) {
+    const int j = tid & 3;
+    const u32x4_t w = *(const u32x4_t*)(p.f + xpk_index(row, 32 * b + 8 * j));
+    float v[8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const u32x4_t w = *(const u32x4_t*)(p.f + xpk_index(row, 32 * b + 8 * h));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * h + 2 * e] = lo_bf(w[e]);
-        v[8 * h + 2 * e + 1] = hi_bf(w[e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = lo_bf(w[e]);
+      v[2 * e + 1] = hi_bf(w[e]);
     }
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     const int e = mx_shared_exp(amax, 8);
     const float inv = ldexpf(1.f, -e);
-    uint32_t words[8];
+    uint32_t words[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 2; ++i)
       words[i] = e4m3_code(v[4 * i] * inv) | (e4m3_code(v[4 * i + 1] * inv) << 8) |
                  (e4m3_code(v[4 * i + 2] * inv) << 16) | (e4m3_code(v[4 * i + 3] * inv) << 24);
-    u32x4_t* dst = (u32x4_t*)(p.xq + (size_t)row * m.d + 32 * b);
-    dst[0] = u32x4_t{words[0], words[1], words[2], words[3]};
-    dst[1] = u32x4_t{words[4], words[5], words[6], words[7]};
-    p.xs[(size_t)row * (m.d / 32) + b] = (uint8_t)(e + 127);
+    *(u32x2_t*)(p.xq + (size_t)row * m.d + 32 * b + 8 * j) = u32x2_t{words[0], words[1]};
+    if (j == 0) p.xs[(size_t)row * (m.d / 32) + b] = (uint8_t)(e + 127);
   }
   // softmax over the routed experts (thread t holds expert t; E <= 256)
   float mx = wave_max(r);
@@ -256,17 +256,29 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
       }
       n = m.rows;
     } else {
-      const int total = m.rows * m.top_k;         // <= 256 entries, row-major (row, rank)
-      for (int c = 0; c < total; c += 64) {
-        const int idx = c + lane;
-        const bool hit = idx < total && p.ro.ids[idx] == e;
+      // the (row, rank) table, <= 256 entries row-major: every id and weight is loaded at once
+      // (entries past the table read zeros and are masked by the index test)
+      const int total = m.rows * m.top_k;
+      const __amdgpu_buffer_rsrc_t ir = make_rsrc(p.ro.ids, (uint32_t)total * 4u);
+      const __amdgpu_buffer_rsrc_t wtr = make_rsrc(p.ro.wts, (uint32_t)total * 4u);
+      int idv[4];
+      float wv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        idv[c] = __builtin_amdgcn_raw_buffer_load_b32(ir, (64 * c + lane) * 4, 0, 0);
+        wv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wtr, (64 * c + lane) * 4, 0, 0));
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int idx = 64 * c + lane;
+        const bool hit = idx < total && idv[c] == e;
         const unsigned long long mask = __ballot(hit);
         if (hit) {
           const int pos = n + __popcll(mask & ((1ull << lane) - 1));
           const int i = idx / m.top_k;
           s_row[pos] = i;
           s_slot[pos] = i * m.NS + idx % m.top_k;
-          s_w[pos] = p.ro.wts[idx];
+          s_w[pos] = wv[c];
         }
         n += __popcll(mask);
       }
