@@ -134,6 +134,9 @@ struct Route {
   int* ids;        // [32][top_k] expert of each rank, by (probability desc, id asc)
   float* wts;      // [32][top_k] its probability (the mixing weight)
   int* hits;       // [n_layers] running count of distinct experts per layer (statistics)
+  int* n_hit;      // number of distinct routed experts some row selected ...
+  int* list;       // ... and their ids, ascending (256 entries)
+  int* done;       // rows routed so far in this launch (left zero)
 };
 
 struct RouteP {
@@ -197,21 +200,50 @@ __global__ __launch_bounds__(256) void moe_route_kernel(RouteP p) {
   const float pr = ex / sum;
   s_p[tid] = has ? pr : -1.f;
   __syncthreads();
-  if (!has) return;
-  int rank = 0;
-  const f32x4_t* sp4 = (const f32x4_t*)s_p;
+  if (has) {
+    int rank = 0;
+    const f32x4_t* sp4 = (const f32x4_t*)s_p;
 #pragma unroll 8
-  for (int e4 = 0; e4 < m.E / 4; ++e4) {
-    const f32x4_t q = sp4[e4];
+    for (int e4 = 0; e4 < m.E / 4; ++e4) {
+      const f32x4_t q = sp4[e4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * e4 + i;
-      rank += (q[i] > pr || (q[i] == pr && e < tid)) ? 1 : 0;
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * e4 + i;
+        rank += (q[i] > pr || (q[i] == pr && e < tid)) ? 1 : 0;
+      }
+    }
+    if (rank < m.top_k) {   // agent-scope stores: the last workgroup below reads them
+      __hip_atomic_store(&p.ro.ids[row * m.top_k + rank], tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      store_coherent(&p.ro.wts[row * m.top_k + rank], pr);
     }
   }
-  if (rank < m.top_k) {
-    p.ro.ids[row * m.top_k + rank] = tid;
-    p.ro.wts[row * m.top_k + rank] = pr;
+  // The last row's workgroup lists the distinct experts hit, ascending, so that the expert
+  // kernels can give their lowest-numbered workgroups to them and let the others exit at once.
+  __shared__ int s_last;
+  __shared__ uint32_t s_bits[8];
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) s_last = atomic_add_agent(p.ro.done, 1) == m.rows - 1;
+  if (tid < 8) s_bits[tid] = 0u;
+  __syncthreads();
+  if (!s_last) return;
+  const int total = m.rows * m.top_k;   // <= 256
+  if (tid < total) {
+    const int e = __hip_atomic_load(&p.ro.ids[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    atomicOr(&s_bits[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  const bool hit = (s_bits[tid >> 5] >> (tid & 31)) & 1u;      // tid < 256 covers every expert
+  const unsigned long long mask = __ballot(hit);
+  __shared__ int s_cnt[4];
+  if ((tid & 63) == 0) s_cnt[tid >> 6] = __popcll(mask);
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < (tid >> 6); ++w) before += s_cnt[w];
+  if (hit) p.ro.list[before + __popcll(mask & ((1ull << (tid & 63)) - 1ull))] = tid;
+  if (tid == 0) {
+    *p.ro.n_hit = ((s_cnt[0] + s_cnt[1]) + s_cnt[2]) + s_cnt[3];
+    store_agent(p.ro.done, 0);
   }
 }
 
@@ -237,11 +269,21 @@ struct ExpP {
 // to the expert (row order, from the top-k table; every row for a shared expert); a workgroup
 // whose expert no row chose exits before touching its weights.  It then runs 4 row groups x up
 // to 2 groups of 16 rows, K in steps of 128, PF weight steps in flight.
-template <int UP>
+// PF: steps of 128 columns in flight per wave
+template <int UP, int PF>
 __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   const MoeDims& m = p.m;
-  const int e = blockIdx.x / p.Q, q = blockIdx.x % p.Q;
+  // workgroup slots: the shared experts first, then the routed experts some row selected (in
+  // the route kernel's list); slots past them exit at once
+  const int slot_e = blockIdx.x / p.Q, q = blockIdx.x % p.Q;
+  int e;
+  if (slot_e < m.S) {
+    e = m.E + slot_e;
+  } else {
+    if (slot_e - m.S >= *p.ro.n_hit) return;
+    e = p.ro.list[slot_e - m.S];
+  }
   const int lane = threadIdx.x;
   __shared__ int s_n;
   __shared__ int s_row[32], s_slot[32];
@@ -321,7 +363,6 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[cg][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // ring of PF steps: weights (4 row groups) and the block rows' activations (2 column groups)
-  constexpr int PF = 4;
   u32x4_t wa[PF][4], blo[PF][2], bhi[PF][2];
   uint32_t wsc[PF][4], bsc[PF][2];
   auto fetch = [&](int u, int s) {
@@ -419,6 +460,9 @@ MoeWs moe_ws_layout(const MoeDims& m, char* base) {
   w.ro.ids = (int*)take((size_t)kMaxRows * 8 * 4);
   w.ro.wts = (float*)take((size_t)kMaxRows * 8 * 4);
   w.ro.hits = (int*)take((size_t)kMaxLayers * 4);
+  w.ro.n_hit = (int*)take(4);
+  w.ro.list = (int*)take(256 * 4);
+  w.ro.done = (int*)take(4);
   w.total = off;
   return w;
 }
@@ -522,7 +566,7 @@ int moe_ffn(const MoeDims& m, int layer, const void* f, const void* router_packe
   up.as = w.as;
   up.y = nullptr;
   up.cont_dev = cont_dev;
-  hipLaunchKernelGGL(moe_expert_kernel<1>, dim3(ET * up.Q), dim3(64), 0, st, up);
+  hipLaunchKernelGGL((moe_expert_kernel<1, 4>), dim3(ET * up.Q), dim3(64), 0, st, up);
   DLM_HIP(hipGetLastError());
   // 4. down (weighted, per slot)
   ExpP dn = up;
@@ -538,7 +582,7 @@ int moe_ffn(const MoeDims& m, int layer, const void* f, const void* router_packe
   dn.aq = nullptr;
   dn.as = nullptr;
   dn.y = w.y;
-  hipLaunchKernelGGL(moe_expert_kernel<0>, dim3(ET * dn.Q), dim3(64), 0, st, dn);
+  hipLaunchKernelGGL((moe_expert_kernel<0, 4>), dim3(ET * dn.Q), dim3(64), 0, st, dn);
   DLM_HIP(hipGetLastError());
   PartialSrc ps{};
   ps.slots = w.y;
