@@ -4,14 +4,17 @@
 //   1. router logits r = f W_r^T (bf16 stream-K GEMM, f32 out);
 //   2. route: softmax over the E routed experts in f32, top-k by (probability desc, expert id
 //      asc), the selected probabilities are the mixing weights (not renormalised); shared
-//      experts take every row with weight 1; per-expert row lists in row order; the list of
-//      experts hit, in id order.  The same launch quantises f to MXFP8 (e4m3 codes, one e8m0
-//      scale per 32 along d);
+//      experts take every row with weight 1.  The same launch quantises f to MXFP8 (e4m3
+//      codes, one e8m0 scale per 32 along d);
 //   3. up: per hit expert and 64 interleaved gate/up rows, act = silu(gate) * up over its rows
 //      with v_mfma_scale_f32_16x16x128_f8f6f4 (A = MXFP4 weights, B = MXFP8 activations), the
 //      32 act values of a row quantised to MXFP8 in the epilogue;
 //   4. down: per hit expert and 64 output columns, y = act W_d^T, scaled by the row's mixing
 //      weight and stored to the row's slot; the next RMSNorm adds the slots in order.
+// The expert kernels read the whole top-k table: it gives each workgroup its expert's rows,
+// in row order, and, in the up kernel, the expert itself (the experts hit, in id order, take
+// the lowest workgroup slots after the shared ones); the up kernel leaves that list for the
+// down kernel.
 // Pages: [ORL-blog] "What shipped" runs routed experts in 4-bit floating point on the
 // matrix units; the MI355X form uses the OCP microscaling formats (MXFP4 weights, MXFP8
 // activations), which the scaled matrix-core instruction consumes directly.
@@ -135,8 +138,7 @@ struct Route {
   float* wts;      // [32][top_k] its probability (the mixing weight)
   int* hits;       // [n_layers] running count of distinct experts per layer (statistics)
   int* n_hit;      // number of distinct routed experts some row selected ...
-  int* list;       // ... and their ids, ascending (256 entries)
-  int* done;       // rows routed so far in this launch (left zero)
+  int* list;       // ... and their ids, ascending (256 entries); both written by the up kernel
 };
 
 struct RouteP {
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(RouteP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   const MoeDims& m = p.m;
   const int row = blockIdx.x, tid = threadIdx.x;
-  __shared__ __align__(16) float s_p[256];
+  __shared__ __align__(16) unsigned long long s_key[256];
   __shared__ float red[4];
   const bool has = tid < m.E;
   const float r = has ? p.logits[(size_t)row * m.E + tid] : -INFINITY;   // issued before the MX work
@@ -198,52 +200,22 @@ __global__ __launch_bounds__(256) void moe_route_kernel(RouteP p) {
   __syncthreads();
   sum = ((red[0] + red[1]) + red[2]) + red[3];
   const float pr = ex / sum;
-  s_p[tid] = has ? pr : -1.f;
+  // rank of expert tid = number of experts with a larger key, where the key is the
+  // probability's bits (non-negative floats order as unsigned integers; not-a-number ranks
+  // lowest) above 255 - id: key order is (probability desc, id asc), keys are distinct, so the
+  // ranks are a permutation and one unsigned compare per expert decides
+  const uint32_t pbits = pr >= 0.f ? __float_as_uint(pr) : 0u;
+  const unsigned long long key = ((unsigned long long)pbits << 8) | (unsigned long long)(255 - tid);
+  s_key[tid] = has ? key : 0ull;
   __syncthreads();
   if (has) {
     int rank = 0;
-    const f32x4_t* sp4 = (const f32x4_t*)s_p;
 #pragma unroll 8
-    for (int e4 = 0; e4 < m.E / 4; ++e4) {
-      const f32x4_t q = sp4[e4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * e4 + i;
-        rank += (q[i] > pr || (q[i] == pr && e < tid)) ? 1 : 0;
-      }
+    for (int e = 0; e < m.E; ++e) rank += s_key[e] > key ? 1 : 0;
+    if (rank < m.top_k) {
+      p.ro.ids[row * m.top_k + rank] = tid;
+      p.ro.wts[row * m.top_k + rank] = pr;
     }
-    if (rank < m.top_k) {   // agent-scope stores: the last workgroup below reads them
-      __hip_atomic_store(&p.ro.ids[row * m.top_k + rank], tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      store_coherent(&p.ro.wts[row * m.top_k + rank], pr);
-    }
-  }
-  // The last row's workgroup lists the distinct experts hit, ascending, so that the expert
-  // kernels can give their lowest-numbered workgroups to them and let the others exit at once.
-  __shared__ int s_last;
-  __shared__ uint32_t s_bits[8];
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) s_last = atomic_add_agent(p.ro.done, 1) == m.rows - 1;
-  if (tid < 8) s_bits[tid] = 0u;
-  __syncthreads();
-  if (!s_last) return;
-  const int total = m.rows * m.top_k;   // <= 256
-  if (tid < total) {
-    const int e = __hip_atomic_load(&p.ro.ids[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    atomicOr(&s_bits[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-  const bool hit = (s_bits[tid >> 5] >> (tid & 31)) & 1u;      // tid < 256 covers every expert
-  const unsigned long long mask = __ballot(hit);
-  __shared__ int s_cnt[4];
-  if ((tid & 63) == 0) s_cnt[tid >> 6] = __popcll(mask);
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < (tid >> 6); ++w) before += s_cnt[w];
-  if (hit) p.ro.list[before + __popcll(mask & ((1ull << (tid & 63)) - 1ull))] = tid;
-  if (tid == 0) {
-    *p.ro.n_hit = ((s_cnt[0] + s_cnt[1]) + s_cnt[2]) + s_cnt[3];
-    store_agent(p.ro.done, 0);
   }
 }
 
@@ -274,23 +246,22 @@ template <int UP, int PF>
 __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   const MoeDims& m = p.m;
-  // workgroup slots: the shared experts first, then the routed experts some row selected (in
-  // the route kernel's list); slots past them exit at once
+  // workgroup slots: the shared experts first, then the routed experts some row selected, in
+  // id order.  The up kernel finds a slot's expert from the routing table (slots past the
+  // experts hit exit once they have read it) and its first quad's workgroups write the list of
+  // experts hit and their count for the down kernel, whose spare slots exit after one load.
   const int slot_e = blockIdx.x / p.Q, q = blockIdx.x % p.Q;
-  int e;
-  if (slot_e < m.S) {
-    e = m.E + slot_e;
-  } else {
-    if (slot_e - m.S >= *p.ro.n_hit) return;
-    e = p.ro.list[slot_e - m.S];
-  }
+  if (!UP && slot_e >= m.S && slot_e - m.S >= *p.ro.n_hit) return;
   const int lane = threadIdx.x;
   __shared__ int s_n;
   __shared__ int s_row[32], s_slot[32];
   __shared__ float s_w[32];
+  __shared__ uint32_t s_hb[8];
+  int e;
   {
     int n = 0;
-    if (e >= m.E) {
+    if (slot_e < m.S) {
+      e = m.E + slot_e;
       if (lane < m.rows) {
         s_row[lane] = lane;
         s_slot[lane] = lane * m.NS + m.top_k + (e - m.E);
@@ -309,6 +280,37 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
       for (int c = 0; c < 4; ++c) {
         idv[c] = __builtin_amdgcn_raw_buffer_load_b32(ir, (64 * c + lane) * 4, 0, 0);
         wv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wtr, (64 * c + lane) * 4, 0, 0));
+      }
+      if (UP) {
+        // this slot's expert: the (slot_e - S)-th of the experts hit, in id order, from a
+        // bitmap of the table (routed ids are < E <= 256)
+        if (lane < 8) s_hb[lane] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (64 * c + lane < total) atomicOr(&s_hb[idv[c] >> 5], 1u << (idv[c] & 31));
+        __syncthreads();
+        int j = slot_e - m.S, word = -1, n_hit = 0;
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t x = s_hb[i];
+          const int c = __popc(x);
+          if (word < 0) {
+            if (j < c) { word = i; bits = x; }
+            else j -= c;
+          }
+          n_hit += c;
+        }
+        if (word < 0) return;             // fewer experts hit than this slot (uniform)
+        for (int t = 0; t < j; ++t) bits &= bits - 1u;
+        e = 32 * word + __builtin_ctz(bits);
+        if (q == 0 && lane == 0) {
+          p.ro.list[slot_e - m.S] = e;
+          if (slot_e - m.S == n_hit - 1) *p.ro.n_hit = n_hit;
+        }
+      } else {
+        e = p.ro.list[slot_e - m.S];
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -462,7 +464,6 @@ MoeWs moe_ws_layout(const MoeDims& m, char* base) {
   w.ro.hits = (int*)take((size_t)kMaxLayers * 4);
   w.ro.n_hit = (int*)take(4);
   w.ro.list = (int*)take(256 * 4);
-  w.ro.done = (int*)take(4);
   w.total = off;
   return w;
 }

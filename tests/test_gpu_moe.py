@@ -73,10 +73,17 @@ def _e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return s * np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
 
 
-def test_moe_stages_one_layer():
+MOE_ROUTING_SHAPE = dict(name="moe-1l-e256", n_layers=1, d=2048, hq=16, hkv=4, head_dim=128, n_experts=256,
+                         expert_ffn=512, top_k=8, n_shared=1)
+
+
+@pytest.mark.parametrize("kw", [dict(name="moe-1l", n_layers=1), MOE_ROUTING_SHAPE], ids=["small", "e256-top8"])
+def test_moe_stages_one_layer(kw):
     """One MoE layer, round 0: router logits, MXFP8 input codes, the top-k routing, the per-row
-    output slots, each against the oracle's own step from the oracle's input."""
-    s = _moe_shape(name="moe-1l", n_layers=1)
+    output slots, each against the oracle's own step from the oracle's input.  The second case
+    has the MoE model's routing shape (256 routed experts, top-8, d 2048)."""
+    s = _moe_shape(**kw)
+    _say(f"moe stages {s.name}: d={s.d} E={s.n_experts} top{s.top_k}")
     dlm, m, w = _model(s, 1234, cap=96)
     prompt = synth.prompt_ids(s, 32, 1234)
     m.set_len(0)
@@ -130,10 +137,13 @@ def test_moe_stages_one_layer():
     aq = _e4m3_decode(m.view("moe_aq", (32 * NS, F), torch.uint8).cpu().numpy())
     asc = m.view("moe_as", (32 * NS, F // 32), torch.uint8).cpu().numpy().astype(np.float64)
     g_act = (aq.reshape(-1, F // 32, 32) * np.exp2(asc - 127)[..., None]).reshape(-1, F)
+    dec = {}
     for i in range(B):
         for j in range(NS):
             e = g_ids[i, j] if j < s.top_k else E + (j - s.top_k)
-            wg, wu, wd = (oracle.mxfp4_decode(*w.expert(0, e, which)) for which in ("wg", "wu", "wd"))
+            if e not in dec:
+                dec[e] = [oracle.mxfp4_decode(*w.expert(0, e, which)) for which in ("wg", "wu", "wd")]
+            wg, wu, wd = dec[e]
             # act in MXFP8: the oracle's quantisation of its own act; codes differ only where the
             # f32 and f64 act values fall on different sides of an e4m3 rounding boundary
             act = oracle.mxfp8_quant_dequant(oracle.block.swiglu(g_x[i] @ wg.T, g_x[i] @ wu.T))

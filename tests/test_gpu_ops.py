@@ -103,6 +103,36 @@ def test_attn_bf16_shapes(L, B, hq, hkv, D):
     _attn_case("bf16", hq, hkv, D, B, L, (L + B + 5 + 31) // 32 * 32, 1236)
 
 
+@pytest.mark.parametrize("L", [100, 1000, 2100])
+def test_attn_bf16_stale_cache_and_workspace(L):
+    """Cache rows past the block and every split slot of the workspace start as NaN and inf
+    (stale contents of a reused cache and workspace): keys past the block and split slots past
+    the prefix's split count must never reach the arithmetic.  The output equals the one
+    computed with clean memory, bit for bit, and the oracle's."""
+    dlm = _dlm()
+    hq, hkv, D, B, cap = 32, 8, 128, 32, 4096
+    _say(f"attn stale cache/workspace L={L} cap={cap}")
+    q = synth.stored_normal(1237, "attn.q", (B, hq, D), 1.0, "bf16")
+    k = synth.stored_normal(1237, "attn.k", (hkv, cap, D), 1.0, "bf16")
+    v = synth.stored_normal(1237, "attn.v", (hkv, cap, D), 1.0, "bf16")
+    k_bad, v_bad = k.copy(), v.copy()
+    k_bad[:, L + B:] = 0x7FC0                    # NaN
+    v_bad[:, L + B:] = 0x7F80                    # +inf
+    k_bad[:, L + B:, ::2] = 0xFF80               # -inf
+    to_vt = lambda a: np.ascontiguousarray(a.reshape(hkv, cap // 32, 32, D).transpose(0, 1, 3, 2))  # noqa: E731
+    ws_bad = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN in every slot
+    out_bad = dlm.block_attn(storage(q, "bf16"), storage(k_bad, "bf16"), storage(to_vt(v_bad), "bf16"), L,
+                             max_prefix_len=cap - B, ws=ws_bad)
+    out = dlm.block_attn(storage(q, "bf16"), storage(k, "bf16"), storage(to_vt(v), "bf16"), L,
+                         max_prefix_len=cap - B)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_bad.float()).all()
+    assert torch.equal(out_bad, out)
+    qf, kf, vf = (oracle.decode_storage(a) for a in (q, k, v))
+    ref = o_attn(qf, kf[:, :L + B], vf[:, :L + B], 1 / math.sqrt(D))
+    np.testing.assert_allclose(out.float().cpu().numpy(), ref, atol=2e-2, rtol=2e-2)
+
+
 @pytest.mark.parametrize("L", [0, 64, 150])
 def test_attn_f32(L):
     _attn_case("f32", 4, 2, 64, 32, L, 256, 1235)
