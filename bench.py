@@ -114,7 +114,7 @@ def run_moe(args, torch, dlm, synth, np):
             sshp = shp[:-1] + (shp[-1] * 2 // 32,)
             dev[f"l{i}.{name}_scale"] = torch.randint(119, 122, sshp, dtype=torch.uint8, device="cuda", generator=gen)
     B = s.block
-    cap = args.prompt + (args.moe_blocks + 2) * B
+    cap = args.prompt + (args.moe_blocks + 4) * B
     model = dlm.Model(s, dev, cap=cap)
     for i in range(s.n_layers):          # decode reads only the packed copies
         for name in ("x_w13", "x_w13_scale", "x_w2", "x_w2_scale"):
@@ -123,11 +123,23 @@ def run_moe(args, torch, dlm, synth, np):
     log(f"moe model built in {time.time() - t0:.1f}s")
     prompt = torch.from_numpy(synth.prompt_ids(s, args.prompt, args.seed))
     rule = dlm.CommitRule.fixed_k(args.k)
+    pipelined = not args.separate_commit
+    bufs = [torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(2)]
     model.set_len(0)
     model.prefill(prompt)
-    model.decode_block(rule)
-    torch.cuda.synchronize()
-    model.set_len(args.prompt)
+    prev = None
+    if pipelined:
+        # as in the dense leg: three warm-up blocks capture every graph the timed loop replays,
+        # and the pending commit pass of the last one lands at [prompt - B, prompt)
+        for i in range(3):
+            model.decode_block_pipelined(rule, prev, bufs[i % 2])
+            prev = bufs[i % 2]
+        torch.cuda.synchronize()
+        model.set_len(args.prompt - B)
+    else:
+        model.decode_block(rule)
+        torch.cuda.synchronize()
+        model.set_len(args.prompt)
     hits = model.view("moe_hits", (s.n_layers,), torch.int32)
     hits.zero_()
     torch.cuda.synchronize()
@@ -136,20 +148,33 @@ def run_moe(args, torch, dlm, synth, np):
     host_tok = torch.empty(args.moe_blocks, B, dtype=torch.int32).pin_memory()
     ev0.record()
     for i in range(args.moe_blocks):
-        model.decode_block(rule)
-        host_tok[i].copy_(model.tokens, non_blocking=True)
+        if pipelined:
+            cur = bufs[1] if prev is bufs[0] else bufs[0]
+            model.decode_block_pipelined(rule, prev, cur)
+            host_tok[i].copy_(cur, non_blocking=True)
+            prev = cur
+        else:
+            model.decode_block(rule)
+            host_tok[i].copy_(model.tokens, non_blocking=True)
     ev1.record()
     torch.cuda.synchronize()
     sec = ev0.elapsed_time(ev1) / 1e3
     R = math.ceil(B / args.k)
     total_hits = int(hits.sum().item())
-    dense = sum(R * moe_dense_pass_bytes(s, args.prompt + B * i, True) +
-                moe_dense_pass_bytes(s, args.prompt + B * i, False) for i in range(args.moe_blocks))
+    if pipelined:
+        # round 0 of a block carries the previous block's commit rows with the same weights; its
+        # expert count is that of the 64-row forward
+        dense = sum(R * moe_dense_pass_bytes(s, args.prompt + B * i, True) for i in range(args.moe_blocks))
+        forwards_per_block = R * s.n_layers
+    else:
+        dense = sum(R * moe_dense_pass_bytes(s, args.prompt + B * i, True) +
+                    moe_dense_pass_bytes(s, args.prompt + B * i, False) for i in range(args.moe_blocks))
+        forwards_per_block = R * s.n_layers + (s.n_layers - 1)
     total = dense + total_hits * moe_expert_bytes(s)
-    forwards_per_block = R * s.n_layers + (s.n_layers - 1)
     out = {"workload": f"MoE 16B-A1B-shaped (20 layers, d 2048, 256 experts of 512 top-8 + 1 shared, MXFP4 "
                        f"experts, MXFP8 activations), bs=1, block 32, fixed k={args.k}, prompt {args.prompt}, "
                        f"{args.moe_blocks * B} new tokens",
+           "commit_pass": "pipelined into the next block's round 0" if pipelined else "separate",
            "tok_s": args.moe_blocks * B / sec, "rounds_s": args.moe_blocks * R / sec,
            "ms_per_block": 1e3 * sec / args.moe_blocks, "hbm_frac": total / sec / HBM_PEAK,
            "mean_experts_hit_per_layer_forward": total_hits / (args.moe_blocks * forwards_per_block),

@@ -508,9 +508,9 @@ static AttnPlan model_attn_plan(const dlm_model* m, const dlm_kv* kv) {
 }
 
 // A round fused with the previous block's commit pass runs 64 rows through the layers: the
-// dense bf16 models with 32-row blocks do so.
+// bf16 models (dense and MoE) with 32-row blocks do so.
 static bool fusable(const dlm_model* m) {
-  return m->d.dtype == DLM_BF16 && !m->d.n_experts && m->d.block == 32;
+  return m->d.dtype == DLM_BF16 && m->d.block == 32;
 }
 
 static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) {
@@ -669,7 +669,9 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     ps = PartialSrc{};
     if (d.n_experts) {
       // the experts' weighted outputs are added into x by the next RMSNorm, slot by slot
-      if ((rc = moe_ffn(moe_dims(d), l, w.xn, pk + m->off_router[l], m->pl_router, pk + m->off_moe[l], w.moe_ws,
+      MoeDims md = moe_dims(d);
+      md.rows = B;
+      if ((rc = moe_ffn(md, l, w.xn, pk + m->off_router[l], m->pl_router, pk + m->off_moe[l], w.moe_ws,
                         w.gemm_ws, cont, &ps, st)))
         return rc;
       continue;

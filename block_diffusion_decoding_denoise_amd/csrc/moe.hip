@@ -48,7 +48,7 @@ size_t moe_layer_packed_bytes(const MoeDims& m) { return (size_t)(m.E + m.S) * m
 
 namespace {
 
-constexpr int kMaxRows = 32;
+constexpr int kMaxRows = 64;       // a round fused with the previous block's commit pass
 constexpr int kMaxExperts = 512;
 constexpr int kMaxLayers = 256;
 
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(RouteP p) {
   // each; the block maximum is taken over the four lanes
   for (int b = tid >> 2; b < m.d / 32; b += 64) {
     const int j = tid & 3;
-    const u32x4_t w = *(const u32x4_t*)(p.f + xpk_index(row, 32 * b + 8 * j));
+    const u32x4_t w = *(const u32x4_t*)(p.f + xpk_index_m(row, 32 * b + 8 * j, m.d));
     float v[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -243,54 +243,59 @@ struct ExpP {
 // to 2 groups of 16 rows, K in steps of 128, PF weight steps in flight.
 // PF: steps of 128 columns in flight per wave
 template <int UP, int PF>
-__global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void moe_expert_kernel(ExpP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   const MoeDims& m = p.m;
   // workgroup slots: the shared experts first, then the routed experts some row selected, in
   // id order.  The up kernel finds a slot's expert from the routing table (slots past the
   // experts hit exit once they have read it) and its first quad's workgroups write the list of
   // experts hit and their count for the down kernel, whose spare slots exit after one load.
+  // a shared expert takes one slot per 32 rows of the block (two for a 64-row fused pass), so
+  // that no shared-expert workgroup makes two passes over its weights
+  const int per = (m.rows + 31) / 32, SV = per * m.S;
   const int slot_e = blockIdx.x / p.Q, q = blockIdx.x % p.Q;
-  if (!UP && slot_e >= m.S && slot_e - m.S >= *p.ro.n_hit) return;
+  if (!UP && slot_e >= SV && slot_e - SV >= *p.ro.n_hit) return;
   const int lane = threadIdx.x;
   __shared__ int s_n;
-  __shared__ int s_row[32], s_slot[32];
-  __shared__ float s_w[32];
+  __shared__ int s_row[kMaxRows], s_slot[kMaxRows];
+  __shared__ float s_w[kMaxRows];
   __shared__ uint32_t s_hb[8];
   int e;
   {
     int n = 0;
-    if (slot_e < m.S) {
-      e = m.E + slot_e;
-      if (lane < m.rows) {
-        s_row[lane] = lane;
-        s_slot[lane] = lane * m.NS + m.top_k + (e - m.E);
+    if (slot_e < SV) {
+      e = m.E + slot_e / per;
+      const int r0 = 32 * (slot_e % per);
+      if (lane < 32 && r0 + lane < m.rows) {
+        s_row[lane] = r0 + lane;
+        s_slot[lane] = (r0 + lane) * m.NS + m.top_k + (e - m.E);
         s_w[lane] = 1.f;
       }
-      n = m.rows;
+      n = max(0, min(32, m.rows - r0));
     } else {
-      // the (row, rank) table, <= 256 entries row-major: every id and weight is loaded at once
+      // the (row, rank) table, <= 512 entries row-major: every id and weight is loaded at once
       // (entries past the table read zeros and are masked by the index test)
+      constexpr int TC = kMaxRows * 8 / 64;      // 64-entry chunks of the largest table
       const int total = m.rows * m.top_k;
       const __amdgpu_buffer_rsrc_t ir = make_rsrc(p.ro.ids, (uint32_t)total * 4u);
       const __amdgpu_buffer_rsrc_t wtr = make_rsrc(p.ro.wts, (uint32_t)total * 4u);
-      int idv[4];
-      float wv[4];
+      int idv[TC];
+      float wv[TC];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < TC; ++c) {
         idv[c] = __builtin_amdgcn_raw_buffer_load_b32(ir, (64 * c + lane) * 4, 0, 0);
         wv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wtr, (64 * c + lane) * 4, 0, 0));
       }
       if (UP) {
-        // this slot's expert: the (slot_e - S)-th of the experts hit, in id order, from a
+        // this slot's expert: the (slot_e - SV)-th of the experts hit, in id order, from a
         // bitmap of the table (routed ids are < E <= 256)
         if (lane < 8) s_hb[lane] = 0u;
         __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < TC; ++c)
           if (64 * c + lane < total) atomicOr(&s_hb[idv[c] >> 5], 1u << (idv[c] & 31));
         __syncthreads();
-        int j = slot_e - m.S, word = -1, n_hit = 0;
+        int j = slot_e - SV, word = -1, n_hit = 0;
         uint32_t bits = 0u;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -306,14 +311,14 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
         for (int t = 0; t < j; ++t) bits &= bits - 1u;
         e = 32 * word + __builtin_ctz(bits);
         if (q == 0 && lane == 0) {
-          p.ro.list[slot_e - m.S] = e;
-          if (slot_e - m.S == n_hit - 1) *p.ro.n_hit = n_hit;
+          p.ro.list[slot_e - SV] = e;
+          if (slot_e - SV == n_hit - 1) *p.ro.n_hit = n_hit;
         }
       } else {
-        e = p.ro.list[slot_e - m.S];
+        e = p.ro.list[slot_e - SV];
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < TC; ++c) {
         const int idx = 64 * c + lane;
         const bool hit = idx < total && idv[c] == e;
         const unsigned long long mask = __ballot(hit);
@@ -329,113 +334,117 @@ __global__ __launch_bounds__(64) void moe_expert_kernel(ExpP p) {
     }
     if (lane == 0) {
       s_n = n;
-      if (UP && q == 0 && n > 0) atomicAdd(&p.ro.hits[p.layer], 1);
+      if (UP && q == 0 && n > 0 && (slot_e >= SV || slot_e % per == 0)) atomicAdd(&p.ro.hits[p.layer], 1);
     }
   }
   __syncthreads();
   const int n = s_n;
   if (n == 0) return;
   const int K = 128 * p.S;
-  const bool two = n > 16;
-  int col[2], brow[2], slot[2];
-#pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
-    col[cg] = 16 * cg + (lane & 15);
-    brow[cg] = -1;
-    slot[cg] = -1;
-    if (col[cg] < n) {
-      slot[cg] = s_slot[col[cg]];
-      brow[cg] = p.b_by_slot ? slot[cg] : s_row[col[cg]];
-    }
-  }
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + e * p.w_stride + (size_t)q * p.S * 4096, (uint32_t)p.S * 4096u);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.ws + e * p.s_stride + (size_t)q * p.S * 256, (uint32_t)p.S * 256u);
-  const int n_brows = p.b_by_slot ? 32 * m.NS : 32;
+  const int n_brows = p.b_by_slot ? m.rows * m.NS : m.rows;
   const __amdgpu_buffer_rsrc_t br = make_rsrc(p.bq, (uint32_t)(n_brows * K));
   const __amdgpu_buffer_rsrc_t bsr = make_rsrc(p.bs, (uint32_t)(n_brows * (K / 32)));
-  uint32_t bo[2], bso[2];
+  // up to 32 of the expert's rows per pass over the weights (two column groups of 16); a routed
+  // expert with more rows (only in a 64-row fused pass) makes a second pass, from L2
+  for (int r0 = 0; r0 < n; r0 += 32) {
+    const bool two = n - r0 > 16;
+    int col[2], brow[2], slot[2];
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
-    bo[cg] = brow[cg] >= 0 ? (uint32_t)(brow[cg] * K + 16 * (lane >> 4)) : 0x80000000u;
-    bso[cg] = brow[cg] >= 0 ? (uint32_t)(brow[cg] * (K / 32) + (lane >> 4)) : 0x80000000u;
-  }
-  f32x4_t acc[2][4];
-#pragma unroll
-  for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[cg][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // ring of PF steps: weights (4 row groups) and the block rows' activations (2 column groups)
-  u32x4_t wa[PF][4], blo[PF][2], bhi[PF][2];
-  uint32_t wsc[PF][4], bsc[PF][2];
-  auto fetch = [&](int u, int s) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      wa[u][g] = bload16_nt(wr, (uint32_t)((s * 4 + g) * 64 + lane) * 16u);
-      wsc[u][g] = bload_u8(sr, (uint32_t)((s * 4 + g) * 64 + lane));
+    for (int cg = 0; cg < 2; ++cg) {
+      col[cg] = r0 + 16 * cg + (lane & 15);
+      brow[cg] = -1;
+      slot[cg] = -1;
+      if (col[cg] < n) {
+        slot[cg] = s_slot[col[cg]];
+        brow[cg] = p.b_by_slot ? slot[cg] : s_row[col[cg]];
+      }
     }
+    uint32_t bo[2], bso[2];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      bo[cg] = brow[cg] >= 0 ? (uint32_t)(brow[cg] * K + 16 * (lane >> 4)) : 0x80000000u;
+      bso[cg] = brow[cg] >= 0 ? (uint32_t)(brow[cg] * (K / 32) + (lane >> 4)) : 0x80000000u;
+    }
+    f32x4_t acc[2][4];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[cg][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // ring of PF steps: weights (4 row groups) and the block rows' activations (2 column groups)
+    u32x4_t wa[PF][4], blo[PF][2], bhi[PF][2];
+    uint32_t wsc[PF][4], bsc[PF][2];
+    auto fetch = [&](int u, int s) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        wa[u][g] = bload16_nt(wr, (uint32_t)((s * 4 + g) * 64 + lane) * 16u);
+        wsc[u][g] = bload_u8(sr, (uint32_t)((s * 4 + g) * 64 + lane));
+      }
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        if (cg == 1 && !two) break;
+        const uint32_t off = s < p.S ? bo[cg] + 128u * s : 0x80000000u;
+        blo[u][cg] = bload16(br, off);
+        bhi[u][cg] = bload16(br, off + 64u);
+        bsc[u][cg] = bload_u8(bsr, s < p.S ? bso[cg] + 4u * s : 0x80000000u);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u) fetch(u, u);
+    for (int s0 = 0; s0 < p.S; s0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int s = s0 + u;
+        if (s < p.S) {
+#pragma unroll
+          for (int cg = 0; cg < 2; ++cg) {
+            if (cg == 1 && !two) break;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              acc[cg][g] = mfma_mx(wa[u][g], blo[u][cg], bhi[u][cg], (int)wsc[u][g], (int)bsc[u][cg], acc[cg][g]);
+          }
+        }
+        fetch(u, s + PF);
+      }
+    }
+    // epilogue.  acc[cg][g][r] = D[row 64q + 16g + 4(l/16) + r][column col[cg]]
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) {
       if (cg == 1 && !two) break;
-      const uint32_t off = s < p.S ? bo[cg] + 128u * s : 0x80000000u;
-      blo[u][cg] = bload16(br, off);
-      bhi[u][cg] = bload16(br, off + 64u);
-      bsc[u][cg] = bload_u8(bsr, s < p.S ? bso[cg] + 4u * s : 0x80000000u);
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < PF; ++u) fetch(u, u);
-  for (int s0 = 0; s0 < p.S; s0 += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int s = s0 + u;
-      if (s < p.S) {
-#pragma unroll
-        for (int cg = 0; cg < 2; ++cg) {
-          if (cg == 1 && !two) break;
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            acc[cg][g] = mfma_mx(wa[u][g], blo[u][cg], bhi[u][cg], (int)wsc[u][g], (int)bsc[u][cg], acc[cg][g]);
-        }
-      }
-      fetch(u, s + PF);
-    }
-  }
-  // epilogue.  acc[cg][g][r] = D[row 64q + 16g + 4(l/16) + r][column col[cg]]
-#pragma unroll
-  for (int cg = 0; cg < 2; ++cg) {
-    if (cg == 1 && !two) break;
-    const bool valid = col[cg] < n;
-    if (UP) {
-      // rows 2i / 2i + 1 are gate / up of intermediate column i = 32q + 8g + 2(l/16) + {0, 1}
-      float act[4][2];
-      float amax = 0.f;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float gt = acc[cg][g][2 * h], up = acc[cg][g][2 * h + 1];
-          act[g][h] = gt / (1.0f + expf(-gt)) * up;
-          amax = fmaxf(amax, fabsf(act[g][h]));
-        }
-      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      const int ex = mx_shared_exp(amax, 8);
-      const float inv = ldexpf(1.f, -ex);
-      if (valid) {
-        uint8_t* dst = p.aq + (size_t)slot[cg] * m.F + 32 * q + 2 * (lane >> 4);
+      const bool valid = col[cg] < n;
+      if (UP) {
+        // rows 2i / 2i + 1 are gate / up of intermediate column i = 32q + 8g + 2(l/16) + {0, 1}
+        float act[4][2];
+        float amax = 0.f;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          *(uint16_t*)(dst + 8 * g) = (uint16_t)(e4m3_code(act[g][0] * inv) | (e4m3_code(act[g][1] * inv) << 8));
-        if ((lane >> 4) == 0) p.as[(size_t)slot[cg] * (m.F / 32) + q] = (uint8_t)(ex + 127);
-      }
-    } else if (valid) {
-      const float wgt = s_w[col[cg]];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t o;
+          for (int h = 0; h < 2; ++h) {
+            const float gt = acc[cg][g][2 * h], up = acc[cg][g][2 * h + 1];
+            act[g][h] = gt / (1.0f + expf(-gt)) * up;
+            amax = fmaxf(amax, fabsf(act[g][h]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int ex = mx_shared_exp(amax, 8);
+        const float inv = ldexpf(1.f, -ex);
+        if (valid) {
+          uint8_t* dst = p.aq + (size_t)slot[cg] * m.F + 32 * q + 2 * (lane >> 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = wgt * acc[cg][g][r];
-        *(f32x4_t*)(p.y + (size_t)slot[cg] * m.d + 64 * q + 16 * g + 4 * (lane >> 4)) = o;
+          for (int g = 0; g < 4; ++g)
+            *(uint16_t*)(dst + 8 * g) = (uint16_t)(e4m3_code(act[g][0] * inv) | (e4m3_code(act[g][1] * inv) << 8));
+          if ((lane >> 4) == 0) p.as[(size_t)slot[cg] * (m.F / 32) + q] = (uint8_t)(ex + 127);
+        }
+      } else if (valid) {
+        const float wgt = s_w[col[cg]];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = wgt * acc[cg][g][r];
+          *(f32x4_t*)(p.y + (size_t)slot[cg] * m.d + 64 * q + 16 * g + 4 * (lane >> 4)) = o;
+        }
       }
     }
   }
@@ -567,7 +576,8 @@ int moe_ffn(const MoeDims& m, int layer, const void* f, const void* router_packe
   up.as = w.as;
   up.y = nullptr;
   up.cont_dev = cont_dev;
-  hipLaunchKernelGGL((moe_expert_kernel<1, 4>), dim3(ET * up.Q), dim3(64), 0, st, up);
+  const int slots = m.E + (m.rows + 31) / 32 * m.S;   // shared experts: one slot per 32 rows
+  hipLaunchKernelGGL((moe_expert_kernel<1, 4>), dim3(slots * up.Q), dim3(64), 0, st, up);
   DLM_HIP(hipGetLastError());
   // 4. down (weighted, per slot)
   ExpP dn = up;
@@ -583,7 +593,7 @@ int moe_ffn(const MoeDims& m, int layer, const void* f, const void* router_packe
   dn.aq = nullptr;
   dn.as = nullptr;
   dn.y = w.y;
-  hipLaunchKernelGGL((moe_expert_kernel<0, 4>), dim3(ET * dn.Q), dim3(64), 0, st, dn);
+  hipLaunchKernelGGL((moe_expert_kernel<0, 4>), dim3(slots * dn.Q), dim3(64), 0, st, dn);
   DLM_HIP(hipGetLastError());
   PartialSrc ps{};
   ps.slots = w.y;

@@ -84,6 +84,41 @@ def test_pipelined_bitexact_bf16(shape, seed, prompt_len, n_blocks, rule_args):
     assert all(torch.equal(a, b) for a, b in zip(k1, k2))
 
 
+MOE_SMALL = synth.small_shape(synth.MOE16B, name="moe-small-pipelined", n_layers=2, d=256, hq=4, hkv=2, head_dim=64,
+                              vocab=1000, n_experts=32, expert_ffn=128, top_k=4, n_shared=1)
+# the MoE model's per-layer shapes (256 experts, top-8, d 2048), two layers
+MOE_E256 = synth.small_shape(synth.MOE16B, name="moe-e256-2-layers", n_layers=2, vocab=4096)
+
+
+@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args", [
+    (MOE_SMALL, 1234, 64, 3, ("fixed_k", 6)),
+    (MOE_SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32)),
+    (MOE_E256, 1236, 64, 3, ("fixed_k", 6)),
+], ids=["moe-small-k6", "moe-small-threshold", "moe-e256-k6"])
+def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args):
+    """MoE models: the 64-row fused pass routes the previous block's commit rows and round 0's
+    rows together (up to 64 rows per expert, shared experts in two slots); every row's routing,
+    expert products and slot outputs are those of the separate passes, so tokens, round states
+    and caches are bitwise equal."""
+    dlm = _dlm()
+    _say(f"pipelined MoE vs separate commit passes: {shape.name} seed {seed} prompt {prompt_len} "
+         f"blocks {n_blocks} rule {rule_args}")
+    from tests.gpu_util import moe_device_weights
+    w = synth.Weights(shape, seed)
+    dev = {n: storage(w[n], "bf16") for n in w.names_dense() if not n.endswith(".router")}
+    dev.update(moe_device_weights(w))
+    m = dlm.Model(shape, dev, cap=prompt_len + 32 * n_blocks)
+    rule = getattr(dlm.CommitRule, rule_args[0])(*rule_args[1:])
+    prompt = synth.prompt_ids(shape, prompt_len, seed)
+    t0, s0, k0, v0 = _run(dlm, m, prompt, n_blocks, rule, pipelined=False)
+    t1, s1, k1, v1 = _run(dlm, m, prompt, n_blocks, rule, pipelined=True)
+    assert s0 == s1
+    assert torch.equal(t0, t1)
+    for l in range(shape.n_layers):
+        assert torch.equal(k0[l], k1[l]), f"layer {l} keys"
+        assert torch.equal(v0[l], v1[l]), f"layer {l} values"
+
+
 def test_pipelined_tiny_fp32_matches_oracle():
     """f32: the pending commit pass runs on its own; tokens and rounds bit-exact with the
     oracle's block loop, and the final cache equal to the oracle's."""
