@@ -314,10 +314,11 @@ int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_
  * and produces the same tokens and cache as dlm_decode_block on each block in turn: the commit
  * pass is the forward of the clean block whose K/V the next block attends to ([ORL-blog]
  * "What shipped"), and nothing in round 0 of the next block depends on it other than those
- * K/V.  For dense bf16 models with block = 32 the commit rows ride along with round 0 as one
- * 64-row forward (rows 0..31: the previous block at positions L .. L + 31; rows 32..63: round
- * 0 at L + 32 .., attending to the prefix, the previous block and each other), so the layer
- * weights stream once for both; other models run the commit pass on its own first.
+ * K/V.  For bf16 models (dense and MoE) with block = 32 the commit rows ride along with round
+ * 0 as one 64-row forward (rows 0..31: the previous block at positions L .. L + 31; rows
+ * 32..63: round 0 at L + 32 .., attending to the prefix, the previous block and each other;
+ * in a MoE layer all 64 rows are routed together), so the layer weights stream once for
+ * both; f32 models run the commit pass on its own first.
  *   prev_tokens must not alias tokens and must hold the previous block's final tokens until
  *   the call's work has run.  The cache must have room for both blocks: L + 2 block <=
  *   max_len at the call (the kernels write no K/V at or past cap).  Other arguments and
