@@ -302,13 +302,17 @@ __global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
   DLM_TRACE_POINT(4);
 }
 
-// merge the splits of (head, query): one workgroup per (query block, head, query), D threads;
-// all partial loads are issued before the arithmetic (at most kMaxSplits splits); splits added
-// in index order
+// merge the splits of (head, query): D / 4 threads per (query block, head, query), each
+// holding 4 output columns (one 8-byte load per split), 256 threads per workgroup; all partial
+// loads are issued before the arithmetic (at most kMaxSplits splits); splits added in index order
 template <int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(AttnP p) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
-  const int qblk = blockIdx.x / (p.hq * p.B), bx = blockIdx.x % (p.hq * p.B);
+  constexpr int TPQ = D / 4, PPW = 256 / TPQ;     // threads per (head, query), pairs per workgroup
+  const int pair = blockIdx.x * PPW + threadIdx.x / TPQ;
+  const int dv = 4 * (threadIdx.x % TPQ);
+  const int qblk = pair / (p.hq * p.B), bx = pair % (p.hq * p.B);
+  if (qblk >= p.nqb) return;
   const int L = (p.len_dev ? *p.len_dev : p.len_host) + 32 * qblk;
   const int N = min(L + p.B, p.cap);
   const int chunk = split_chunk(N, p.nsplit_max);
@@ -317,13 +321,13 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnP p) {
   const int head = bx / p.B, qi = bx % p.B;
   const int G = p.hq / p.hkv;
   const int g = head / G, hh = head % G;
-  const int dv = threadIdx.x;
   constexpr int MAXS = kMaxSplits;
   // branch-free loads: split slots past nsplit use out-of-range buffer offsets (zeros)
   const size_t nrow = (size_t)p.nqb * p.hkv * p.nsplit_max * G * 32;
   const __amdgpu_buffer_rsrc_t mr = make_rsrc(p.part_ml, (uint32_t)(nrow * 8));
   const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.part_o, (uint32_t)(nrow * D * 2));
-  float mv[MAXS], lv[MAXS], ov[MAXS];
+  float mv[MAXS], lv[MAXS];
+  u32x2_t ov[MAXS];
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
     const size_t row = ((((size_t)qblk * p.hkv + g) * p.nsplit_max + s) * G + hh) * 32 + qi;
@@ -331,21 +335,25 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnP p) {
     const u32x2_t mlv = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(mr, ok ? (int)(row * 8) : (int)0x80000000, 0, 0));
     mv[s] = ok ? __uint_as_float(mlv[0]) : -INFINITY;
     lv[s] = __uint_as_float(mlv[1]);
-    ov[s] = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(orr, ok ? (int)((row * D + dv) * 2) : (int)0x80000000, 0, 0));
+    ov[s] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(orr, ok ? (int)((row * D + dv) * 2) : (int)0x80000000, 0, 0));
   }
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) M = fmaxf(M, mv[s]);
-  float num = 0.f, den = 0.f;
+  float num[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
     const float f = mv[s] == -INFINITY ? 0.f : lv[s] * exp2f(mv[s] - M);   // split weight
-    num += f * ov[s];
+    num[0] += f * lo_bf(ov[s][0]);
+    num[1] += f * hi_bf(ov[s][0]);
+    num[2] += f * lo_bf(ov[s][1]);
+    num[3] += f * hi_bf(ov[s][1]);
     den += f;
   }
   const int qr = 32 * qblk + qi;
   const size_t o = p.out_packed ? xpk_index_m(qr, head * D + dv, p.hq * D) : ((size_t)qr * p.hq + head) * D + dv;
-  p.out[o] = f2bf(num / den);
+  // 4 consecutive columns are 8 contiguous bytes in both layouts
+  *(u32x2_t*)(p.out + o) = u32x2_t{pack2bf(num[0] / den, num[1] / den), pack2bf(num[2] / den, num[3] / den)};
 }
 
 // ------------------------------------------------------------------ f32 reference-style path
@@ -451,12 +459,12 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
     if (WPG == 4) launch(attn_bf16_kernel<128, 4>, 256);
     else if (WPG == 2) launch(attn_bf16_kernel<128, 2>, 128);
     else launch(attn_bf16_kernel<128, 1>, 64);
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(nqb * hq * B), dim3(128), 0, st, p);
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((nqb * hq * B + 7) / 8), dim3(256), 0, st, p);
   } else {
     if (WPG == 4) launch(attn_bf16_kernel<64, 4>, 256);
     else if (WPG == 2) launch(attn_bf16_kernel<64, 2>, 128);
     else launch(attn_bf16_kernel<64, 1>, 64);
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(nqb * hq * B), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((nqb * hq * B + 15) / 16), dim3(256), 0, st, p);
   }
   return check_hip(hipGetLastError(), "attn_bf16 launch");
 }
