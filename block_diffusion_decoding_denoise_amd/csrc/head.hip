@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256) void head_f32_kernel(HeadP p) {
 
 // combine: one workgroup (256 threads) per (output row, 256-wide d slice).  Thread c loads
 // chunk c's statistics; the chunk statistics are merged with fixed-order tree reductions, and
-// the pe partials are read 16 chunks at a time so the loads overlap.
+// the pe partials are read 64 chunks at a time so the loads overlap.
 __device__ inline float block_max(float v, float* red) {
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -397,18 +397,23 @@ __global__ __launch_bounds__(256) void head_combine_kernel(HeadP p, int bf16_pat
     p.amax[row] = (fbi >= 0 && fbi < p.V) ? fbi : 0;   // all-NaN rows still name a valid id
   }
   if (!p.pe) return;
-  if (tid < CH) wts[tid] = f / S;
+  wts[tid] = tid < CH ? f / S : 0.f;     // 256 threads: every slot, zero past the chunks
   __syncthreads();
   if (dcol < p.d) {
-    const float* base = p.pe_part + (size_t)k * p.d + dcol;
-    const size_t cstride = (size_t)p.rows_max * p.d;
+    // branch-free buffer loads (chunks past CH read zeros; the host keeps the partial area
+    // below 2^31 bytes)
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(p.pe_part, (uint32_t)((size_t)CH * p.rows_max * p.d * 4));
+    const uint32_t off0 = (uint32_t)(((size_t)k * p.d + dcol) * 4), cstride = (uint32_t)(p.rows_max * p.d * 4);
     float a = 0.f;
-    for (int c0 = 0; c0 < CH; c0 += 16) {
-      float v[16];
+    constexpr int NB = 64;     // partial loads in flight per thread
+    for (int c0 = 0; c0 < CH; c0 += NB) {
+      float v[NB];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = c0 + j < CH ? base[(size_t)(c0 + j) * cstride] : 0.f;
+      for (int j = 0; j < NB; ++j)
+        v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            pr, c0 + j < CH ? (int)(off0 + (uint32_t)(c0 + j) * cstride) : (int)0x80000000, 0, 0));
 #pragma unroll
-      for (int j = 0; j < 16; ++j) a = fmaf(c0 + j < CH ? wts[c0 + j] : 0.f, v[j], a);
+      for (int j = 0; j < NB; ++j) a = fmaf(wts[c0 + j], v[j], a);     // c0 + j < 256
     }
     p.pe[(size_t)row * p.d + dcol] = a;
   }
@@ -446,6 +451,7 @@ int head_launch(int dtype, const void* h, const void* E, const uint8_t* committe
   p.cont_dev = cont_dev;
   if (dtype == DLM_BF16) {
     if ((size_t)V * d * 2 >= (1ull << 31)) return fail(DLM_ERR_SHAPE, "head: embedding of %d x %d too large", V, d);
+    if ((size_t)CH * rows * d * 4 >= (1ull << 31)) return fail(DLM_ERR_SHAPE, "head: %d rows of %d too large", rows, d);
     const int grid = 256;   // n_groups * chunks <= 256, extra workgroups exit
     const int k8 = (d / 32 + 7) / 8;     // k-steps per wave with 8 waves
     const bool dbg = logits_dbg != nullptr;
