@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(MxPackP p) {
 
 // -------------------------------------------------------------------- route + quantise
 struct Route {
-  int* ids;        // [32][top_k] expert of each rank, by (probability desc, id asc)
-  float* wts;      // [32][top_k] its probability (the mixing weight)
+  int* ids;        // [rows][top_k] expert of each rank, by (probability desc, id asc)
+  float* wts;      // [rows][top_k] its probability (the mixing weight)
   int* hits;       // [n_layers] running count of distinct experts per layer (statistics)
   int* n_hit;      // number of distinct routed experts some row selected ...
   int* list;       // ... and their ids, ascending (256 entries); both written by the up kernel
@@ -144,9 +144,9 @@ struct Route {
 struct RouteP {
   MoeDims m;
   const float* logits;     // [rows][E]
-  const uint16_t* f;       // bf16 packed activations, 32 x d
-  uint8_t* xq;             // [32][d] e4m3 codes
-  uint8_t* xs;             // [32][d/32] e8m0
+  const uint16_t* f;       // bf16 packed activations, rows x d in 32-row panels
+  uint8_t* xq;             // [rows][d] e4m3 codes
+  uint8_t* xs;             // [rows][d/32] e8m0
   Route ro;
   const int32_t* cont_dev;
 };
@@ -231,9 +231,9 @@ struct ExpP {
   const uint8_t* bs;       // B operand scales: [rows or slots][K/32]
   int b_by_slot;           // B rows are indexed by slot (down) or by row (up)
   Route ro;
-  uint8_t* aq;             // up: act codes [32 NS][F]
-  uint8_t* as;             // up: act scales [32 NS][F/32]
-  float* y;                // down: [32 NS][d]
+  uint8_t* aq;             // up: act codes [rows NS][F]
+  uint8_t* as;             // up: act scales [rows NS][F/32]
+  float* y;                // down: [rows NS][d]
   const int32_t* cont_dev;
 };
 
