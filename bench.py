@@ -95,6 +95,81 @@ def moe_expert_bytes(s):
     return 2 * F * d // 2 + 2 * F * d // 32 + d * F // 2 + d * F // 32
 
 
+def run_ops(torch, dlm, emb, seed):
+    """The head and attention ops alone at their workload sizes (the head with 32 / 24 / 16 / 0
+    open rows of 32 over the 151,936 x 2560 embedding; attention with 32 / 8 heads of 128, a
+    32-query block, prefix 512 / 4096 / 32768), each call replayed from a captured graph and
+    timed with HIP events; bytes are the algorithmic ones (every embedding or K/V byte once)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    V, d = emb.shape
+    out = {"head": [], "attention": []}
+    # ---- head: rows N(0, 1) normalised to unit RMS, in bf16; committed rows by a seeded permutation
+    h = torch.randn(32, d, device="cuda", generator=g)
+    h = (h / h.pow(2).mean(dim=1, keepdim=True).sqrt()).to(torch.bfloat16)
+    perm = torch.randperm(32, device="cuda", generator=g)
+    ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+    for n_committed in (0, 8, 16, 32):
+        committed = torch.zeros(32, dtype=torch.uint8, device="cuda")
+        committed[perm[:n_committed]] = 1
+        dlm.head_rowstats(h, emb, committed, ws=ws)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(4):
+                dlm.head_rowstats(h, emb, committed, ws=ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / 20
+        m = 32 - n_committed
+        nbytes = V * d * 2 + m * d * 2 + 32 * (4 * 4 + d * 4) if m else 0
+        out["head"].append({"open_rows": m, "us": round(t * 1e6, 2),
+                            "GB_s": round(nbytes / t / 1e9, 1), "frac": round(nbytes / t / HBM_PEAK, 4)})
+    del ws
+    # ---- attention: K/V copies rotated so that at least 512 MiB is cycled (short prefixes would
+    # otherwise sit in the 256 MB memory-side cache)
+    hq, hkv, D, B = 32, 8, 128, 32
+    for L in (512, 4096, 32768):
+        cap = (L + B + 31) // 32 * 32
+        per = 2 * hkv * cap * D * 2
+        n = max(2, -(-(512 << 20) // per))
+        kc = torch.randn(n, hkv, cap, D, device="cuda", generator=g).to(torch.bfloat16)
+        vc = torch.randn(n, hkv, cap // 32, D, 32, device="cuda", generator=g).to(torch.bfloat16)
+        q = torch.randn(B, hq, D, device="cuda", generator=g).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        aws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+        dlm.block_attn(q, kc[0], vc[0], L, out=o, ws=aws)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                dlm.block_attn(q, kc[i], vc[i], L, out=o, ws=aws)
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, 200 // n)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / (reps * n)
+        nbytes = (L + B) * hkv * D * 2 * 2 + 2 * B * hq * D * 2
+        out["attention"].append({"L": L, "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
+                                 "frac": round(nbytes / t / HBM_PEAK, 4), "rotated_copies": n})
+        del kc, vc, aws, graph
+        torch.cuda.empty_cache()
+    log("ops: head " + ", ".join(f"{r['open_rows']} open {r['us']:.0f} us" for r in out["head"]) +
+        "; attention " + ", ".join(f"L={r['L']} {r['us']:.1f} us {r['GB_s']:.0f} GB/s" for r in out["attention"]))
+    return out
+
+
 def run_moe(args, torch, dlm, synth, np):
     """The MoE configuration: bf16 attention and head, MXFP4 experts (codes drawn on the device
     from a seeded generator: expert values do not change the work), k commits per round."""
@@ -196,6 +271,7 @@ def main():
     ap.add_argument("--k-list", default="1,2,6,11", help="other k values also timed (empty to skip)")
     ap.add_argument("--prompt", type=int, default=256)
     ap.add_argument("--seed", type=int, default=1234, help="seed of the model and prompt of every leg")
+    ap.add_argument("--no-ops", action="store_true", help="skip the head and attention op leg")
     ap.add_argument("--seeds", default="1234,1235,1236",
                     help="seeds of the headline k: the first is --seed's run, each further seed draws a new "
                          "model and prompt; the reported value is the median (empty: --seed only)")
@@ -357,6 +433,9 @@ def main():
         model.close()
         return
 
+    # ---- the head and attention ops alone (uses the model's embedding)
+    ops = run_ops(torch, dlm, dev_w["emb"], args.seed) if not args.no_ops else None
+
     # ---- measured streaming rate of this GPU: a 1 GiB device-to-device copy (read + write bytes)
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -448,7 +527,7 @@ def main():
         "prefill": {"tokens": args.prompt, "ms": round(prefill_ms[0], 3),
                     "tok_s": round(args.prompt / (prefill_ms[0] / 1e3), 1),
                     "how": "commit passes over 32-token prompt blocks, HIP events, first leg"},
-        "hbm_stream_measured": stream,
+        "hbm_stream_measured": stream, "ops": ops,
         "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
                   for k, r in results.items()},
         "roofline": roofline, "cpu_baseline": cpu, "moe": moe,
