@@ -66,8 +66,10 @@ __device__ inline int split_chunk(int N, int nsplit_max) {
 // double-buffered, the next pass in flight while this one is computed) and shared by the
 // waves.  Per pass each wave forms the scores of all PT tiles (independent MFMA chains), takes
 // one online-softmax step over the pass and adds P V.
+// Two waves per SIMD (at most 256 registers per lane): the compiler fits the 4-wave form in
+// 228 without spills, so two workgroups share a CU; left to itself it takes 288.
 template <int D, int WPG>
-__global__ __launch_bounds__(64 * WPG) void attn_bf16_kernel(AttnP p) {
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnP p) {
   DLM_TRACE_POINT(0);
   if (p.cont_dev && *p.cont_dev == 0) return;
   constexpr int DS = D / 32;    // d-steps of the score MFMA
