@@ -526,7 +526,7 @@ def main():
         "value_per_seed": {k: round(v, 2) for k, v in per_seed.items()},
         "prefill": {"tokens": args.prompt, "ms": round(prefill_ms[0], 3),
                     "tok_s": round(args.prompt / (prefill_ms[0] / 1e3), 1),
-                    "how": "commit passes over 32-token prompt blocks, HIP events, first leg"},
+                    "how": "64-row forwards over pairs of 32-token prompt blocks, HIP events, first leg"},
         "hbm_stream_measured": stream, "ops": ops,
         "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
                   for k, r in results.items()},

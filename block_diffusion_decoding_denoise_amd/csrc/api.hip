@@ -973,7 +973,21 @@ extern "C" int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const 
   DLM_REQUIRE(n >= 0 && n % m->d.block == 0, DLM_ERR_SHAPE, "n must be a multiple of the block size");
   DLM_DEVICE_CHECK();
   DecodeWs w = decode_layout(m, kv, (char*)ws);
-  for (int b = 0; b < n / m->d.block; ++b)
-    if ((rc = enqueue_commit_pass(m, kv, ids + (size_t)b * m->d.block, w, (hipStream_t)stream))) return rc;
+  const int B = m->d.block, nb = n / B;
+  hipStream_t st = (hipStream_t)stream;
+  int b = 0;
+  // models that run 64-row forwards take the prompt two blocks per pass: the second block's
+  // rows attend to the first block's keys and their own, as in two consecutive commit passes
+  if (fusable(m)) {
+    for (; b + 1 < nb; b += 2) {
+      const dlm_model_desc& d = m->d;
+      if ((rc = embed(ids + (size_t)b * B, m->emb, w.x, 2 * B, d.d, d.vocab, 1, st))) return rc;
+      PartialSrc ps{};
+      if ((rc = enqueue_layers(m, kv, w, nullptr, /*last_kv_only=*/true, st, &ps, /*nqb=*/2))) return rc;
+      if ((rc = len_add(kv->len_dev, 2 * B, st))) return rc;
+    }
+  }
+  for (; b < nb; ++b)
+    if ((rc = enqueue_commit_pass(m, kv, ids + (size_t)b * B, w, st))) return rc;
   return DLM_OK;
 }

@@ -329,7 +329,10 @@ int dlm_decode_block_pipelined(const dlm_model* m, const dlm_commit_rule* rule, 
                                void* ws, size_t ws_bytes, void* stream);
 
 /* Commit passes over n / block consecutive prompt blocks (n % block == 0): forwards each
- * block of ids (device int32 [n]) and appends its K/V; L += n. */
+ * block of ids (device int32 [n]) and appends its K/V; L += n.  bf16 models with block = 32 take
+ * two blocks per 64-row forward (the second block's rows attend to the first block's keys and
+ * their own, the prompt attention being block-causal), with the same cache as one pass per
+ * block; an odd last block runs alone. */
 int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
                 size_t ws_bytes, void* stream);
 

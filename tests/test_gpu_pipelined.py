@@ -119,6 +119,38 @@ def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args):
         assert torch.equal(v0[l], v1[l]), f"layer {l} values"
 
 
+@pytest.mark.parametrize("shape,seed,prompt_len", [(SMALL, 1237, 96), (QWEN4B_2L, 1238, 64), (MOE_SMALL, 1239, 160)],
+                         ids=["small-3blocks", "qwen4b-2l", "moe-small-5blocks"])
+def test_prefill_pairs_bitexact(shape, seed, prompt_len):
+    """dlm_prefill forwards two prompt blocks per 64-row pass: the cache equals the one built
+    block by block (one prefill call per block), bitwise."""
+    dlm = _dlm()
+    _say(f"prefill in block pairs vs block by block: {shape.name} seed {seed} prompt {prompt_len}")
+    if shape.n_experts:
+        from tests.gpu_util import moe_device_weights
+        w = synth.Weights(shape, seed)
+        dev = {n: storage(w[n], "bf16") for n in w.names_dense() if not n.endswith(".router")}
+        dev.update(moe_device_weights(w))
+        m = dlm.Model(shape, dev, cap=prompt_len + 32)
+    else:
+        m, _ = _model(shape, seed, cap=prompt_len + 32)
+    prompt = torch.from_numpy(synth.prompt_ids(shape, prompt_len, seed))
+    m.set_len(0)
+    m.prefill(prompt)
+    torch.cuda.synchronize()
+    assert int(m.len_dev.item()) == prompt_len
+    k0 = [x[:, :prompt_len].clone() for x in m.k]
+    v0 = [dlm.v_cache_to_natural(x)[:, :prompt_len].clone() for x in m.v]
+    m.set_len(0)
+    for b in range(prompt_len // 32):
+        m.prefill(prompt[32 * b:32 * (b + 1)])
+    torch.cuda.synchronize()
+    assert int(m.len_dev.item()) == prompt_len
+    for l in range(shape.n_layers):
+        assert torch.equal(k0[l], m.k[l][:, :prompt_len]), f"layer {l} keys"
+        assert torch.equal(v0[l], dlm.v_cache_to_natural(m.v[l])[:, :prompt_len]), f"layer {l} values"
+
+
 def test_pipelined_tiny_fp32_matches_oracle():
     """f32: the pending commit pass runs on its own; tokens and rounds bit-exact with the
     oracle's block loop, and the final cache equal to the oracle's."""
