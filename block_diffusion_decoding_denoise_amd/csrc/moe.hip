@@ -85,6 +85,8 @@ __device__ inline uint32_t e4m3_code(float v) {
   return sign | ((uint32_t)(E + 7) << 3) | (uint32_t)(q * ldexpf(1.f, 3 - E) - 8.f);
 }
 
+// SA: the byte of sa that holds the A scale (four row groups share one scale word)
+template <int SA = 0>
 __device__ inline f32x4_t mfma_mx(u32x4_t a_fp4, u32x4_t b_lo, u32x4_t b_hi, int sa, int sb, f32x4_t c) {
   typedef int v8i_t __attribute__((ext_vector_type(8)));
   v8i_t a, b;
@@ -94,8 +96,8 @@ __device__ inline f32x4_t mfma_mx(u32x4_t a_fp4, u32x4_t b_lo, u32x4_t b_hi, int
   b[4] = (int)b_hi[0]; b[5] = (int)b_hi[1]; b[6] = (int)b_hi[2]; b[7] = (int)b_hi[3];
   // A format 4 = e2m1 (lane l: row l%16, columns 32(l/16) .. +32), B format 0 = e4m3 (lane l:
   // column l%16, rows 16(l/16) .. +16 then 64 + 16(l/16) .. +16); scales: lane 16b + i holds the
-  // e8m0 of row / column i, 32-element block b, in byte 0.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
+  // e8m0 of row / column i, 32-element block b, in byte SA of sa and byte 0 of sb.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, SA, sa, 0, sb);
 }
 
 __device__ inline uint32_t bload_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -129,7 +131,9 @@ __global__ __launch_bounds__(256) void mx_pack_kernel(MxPackP p) {
   const int k0 = 128 * s + 32 * (lane >> 4);
   const size_t so = (size_t)mat * p.R * (p.K / 2) + (size_t)srow * (p.K / 2) + k0 / 2;
   *(u32x4_t*)(p.dst + (size_t)c * 16) = *(const u32x4_t*)(p.src + so);
-  p.dst_scale[c] = p.src_scale[(size_t)mat * p.R * (p.K / 32) + (size_t)srow * (p.K / 32) + k0 / 32];
+  // the four row groups' scales of one (quad, step, lane) share a 4-byte word, so that one
+  // load per step brings them
+  p.dst_scale[((c >> 8) * 64 + lane) * 4 + gq] = p.src_scale[(size_t)mat * p.R * (p.K / 32) + (size_t)srow * (p.K / 32) + k0 / 32];
 }
 
 // -------------------------------------------------------------------- route + quantise
@@ -374,13 +378,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void mo
       for (int g = 0; g < 4; ++g) acc[cg][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // ring of PF steps: weights (4 row groups) and the block rows' activations (2 column groups)
     u32x4_t wa[PF][4], blo[PF][2], bhi[PF][2];
-    uint32_t wsc[PF][4], bsc[PF][2];
+    uint32_t wsc[PF], bsc[PF][2];
     auto fetch = [&](int u, int s) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         wa[u][g] = bload16_nt(wr, (uint32_t)((s * 4 + g) * 64 + lane) * 16u);
-        wsc[u][g] = bload_u8(sr, (uint32_t)((s * 4 + g) * 64 + lane));
       }
+      wsc[u] = __builtin_amdgcn_raw_buffer_load_b32(sr, (int)(s * 64 + lane) * 4, 0, 0);
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) {
         if (cg == 1 && !two) break;
@@ -400,9 +404,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void mo
 #pragma unroll
           for (int cg = 0; cg < 2; ++cg) {
             if (cg == 1 && !two) break;
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              acc[cg][g] = mfma_mx(wa[u][g], blo[u][cg], bhi[u][cg], (int)wsc[u][g], (int)bsc[u][cg], acc[cg][g]);
+            acc[cg][0] = mfma_mx<0>(wa[u][0], blo[u][cg], bhi[u][cg], (int)wsc[u], (int)bsc[u][cg], acc[cg][0]);
+            acc[cg][1] = mfma_mx<1>(wa[u][1], blo[u][cg], bhi[u][cg], (int)wsc[u], (int)bsc[u][cg], acc[cg][1]);
+            acc[cg][2] = mfma_mx<2>(wa[u][2], blo[u][cg], bhi[u][cg], (int)wsc[u], (int)bsc[u][cg], acc[cg][2]);
+            acc[cg][3] = mfma_mx<3>(wa[u][3], blo[u][cg], bhi[u][cg], (int)wsc[u], (int)bsc[u][cg], acc[cg][3]);
           }
         }
         fetch(u, s + PF);
