@@ -66,6 +66,46 @@ def test_head_bf16_small(rows, d, V, nc):
     _head_case("bf16", rows, d, V, nc, 1234)
 
 
+@pytest.fixture(scope="module")
+def full_head_emb():
+    """The 151,936 x 2560 bf16 embedding of the Qwen3-4B-shaped head (host bits and device copy)."""
+    require_gpu()
+    _say("full-size head embedding: generating 151936 x 2560 bf16")
+    E = synth.stored_normal(1234, "head.E.full", (151936, 2560), 0.02, "bf16")
+    return E, storage(E, "bf16")
+
+
+@pytest.mark.parametrize("n_committed", [0, 8, 16, 32])
+def test_head_bf16_full_size(full_head_emb, n_committed):
+    """The head at its full workload size, in the bench's launch configuration (32 rows, p.E on,
+    no logits buffer, a 128 MiB workspace), every row against the oracle."""
+    dlm = _dlm()
+    E, E_dev = full_head_emb
+    rows, d = 32, 2560
+    _say(f"head full size rows={rows} d={d} V=151936 committed={n_committed}")
+    h = synth.f32_to_bf16_bits(synth.unit_rms_rows(1234, "head.h.full", rows, d))
+    committed = synth.committed_mask(1234, rows, n_committed)
+    ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+    out = dlm.head_rowstats(storage(h, "bf16"), E_dev, torch.from_numpy(committed).cuda(), ws=ws)
+    torch.cuda.synchronize()
+    g = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+    for i in np.nonzero(committed)[0]:
+        assert g["argmax"][i] == -1 and g["lse"][i] == 0 and g["entropy"][i] == 0 and g["maxprob"][i] == 0
+        assert not g["pe"][i].any()
+    open_rows = np.nonzero(committed == 0)[0]
+    if open_rows.size == 0:
+        return
+    ref = o_head(oracle.decode_storage(h), E, committed, Prec("bf16", np.float64))
+    np.testing.assert_allclose(g["lse"][open_rows], ref["lse"][open_rows], rtol=1e-3)
+    np.testing.assert_allclose(g["entropy"][open_rows], ref["entropy"][open_rows], rtol=1e-2)
+    np.testing.assert_allclose(g["maxprob"][open_rows], ref["maxprob"][open_rows], rtol=1e-2)
+    mism = [i for i in open_rows if g["argmax"][i] != ref["argmax"][i]]
+    assert all(ref["top2_gap"][i] < 1e-3 for i in mism), f"argmax mismatch rows {mism}"
+    num = np.linalg.norm(g["pe"][open_rows] - ref["pe"][open_rows], axis=1)
+    den = np.linalg.norm(ref["pe"][open_rows], axis=1)
+    assert np.all(num / den < 1e-2), (num / den).max()
+
+
 @pytest.mark.parametrize("rows,d,V,nc", [(32, 256, 4096, 0), (32, 256, 4096, 24), (5, 64, 100, 1)])
 def test_head_f32(rows, d, V, nc):
     _head_case("f32", rows, d, V, nc, 1235)
