@@ -35,3 +35,4 @@ from .commit import CommitRule, commit, THRESHOLD, FIXED_K, FLAG_HIT_MAX_ROUNDS,
 from .loop import (OracleModel, KVCache, selfcond, denoise_round, decode_block,  # noqa: F401
                    commit_pass, prefill, generate, blockcausal_reference)
 from .moe import (mxfp4_decode, mxfp8_quant_dequant, router_topk, moe_ffn)  # noqa: F401
+from .kvcache import e4m3_decode, e4m3_encode, attention_fp8_cache  # noqa: F401

@@ -107,6 +107,16 @@ def uniform_ints(seed: int, name: str, n: int, high: int) -> np.ndarray:
     return _ss(seed, name, 0).integers(0, high, size=n, dtype=np.int64).astype(np.int32)
 
 
+def e4m3_codes(seed: int, name: str, shape, max_mag_code: int = 0x4F) -> np.ndarray:
+    """uint8 FP8 e4m3 codes: a random sign bit over magnitude codes drawn uniformly from
+    [0, max_mag_code] (0x4F is 7.5; the NaN codes 0x7F / 0xFF are never drawn)."""
+    n = int(np.prod(shape))
+    r = _ss(seed, name, 0)
+    mag = r.integers(0, max_mag_code + 1, size=n, dtype=np.int64)
+    sgn = r.integers(0, 2, size=n, dtype=np.int64) << 7
+    return (mag | sgn).astype(np.uint8).reshape(shape)
+
+
 def permutation(seed: int, name: str, n: int) -> np.ndarray:
     return _ss(seed, name, 0).permutation(n).astype(np.int32)
 

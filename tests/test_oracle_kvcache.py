@@ -1,0 +1,81 @@
+"""Pins of the oracle's FP8 (e4m3) KV cache: code table, rounding, encoder, attention."""
+import json
+import math
+import os
+
+import numpy as np
+
+import synth
+from oracle import attention, e4m3_decode, e4m3_encode, attention_fp8_cache
+from oracle.moe import e4m3_round
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mx_formats.json")
+
+
+def test_e4m3_code_table():
+    """Codes from the OCP format definition (bias 7, 3 mantissa bits, subnormals, NaN)."""
+    with open(GOLDEN) as f:
+        table = json.load(f)["e4m3"]["values_by_code"]
+    for code, want in table.items():
+        got = e4m3_decode(np.array([int(code, 16)], np.uint8))[0]
+        if want == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), (code, got, want)
+
+
+def test_e4m3_decode_against_rounding():
+    """Every finite code is a fixed point of the independently written nearest-even rounding,
+    the 127 non-negative finite codes are strictly increasing, and the extremes match the
+    rounding's saturation and smallest subnormal."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = e4m3_decode(codes)
+    finite = ~np.isnan(vals)
+    assert finite.sum() == 254
+    np.testing.assert_array_equal(e4m3_round(vals[finite]), vals[finite])
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    np.testing.assert_array_equal(vals[0x80:0xFF], -pos)
+    assert pos[-1] == e4m3_round(np.array([1e9]))[0] == 448.0
+    assert pos[1] == 2.0 ** -9
+
+
+def test_e4m3_encode_inverts_decode_and_ties():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], np.uint8)
+    np.testing.assert_array_equal(e4m3_encode(e4m3_decode(codes)), codes)
+    # midpoints between neighbours go to the even mantissa, and beyond 448 saturates
+    v = np.array([1.0625, 1.1875, 3 * 2.0 ** -10, 464.0, 1e6, -1e6, -1.0625])
+    np.testing.assert_array_equal(e4m3_decode(e4m3_encode(v)), [1.0, 1.25, 2.0 ** -8, 448.0, 448.0, -448.0, -1.0])
+    assert e4m3_encode(np.array([np.nan]))[0] == 0x7F
+
+
+def _case(seed, B=5, hq=4, hkv=2, N=70, D=16):
+    q = synth.normal_f32(seed, "kv8.q", (B, hq, D)).astype(np.float64)
+    kc = synth.e4m3_codes(seed, "kv8.k", (hkv, N, D))
+    vc = synth.e4m3_codes(seed, "kv8.v", (hkv, N, D))
+    return q, kc, vc
+
+
+def test_attention_fp8_cache_reduces_to_attention():
+    """Unit scales: the same as the float64 attention over the decoded values; a key scale is
+    a softmax-scale factor; a value scale multiplies the output."""
+    q, kc, vc = _case(11)
+    k, v = e4m3_decode(kc), e4m3_decode(vc)
+    s = 0.25
+    np.testing.assert_allclose(attention_fp8_cache(q, kc, vc, 1.0, 1.0, s), attention(q, k, v, s), rtol=0, atol=0)
+    np.testing.assert_allclose(attention_fp8_cache(q, kc, vc, 0.125, 1.0, s), attention(q, k, v, s * 0.125),
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(attention_fp8_cache(q, kc, vc, 1.0, 0.03, s), 0.03 * attention(q, k, v, s),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_attention_fp8_cache_one_key_and_equal_keys():
+    """One visible key returns v_scale times its value row; identical keys average the values."""
+    q, kc, vc = _case(12, N=1)
+    o = attention_fp8_cache(q, kc, vc, 0.5, 0.25, 1.0)
+    for h in range(q.shape[1]):
+        np.testing.assert_array_equal(o[:, h], np.broadcast_to(0.25 * e4m3_decode(vc[h // 2, 0]), o[:, h].shape))
+    q, kc, vc = _case(13, N=6)
+    kc[:] = kc[:, :1]
+    o = attention_fp8_cache(q, kc, vc, 1.0, 1.0, 1.0)
+    np.testing.assert_allclose(o[:, 0], np.broadcast_to(e4m3_decode(vc[0]).mean(axis=0), o[:, 0].shape), rtol=1e-12)
