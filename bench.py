@@ -98,8 +98,9 @@ def moe_expert_bytes(s):
 def run_ops(torch, dlm, emb, seed):
     """The head and attention ops alone at their workload sizes (the head with 32 / 24 / 16 / 0
     open rows of 32 over the 151,936 x 2560 embedding; attention with 32 / 8 heads of 128, a
-    32-query block, prefix 512 / 4096 / 32768), each call replayed from a captured graph and
-    timed with HIP events; bytes are the algorithmic ones (every embedding or K/V byte once)."""
+    32-query block, prefix 512 / 4096 / 32768, over a bf16 and over an FP8 e4m3 cache), each
+    call replayed from a captured graph and timed with HIP events; bytes are the algorithmic
+    ones (every embedding or K/V byte once)."""
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     V, d = emb.shape
@@ -135,38 +136,54 @@ def run_ops(torch, dlm, emb, seed):
     # ---- attention: K/V copies rotated so that at least 512 MiB is cycled (short prefixes would
     # otherwise sit in the 256 MB memory-side cache)
     hq, hkv, D, B = 32, 8, 128, 32
-    for L in (512, 4096, 32768):
-        cap = (L + B + 31) // 32 * 32
-        per = 2 * hkv * cap * D * 2
-        n = max(2, -(-(512 << 20) // per))
-        kc = torch.randn(n, hkv, cap, D, device="cuda", generator=g).to(torch.bfloat16)
-        vc = torch.randn(n, hkv, cap // 32, D, 32, device="cuda", generator=g).to(torch.bfloat16)
-        q = torch.randn(B, hq, D, device="cuda", generator=g).to(torch.bfloat16)
-        o = torch.empty_like(q)
-        aws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
-        dlm.block_attn(q, kc[0], vc[0], L, out=o, ws=aws)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(n):
-                dlm.block_attn(q, kc[i], vc[i], L, out=o, ws=aws)
-        graph.replay()
-        torch.cuda.synchronize()
-        reps = max(1, 200 // n)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+    out["attention_fp8_cache"] = []
+    for kv in ("bf16", "fp8"):
+        es = 2 if kv == "bf16" else 1
+        for L in (512, 4096, 32768):
+            cap = (L + B + 31) // 32 * 32
+            per = 2 * hkv * cap * D * es
+            n = max(2, -(-(512 << 20) // per))
+            if kv == "bf16":
+                kc = torch.randn(n, hkv, cap, D, device="cuda", generator=g).to(torch.bfloat16)
+                vc = torch.randn(n, hkv, cap // 32, D, 32, device="cuda", generator=g).to(torch.bfloat16)
+                scales = None
+            else:
+                # e4m3 codes of magnitude <= 7.5 with random signs (no NaN codes)
+                def codes(*shape):
+                    mag = torch.randint(0, 0x50, shape, device="cuda", generator=g, dtype=torch.int32)
+                    sgn = torch.randint(0, 2, shape, device="cuda", generator=g, dtype=torch.int32) << 7
+                    return (mag | sgn).to(torch.uint8)
+                kc = codes(n, hkv, cap, D)
+                vc = codes(n, hkv, cap // 32, D, 32)
+                scales = (0.125, 0.2)
+            q = torch.randn(B, hq, D, device="cuda", generator=g).to(torch.bfloat16)
+            o = torch.empty_like(q)
+            aws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+            dlm.block_attn(q, kc[0], vc[0], L, out=o, ws=aws, kv_scales=scales)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(n):
+                    dlm.block_attn(q, kc[i], vc[i], L, out=o, ws=aws, kv_scales=scales)
             graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / 1e3 / (reps * n)
-        nbytes = (L + B) * hkv * D * 2 * 2 + 2 * B * hq * D * 2
-        out["attention"].append({"L": L, "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
-                                 "frac": round(nbytes / t / HBM_PEAK, 4), "rotated_copies": n})
-        del kc, vc, aws, graph
-        torch.cuda.empty_cache()
+            torch.cuda.synchronize()
+            reps = max(1, 200 // n)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / (reps * n)
+            nbytes = (L + B) * hkv * D * es * 2 + 2 * B * hq * D * 2
+            out["attention" if kv == "bf16" else "attention_fp8_cache"].append(
+                {"L": L, "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
+                 "frac": round(nbytes / t / HBM_PEAK, 4), "rotated_copies": n})
+            del kc, vc, aws, graph
+            torch.cuda.empty_cache()
     log("ops: head " + ", ".join(f"{r['open_rows']} open {r['us']:.0f} us" for r in out["head"]) +
-        "; attention " + ", ".join(f"L={r['L']} {r['us']:.1f} us {r['GB_s']:.0f} GB/s" for r in out["attention"]))
+        "; attention " + ", ".join(f"L={r['L']} {r['us']:.1f} us {r['GB_s']:.0f} GB/s" for r in out["attention"]) +
+        "; FP8 cache " + ", ".join(f"L={r['L']} {r['us']:.1f} us {r['GB_s']:.0f} GB/s" for r in out["attention_fp8_cache"]))
     return out
 
 

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdlm.so")
 
-DLM_F32, DLM_BF16, DLM_MXFP4 = 0, 1, 2
+DLM_F32, DLM_BF16, DLM_MXFP4, DLM_FP8_E4M3 = 0, 1, 2, 3
 THRESHOLD, FIXED_K = 0, 1
 FLAG_HIT_MAX_ROUNDS, FLAG_NONFINITE = 1, 2
 MAX_ROWS = 64
@@ -30,7 +30,8 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("hq", ctypes.c_int), ("hkv", ctypes.c_int),
                 ("head_dim", ctypes.c_int), ("block", ctypes.c_int), ("cap", ctypes.c_int),
                 ("softmax_scale", ctypes.c_float), ("prefix_len", ctypes.c_int),
-                ("prefix_len_dev", ctypes.c_void_p), ("max_prefix_len", ctypes.c_int)]
+                ("prefix_len_dev", ctypes.c_void_p), ("max_prefix_len", ctypes.c_int),
+                ("kv_dtype", ctypes.c_int), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class HeadDesc(ctypes.Structure):
@@ -173,16 +174,23 @@ def _dev(t: torch.Tensor, name: str):
 
 # ------------------------------------------------------------------ op calls
 def block_attn(q, k_cache, v_cache, prefix_len, out=None, prefix_len_dev=None, max_prefix_len=None,
-               scale=None, ws=None):
+               scale=None, ws=None, kv_scales=None):
     """o = softmax(q K^T * scale) V over the L prefix keys and the B block keys (no mask).
     q [B, hq, D]; k_cache [hkv, cap, D]; v_cache in the blocked transposed layout
-    [hkv, cap/32, D, 32] (v_cache_from_natural); returns out [B, hq, D]."""
+    [hkv, cap/32, D, 32] (v_cache_from_natural); returns out [B, hq, D].
+    uint8 caches hold FP8 e4m3 codes (bf16 q); kv_scales = (k_scale, v_scale) then gives the
+    stored values' scales."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, n)
     B, hq, D = q.shape
     hkv, cap, _ = k_cache.shape
+    fp8 = k_cache.dtype == torch.uint8
+    if fp8 != (v_cache.dtype == torch.uint8):
+        raise ValueError("k_cache and v_cache must both be FP8 (uint8 codes) or neither")
+    ks, vs = kv_scales if kv_scales is not None else (1.0, 1.0)
     d = AttnDesc(_dtype_code(q), hq, hkv, D, B, cap, scale if scale is not None else D ** -0.5,
-                 int(prefix_len), _ptr(prefix_len_dev), int(max_prefix_len if max_prefix_len is not None else prefix_len))
+                 int(prefix_len), _ptr(prefix_len_dev), int(max_prefix_len if max_prefix_len is not None else prefix_len),
+                 DLM_FP8_E4M3 if fp8 else _dtype_code(q), float(ks), float(vs))
     if out is None:
         out = torch.empty_like(q)
     need = lib().dlm_block_attn_ws_bytes(ctypes.byref(d))

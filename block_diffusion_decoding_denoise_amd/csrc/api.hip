@@ -1,6 +1,7 @@
 // C ABI of the library: argument validation, workspace layout, the per-round sequence of
 // kernels and the device-resident block loop captured in a HIP graph.
 #include <stdarg.h>
+#include <math.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -73,6 +74,11 @@ static int check_attn(const dlm_attn_desc* d) {
   DLM_REQUIRE(d->cap % 32 == 0, DLM_ERR_SHAPE, "cap must be a multiple of 32 (blocked V cache)");
   DLM_REQUIRE(d->hq % d->hkv == 0, DLM_ERR_SHAPE, "hq %% hkv != 0");
   DLM_REQUIRE(d->head_dim == 64 || d->head_dim == 128, DLM_ERR_SHAPE, "head_dim must be 64 or 128");
+  DLM_REQUIRE(d->kv_dtype == d->dtype || (d->kv_dtype == DLM_FP8_E4M3 && d->dtype == DLM_BF16), DLM_ERR_DTYPE,
+              "kv_dtype %d with dtype %d (an FP8 cache needs bf16 queries)", d->kv_dtype, d->dtype);
+  if (d->kv_dtype == DLM_FP8_E4M3)
+    DLM_REQUIRE(isfinite(d->k_scale) && isfinite(d->v_scale) && d->k_scale > 0.f && d->v_scale > 0.f,
+                DLM_ERR_ARG, "FP8 cache scales must be finite and positive");
   DLM_REQUIRE(d->block <= 32, DLM_ERR_SHAPE, "block must be <= 32");
   const int maxL = d->prefix_len_dev ? d->max_prefix_len : d->prefix_len;
   DLM_REQUIRE(maxL >= 0 && d->prefix_len >= 0, DLM_ERR_ARG, "negative prefix length");
@@ -104,7 +110,8 @@ extern "C" int dlm_block_attn(const dlm_attn_desc* d, const void* q, const void*
   const int maxL = d->prefix_len_dev ? d->max_prefix_len : d->prefix_len;
   return attn_bf16(q, k, v, out, d->hq, d->hkv, d->head_dim, d->block, 1, d->cap, d->softmax_scale,
                    d->prefix_len_dev, d->prefix_len, nullptr,
-                   attn_plan(d->hq, d->hkv, d->head_dim, d->block, maxL), ws, /*out_packed=*/0, st);
+                   attn_plan(d->hq, d->hkv, d->head_dim, d->block, maxL), ws, /*out_packed=*/0, st,
+                   AttnKv{d->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, d->k_scale, d->v_scale});
 }
 
 // ------------------------------------------------------------------ head op

@@ -21,6 +21,7 @@
 #include "attn.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dlm {
 
@@ -45,7 +46,8 @@ struct AttnP {
   uint16_t* part_o;             // [nqb][hkv][ns][G][32][D] bf16: each split's normalised output
   float* part_ml;               // [nqb][hkv][ns][G][32][2]
   int hq, hkv, B, nqb, cap, chunk, nsplit_max, out_packed;
-  float scale_log2;             // softmax scale * log2(e)
+  float scale_log2;             // softmax scale * log2(e) (times the key scale of an FP8 cache)
+  float v_scale;                // value scale of an FP8 cache
   const int32_t* len_dev;
   int len_host;
   const int32_t* cont_dev;
@@ -68,7 +70,20 @@ __device__ inline int split_chunk(int N, int nsplit_max) {
 // one online-softmax step over the pass and adds P V.
 // Two waves per SIMD (at most 256 registers per lane): the compiler fits the 4-wave form in
 // 228 without spills, so two workgroups share a CU; left to itself it takes 288.
-template <int D, int WPG>
+// KV8: the caches hold FP8 e4m3 codes (same layouts, one byte per element).  A pass then
+// loads half the bytes, and the codes are widened to bf16 (exactly: every e4m3 value is a
+// bf16 value) on their way into LDS, so everything after the LDS write is the bf16 path; the
+// key scale is folded into the softmax scale and the value scale into the output.
+__device__ inline u32x4_t e4m3x8_to_bf16(u32x2_t x) {
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true));
+  return r;
+}
+
+template <int D, int WPG, bool KV8 = false>
 __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnP p) {
   DLM_TRACE_POINT(0);
   if (p.cont_dev && *p.cont_dev == 0) return;
@@ -116,12 +131,23 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) v
   // buffer descriptors: K rows past c1 read as zeros; V^T tiles stay inside this head's
   // [cap/32][D][32] block (a tile wholly past c1 is not loaded; keys past c1 inside a tile are
   // masked after the LDS read)
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.k + (size_t)g * p.cap * D, (uint32_t)c1 * D * 2u);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.v + (size_t)g * D * p.cap, (uint32_t)D * p.cap * 2u);
+  constexpr int ES = KV8 ? 1 : 2;                          // cache bytes per element
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint8_t*)p.k + (size_t)g * p.cap * D * ES, (uint32_t)c1 * D * ES);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint8_t*)p.v + (size_t)g * D * p.cap * ES, (uint32_t)D * p.cap * ES);
   const int lg = lane >> 4;                                // lane group: keys 8lg .. 8lg+7
 
-  // global -> register staging of one pass (PT tiles; KC + VC 16-byte chunks per thread each)
-  u32x4_t stk[PT][KC], stv[PT][VC];
+  // global -> register staging of one pass (PT tiles; KC + VC chunks of 8 elements per thread
+  // each: 16 bytes, or 8 for an FP8 cache)
+  typedef typename std::conditional<KV8, u32x2_t, u32x4_t>::type chunk_t;
+  chunk_t stk[PT][KC], stv[PT][VC];
+  auto ld = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) -> chunk_t {
+    if constexpr (KV8) return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 2));
+    else return bload16_nt(r, off);
+  };
+  auto widen = [&](chunk_t x) -> u32x4_t {
+    if constexpr (KV8) return e4m3x8_to_bf16(x);
+    else return x;
+  };
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
@@ -130,12 +156,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const int c = tid + NT * j, key = c / (D / 8), col = c % (D / 8);
-        stk[u][j] = bload16_nt(kr, in ? (uint32_t)((tu + key) * D * 2 + col * 16) : 0x80000000u);
+        stk[u][j] = ld(kr, in ? (uint32_t)(((tu + key) * D + col * 8) * ES) : 0x80000000u);
       }
 #pragma unroll
       for (int j = 0; j < VC; ++j) {
         const int c = tid + NT * j, dv = c >> 2, part = c & 3;
-        stv[u][j] = bload16_nt(vr, in ? (uint32_t)((((tu >> 5) * D + dv) * 32) * 2 + part * 16) : 0x80000000u);
+        stv[u][j] = ld(vr, in ? (uint32_t)((((tu >> 5) * D + dv) * 32 + part * 8) * ES) : 0x80000000u);
       }
     }
   };
@@ -147,12 +173,12 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const int c = tid + NT * j, key = c / (D / 8), col = c % (D / 8);
-        *(u32x4_t*)(sk + key * KROW + col * 16) = stk[u][j];
+        *(u32x4_t*)(sk + key * KROW + col * 16) = widen(stk[u][j]);
       }
 #pragma unroll
       for (int j = 0; j < VC; ++j) {
         const int c = tid + NT * j, dv = c >> 2, part = c & 3;
-        *(u32x4_t*)(sv + dv * VROW + part * 16) = stv[u][j];
+        *(u32x4_t*)(sv + dv * VROW + part * 16) = widen(stv[u][j]);
       }
     }
   };
@@ -272,7 +298,7 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = 16 * qb + (lane & 15);
     if (qi >= p.B) continue;
-    const float inv = 1.0f / lrow[qb];
+    const float inv = (KV8 ? p.v_scale : 1.0f) / lrow[qb];
     if (nsplit == 1) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
@@ -428,7 +454,7 @@ size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl, int nqb) {
 
 int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, int hkv, int D,
               int B, int nqb, int cap, float scale, const int32_t* len_dev, int len_host,
-              const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st) {
+              const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st, AttnKv kvf) {
   if (nqb < 1 || nqb > 2 || (nqb == 2 && B != 32))
     return fail(DLM_ERR_SHAPE, "attention: one query block, or two of 32 rows");
   AttnP p;
@@ -448,7 +474,8 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
   p.cap = cap;
   p.chunk = pl.chunk;
   p.nsplit_max = pl.nsplit_max;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale_log2 = scale * (kvf.fp8 ? kvf.k_scale : 1.f) * 1.4426950408889634f;
+  p.v_scale = kvf.fp8 ? kvf.v_scale : 1.f;
   p.len_dev = len_dev;
   p.len_host = len_host;
   p.cont_dev = cont_dev;
@@ -458,12 +485,20 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
   const int grid = nqb * hkv * (G / WPG) * pl.nsplit_max;
   auto launch = [&](auto kern, int threads) { hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, p); };
   if (D == 128) {
-    if (WPG == 4) launch(attn_bf16_kernel<128, 4>, 256);
+    if (kvf.fp8) {
+      if (WPG == 4) launch(attn_bf16_kernel<128, 4, true>, 256);
+      else if (WPG == 2) launch(attn_bf16_kernel<128, 2, true>, 128);
+      else launch(attn_bf16_kernel<128, 1, true>, 64);
+    } else if (WPG == 4) launch(attn_bf16_kernel<128, 4>, 256);
     else if (WPG == 2) launch(attn_bf16_kernel<128, 2>, 128);
     else launch(attn_bf16_kernel<128, 1>, 64);
     hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((nqb * hq * B + 7) / 8), dim3(256), 0, st, p);
   } else {
-    if (WPG == 4) launch(attn_bf16_kernel<64, 4>, 256);
+    if (kvf.fp8) {
+      if (WPG == 4) launch(attn_bf16_kernel<64, 4, true>, 256);
+      else if (WPG == 2) launch(attn_bf16_kernel<64, 2, true>, 128);
+      else launch(attn_bf16_kernel<64, 1, true>, 64);
+    } else if (WPG == 4) launch(attn_bf16_kernel<64, 4>, 256);
     else if (WPG == 2) launch(attn_bf16_kernel<64, 2>, 128);
     else launch(attn_bf16_kernel<64, 1>, 64);
     hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((nqb * hq * B + 15) / 16), dim3(256), 0, st, p);

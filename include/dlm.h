@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DLM_ABI_VERSION 1
+#define DLM_ABI_VERSION 2
 #define DLM_MAX_ROWS 64
 #define DLM_MAX_ROUNDS 64
 
@@ -54,7 +54,7 @@ typedef enum {
   DLM_ERR_UNSUPPORTED = -6  /* device is not gfx950 */
 } dlm_status;
 
-typedef enum { DLM_F32 = 0, DLM_BF16 = 1, DLM_MXFP4 = 2 } dlm_dtype;
+typedef enum { DLM_F32 = 0, DLM_BF16 = 1, DLM_MXFP4 = 2, DLM_FP8_E4M3 = 3 } dlm_dtype;
 
 typedef enum { DLM_COMMIT_THRESHOLD = 0, DLM_COMMIT_FIXED_K = 1 } dlm_commit_mode;
 
@@ -83,14 +83,23 @@ const char* dlm_last_error(void);
  *   hq % hkv == 0, 1 <= B <= 64, L + B <= cap.
  *   ws: device scratch of at least dlm_block_attn_ws_bytes(desc) bytes; must be zeroed
  *   once before first use (the kernels leave it zeroed again).
+ *   FP8 cache (kv_dtype = DLM_FP8_E4M3, with dtype = DLM_BF16): k_cache and v_cache hold one
+ *   OCP FP8 e4m3 code per element in the same layouts, and the stored key (value) is
+ *   k_scale (v_scale) times the code's value; q and out stay bf16.  This is the FP8 KV cache
+ *   the pages list among the long-context memory levers ([ORL-blog] "What shipped": the
+ *   attention over the prefix cache is the part of a round that grows with context); the
+ *   format, one e4m3 code per element with one scale per cache, is this library's reading.
+ *   The caller writes the codes; NaN codes must not occur at positions below L + B.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
-  int dtype;            /* DLM_BF16 or DLM_F32 (all of q, caches, out) */
+  int dtype;            /* DLM_BF16 or DLM_F32 (q and out; the caches too unless kv_dtype says FP8) */
   int hq, hkv, head_dim, block, cap;
   float softmax_scale;  /* usually 1/sqrt(head_dim) */
   int prefix_len;       /* host value of L (used if prefix_len_dev is NULL) */
   const int32_t* prefix_len_dev;
   int max_prefix_len;   /* upper bound of L when prefix_len_dev is used (sizes the workspace) */
+  int kv_dtype;         /* equal to dtype, or DLM_FP8_E4M3 (dtype DLM_BF16 only) */
+  float k_scale, v_scale;   /* FP8 cache scales: finite and > 0 (ignored otherwise) */
 } dlm_attn_desc;
 
 size_t dlm_block_attn_ws_bytes(const dlm_attn_desc* desc);

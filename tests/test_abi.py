@@ -26,12 +26,13 @@ def test_library_exports_every_declared_call():
     assert len(names) >= 20
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
-    assert L.dlm_abi_version() == 1
+    assert L.dlm_abi_version() == 2
 
 
 def _attn(**kw):
     base = dict(dtype=dlm.DLM_BF16, hq=32, hkv=8, head_dim=128, block=32, cap=1024, softmax_scale=0.088,
-                prefix_len=100, prefix_len_dev=None, max_prefix_len=100)
+                prefix_len=100, prefix_len_dev=None, max_prefix_len=100, kv_dtype=dlm.DLM_BF16, k_scale=1.0,
+                v_scale=1.0)
     base.update(kw)
     return dlm.AttnDesc(**base)
 
@@ -39,6 +40,9 @@ def _attn(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(hq=30), SHAPE), (dict(head_dim=96), SHAPE), (dict(block=33), SHAPE), (dict(prefix_len=1000), SHAPE),
     (dict(dtype=7), DTYPE), (dict(hkv=0), ARG), (dict(prefix_len=-1), ARG),
+    (dict(kv_dtype=dlm.DLM_F32), DTYPE), (dict(dtype=dlm.DLM_F32, kv_dtype=dlm.DLM_FP8_E4M3), DTYPE),
+    (dict(kv_dtype=dlm.DLM_FP8_E4M3, k_scale=0.0), ARG), (dict(kv_dtype=dlm.DLM_FP8_E4M3, v_scale=float("nan")), ARG),
+    (dict(kv_dtype=dlm.DLM_FP8_E4M3, k_scale=float("inf")), ARG), (dict(kv_dtype=dlm.DLM_FP8_E4M3, head_dim=96), SHAPE),
 ])
 def test_block_attn_validation(kw, code):
     d = _attn(**kw)

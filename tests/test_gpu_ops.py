@@ -132,6 +132,77 @@ def _attn_case(dtype, hq, hkv, D, B, L, cap, seed):
         np.testing.assert_allclose(got, ref, atol=1e-5, rtol=1e-4)
 
 
+def _attn_fp8_case(hq, hkv, D, B, L, cap, seed, k_scale=0.125, v_scale=0.2, stale=False):
+    """bf16 queries over an FP8 (e4m3) cache with one scale per cache, against the oracle's
+    attention over the decoded cache."""
+    dlm = _dlm()
+    _say(f"attn fp8-cache case hq={hq} hkv={hkv} D={D} B={B} L={L} cap={cap} seed={seed} stale={stale}")
+    q = synth.stored_normal(seed, "attn8.q", (B, hq, D), 1.0, "bf16")
+    kc = synth.e4m3_codes(seed, "attn8.k", (hkv, cap, D))
+    vc = synth.e4m3_codes(seed, "attn8.v", (hkv, cap, D))
+    if stale:
+        # positions past the block hold NaN codes and the largest finite ones
+        kc[:, L + B:] = 0x7F
+        vc[:, L + B:] = 0xFF
+        kc[:, L + B + 1::3] = 0x7E
+    vt = np.ascontiguousarray(vc.reshape(hkv, cap // 32, 32, D).transpose(0, 1, 3, 2))
+    out = dlm.block_attn(storage(q, "bf16"), torch.from_numpy(kc).cuda(), torch.from_numpy(vt).cuda(), L,
+                         kv_scales=(k_scale, v_scale))
+    torch.cuda.synchronize()
+    ref = oracle.attention_fp8_cache(oracle.decode_storage(q), kc[:, :L + B], vc[:, :L + B], k_scale, v_scale,
+                                     1 / math.sqrt(D))
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    # as for the bf16 cache: one rounding of the output and bf16 probabilities inside P.V (the
+    # decoded cache values are exact in bf16)
+    np.testing.assert_allclose(got, ref, atol=2e-2 * max(1.0, v_scale * 7.5), rtol=2e-2)
+
+
+@pytest.mark.parametrize("L", [0, 33, 300, 511])
+def test_attn_fp8_cache_small(L):
+    _attn_fp8_case(32, 8, 128, 32, L, 1024, 1240)
+
+
+@pytest.mark.parametrize("L,B,hq,hkv,D", [(0, 1, 4, 2, 64), (17, 7, 8, 8, 128), (1000, 32, 16, 4, 128),
+                                          (64, 32, 4, 1, 64), (200, 32, 8, 4, 128)])
+def test_attn_fp8_cache_shapes(L, B, hq, hkv, D):
+    _attn_fp8_case(hq, hkv, D, B, L, (L + B + 5 + 31) // 32 * 32, 1241)
+
+
+@pytest.mark.parametrize("L", [100, 2100])
+def test_attn_fp8_cache_stale_codes(L):
+    _attn_fp8_case(32, 8, 128, 32, L, (L + 32 + 200 + 31) // 32 * 32, 1242, stale=True)
+
+
+@pytest.mark.parametrize("L", [512, 4096, 32768])
+def test_attn_fp8_cache_full_size(L):
+    """The FP8-cache attention at the block-attention workload's sizes (32/8 heads of 128, 32
+    queries, prefix L), every output against the oracle."""
+    _attn_fp8_case(32, 8, 128, 32, L, L + 32, 1243, k_scale=0.0625, v_scale=0.25)
+
+
+def test_attn_fp8_cache_decodes_every_code():
+    """One visible key: the output is v_scale times the decoded value row, exactly (a power-of-
+    two scale of an e4m3 value is a bf16 value).  The two kv heads' 256 value columns hold every
+    code (the two NaN codes replaced by zero), so this pins the kernel's e4m3 widening."""
+    dlm = _dlm()
+    hq = hkv = 2
+    D, cap = 128, 32
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    vc = np.zeros((hkv, cap, D), np.uint8)
+    vc[:, 0, :] = codes.reshape(2, 128)
+    kc = synth.e4m3_codes(1244, "attn8.k1", (hkv, cap, D))
+    q = synth.stored_normal(1244, "attn8.q1", (1, hq, D), 1.0, "bf16")
+    vt = np.ascontiguousarray(vc.reshape(hkv, cap // 32, 32, D).transpose(0, 1, 3, 2))
+    out = dlm.block_attn(storage(q, "bf16"), torch.from_numpy(kc).cuda(), torch.from_numpy(vt).cuda(), 0,
+                         kv_scales=(0.5, 0.25))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()[0]
+    want = 0.25 * oracle.e4m3_decode(codes).reshape(2, 128)
+    np.testing.assert_array_equal(got, want)
+
+
 @pytest.mark.parametrize("L", [0, 1, 33, 300, 511])
 def test_attn_bf16_small(L):
     _attn_case("bf16", 32, 8, 128, 32, L, 1024, 1234)
