@@ -88,8 +88,8 @@ def attention_sublayer(x, lw, kc, vc, L, shape, prec: Prec, pos=None):
     q = prec.act(rope(q, pos, shape.rope_base))
     k = prec.act(rope(k, pos, shape.rope_base))
     v = prec.act(v)
-    kc[:, L:L + B, :] = k.transpose(1, 0, 2)
-    vc[:, L:L + B, :] = v.transpose(1, 0, 2)
+    kc[:, L:L + B, :] = prec.kv_store(k, 0).transpose(1, 0, 2)
+    vc[:, L:L + B, :] = prec.kv_store(v, 1).transpose(1, 0, 2)
     o = attention(q, kc[:, :L + B, :], vc[:, :L + B, :], 1.0 / np.sqrt(D))
     o = prec.act(o.reshape(B, Hq * D))
     return x + o @ lw["wo"].T

@@ -41,9 +41,22 @@ class Prec:
     storage: "f32" (every tensor an fp32 value, no activation rounding) or
              "bf16" (activations rounded to bf16 at the library's storage points).
     compute: np.float64 for parity, np.float32 for the CPU timing baseline.
+    kv_scales: None (the KV cache holds the stored k and v), or (k_scale, v_scale) for an
+             FP8 cache: the cache then holds scale * e4m3(value / scale), the value being the
+             bf16 k (v) after RoPE, rounded to nearest-even e4m3 with saturation
+             (oracle/kvcache.py states the format reading).
     """
     storage: str = "f32"
     compute: type = np.float64
+    kv_scales: tuple | None = None
+
+    def kv_store(self, x: np.ndarray, which: int) -> np.ndarray:
+        """What the KV cache holds for the stored keys (which = 0) or values (which = 1)."""
+        if self.kv_scales is None:
+            return x
+        from .moe import e4m3_round
+        s = float(self.kv_scales[which])
+        return (s * e4m3_round(np.asarray(x, dtype=np.float64) / s)).astype(self.compute, copy=False)
 
     def act(self, x: np.ndarray) -> np.ndarray:
         """Round an activation at a storage point."""

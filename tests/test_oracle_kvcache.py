@@ -79,3 +79,57 @@ def test_attention_fp8_cache_one_key_and_equal_keys():
     kc[:] = kc[:, :1]
     o = attention_fp8_cache(q, kc, vc, 1.0, 1.0, 1.0)
     np.testing.assert_allclose(o[:, 0], np.broadcast_to(e4m3_decode(vc[0]).mean(axis=0), o[:, 0].shape), rtol=1e-12)
+
+
+def _tiny_layer():
+    from oracle import KVCache
+    s = synth.small_shape(synth.TINY, n_layers=1, d=8, hq=2, hkv=1, head_dim=4, ffn=6, vocab=16, block=3)
+    rng = np.random.default_rng(7)
+    W = {n: rng.standard_normal(shp) * 0.5 for n, shp in [
+        ("wq", (8, 8)), ("wk", (4, 8)), ("wv", (4, 8)), ("wo", (8, 8)), ("wg", (6, 8)), ("wu", (6, 8)),
+        ("wd", (8, 6))]}
+    W["attn_norm"] = rng.uniform(0.5, 1.5, 8)
+    W["ffn_norm"] = rng.uniform(0.5, 1.5, 8)
+    return s, W, rng, KVCache
+
+
+def test_fp8_cache_write_quantises_the_stored_kv():
+    """With an FP8 cache the rows a layer writes are scale * e4m3(bf16 k or v / scale), the
+    bf16 values being those the bf16-cache run writes; earlier rows are untouched."""
+    from oracle import dense_layer, Prec
+    s, W, rng, KVCache = _tiny_layer()
+    L = 2
+    x = rng.standard_normal((3, 8))
+    runs = {}
+    for name, prec in (("bf16", Prec("bf16")), ("fp8", Prec("bf16", kv_scales=(0.25, 0.5)))):
+        kv = KVCache.empty(s, 8)
+        kv.k[0][:, :L] = 0.25 * e4m3_decode(synth.e4m3_codes(3, "kv8.kprev", (1, L, 4)))
+        kv.v[0][:, :L] = 0.5 * e4m3_decode(synth.e4m3_codes(3, "kv8.vprev", (1, L, 4)))
+        dense_layer(x, W, kv.k[0], kv.v[0], L, s, prec)
+        runs[name] = kv
+    k16, v16 = runs["bf16"].k[0], runs["bf16"].v[0]
+    k8, v8 = runs["fp8"].k[0], runs["fp8"].v[0]
+    np.testing.assert_array_equal(k8[:, :L], k16[:, :L])
+    np.testing.assert_array_equal(k8[:, L:L + 3], 0.25 * e4m3_round(k16[:, L:L + 3] / 0.25))
+    np.testing.assert_array_equal(v8[:, L:L + 3], 0.5 * e4m3_round(v16[:, L:L + 3] / 0.5))
+    # every written value is a code of the format times its scale
+    codes = e4m3_encode(k8[:, L:L + 3] / 0.25)
+    np.testing.assert_array_equal(0.25 * e4m3_decode(codes), k8[:, L:L + 3])
+
+
+def test_fp8_cache_layer_equals_bf16_cache_on_representable_values():
+    """When every k and v the layer stores is already a scale * e4m3 value (here: values of
+    zero, a weight matrix of zeros), the FP8 cache changes nothing."""
+    from oracle import dense_layer, Prec
+    s, W, rng, KVCache = _tiny_layer()
+    W["wk"] = np.zeros_like(W["wk"])
+    W["wv"] = np.zeros_like(W["wv"])
+    L = 2
+    x = rng.standard_normal((3, 8))
+    outs = []
+    for prec in (Prec("bf16"), Prec("bf16", kv_scales=(0.125, 2.0))):
+        kv = KVCache.empty(s, 8)
+        kv.k[0][:, :L] = 0.125 * e4m3_decode(synth.e4m3_codes(4, "kv8.kprev", (1, L, 4)))
+        kv.v[0][:, :L] = 2.0 * e4m3_decode(synth.e4m3_codes(4, "kv8.vprev", (1, L, 4)))
+        outs.append(dense_layer(x, W, kv.k[0], kv.v[0], L, s, prec))
+    np.testing.assert_array_equal(outs[0], outs[1])
