@@ -31,16 +31,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(shape, L, head_rows=32):
+def algorithmic_bytes(shape, L, head_rows=32, kv_elem_bytes=2):
     """HBM bytes one round must move at prefix length L: every weight once, the
-    embedding once for the head, the adapter, the prefix + block K/V of every layer."""
+    embedding once for the head, the adapter, the prefix + block K/V of every layer
+    (kv_elem_bytes per cached element: 2 for bf16, 1 for an FP8 cache)."""
     s = shape
     D = s.head_dim
     per_layer = 2 * ((s.hq + 2 * s.hkv) * D * s.d + s.d * s.hq * D + 3 * s.ffn * s.d)
     w = s.n_layers * per_layer + 2 * s.d * s.d          # layers + W_sc
     head = 2 * s.vocab * s.d
-    kv = s.n_layers * 2 * 2 * s.hkv * D * (L + s.block)
+    kv = s.n_layers * 2 * kv_elem_bytes * s.hkv * D * (L + s.block)
     return w + head + kv
+
+
+FP8_CACHE_SCALES = (0.0625, 0.0625)     # k, v: |k|, |v| up to 28 before saturation
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_swiglu_qwen4b_counters.txt")
@@ -289,6 +293,7 @@ def main():
     ap.add_argument("--prompt", type=int, default=256)
     ap.add_argument("--seed", type=int, default=1234, help="seed of the model and prompt of every leg")
     ap.add_argument("--no-ops", action="store_true", help="skip the head and attention op leg")
+    ap.add_argument("--no-fp8-cache", action="store_true", help="skip the headline k with an FP8 KV cache")
     ap.add_argument("--seeds", default="1234,1235,1236",
                     help="seeds of the headline k: the first is --seed's run, each further seed draws a new "
                          "model and prompt; the reported value is the median (empty: --seed only)")
@@ -403,6 +408,22 @@ def main():
                       "bytes_per_block": rb / args.steps, "mean_prefix": L_mean}
         log(f"k={k}: {results[k]['tok_s']:.0f} tok/s, {results[k]['rounds_s']:.0f} rounds/s, "
             f"{results[k]['ms_per_block']:.2f} ms/block, {100 * results[k]['hbm_frac']:.1f}% of 8 TB/s")
+
+    # ---- the headline k with an FP8 e4m3 KV cache (same weights, prompt and rule)
+    fp8_cache = None
+    if ks and pipelined and not args.no_fp8_cache:
+        bf16_model = model
+        model = dlm.Model(shape, dev_w, cap=cap, kv_scales=FP8_CACHE_SCALES)
+        sec, wall, R = run(args.k, args.steps, args.warmup)
+        rb = sum(algorithmic_bytes(shape, args.prompt + B * i, kv_elem_bytes=1) * R for i in range(args.steps))
+        fp8_cache = {"k": args.k, "kv_scales": list(FP8_CACHE_SCALES), "tok_s": round(n_new / sec, 1),
+                     "ms_per_block": round(1e3 * sec / args.steps, 3), "hbm_frac": round(rb / sec / HBM_PEAK, 4),
+                     "bytes_per_block": rb / args.steps}
+        log(f"k={args.k} with an FP8 KV cache: {fp8_cache['tok_s']:.0f} tok/s, {fp8_cache['ms_per_block']:.2f} ms/block")
+        model.close()
+        del model
+        model = bf16_model
+        torch.cuda.empty_cache()
 
     # ---- dominant kernel: the FFN gate/up projection + SwiGLU, the round's largest weight
     # stream, launched alone exactly as inside the round (dlm_ffn_gate_up: same kernel, plan
@@ -544,7 +565,7 @@ def main():
         "prefill": {"tokens": args.prompt, "ms": round(prefill_ms[0], 3),
                     "tok_s": round(args.prompt / (prefill_ms[0] / 1e3), 1),
                     "how": "64-row forwards over pairs of 32-token prompt blocks, HIP events, first leg"},
-        "hbm_stream_measured": stream, "ops": ops,
+        "hbm_stream_measured": stream, "ops": ops, "fp8_cache": fp8_cache,
         "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
                   for k, r in results.items()},
         "roofline": roofline, "cpu_baseline": cpu, "moe": moe,

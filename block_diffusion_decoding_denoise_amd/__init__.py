@@ -78,7 +78,8 @@ class LayerWeights(ctypes.Structure):
 
 class KV(ctypes.Structure):
     _fields_ = [("k", ctypes.POINTER(ctypes.c_void_p)), ("v", ctypes.POINTER(ctypes.c_void_p)),
-                ("cap", ctypes.c_int), ("len_dev", ctypes.c_void_p), ("max_len", ctypes.c_int)]
+                ("cap", ctypes.c_int), ("len_dev", ctypes.c_void_p), ("max_len", ctypes.c_int),
+                ("kv_dtype", ctypes.c_int), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class DecodeViews(ctypes.Structure):
@@ -294,9 +295,11 @@ class Model:
     weights: mapping name -> torch tensor (device), names as in synth.Weights
     (``emb``, ``mask_emb``, ``w_sc``, ``final_norm``, ``l{i}.{attn_norm,wq,wk,wv,wo,ffn_norm,
     wg,wu,wd}``).  bf16 tensors are given as torch.bfloat16.
+    kv_scales: None for a cache in the model dtype, or (k_scale, v_scale) for an FP8 e4m3
+    cache (bf16 models): uint8 codes, stored value = scale * e4m3(code).
     """
 
-    def __init__(self, shape, weights, cap, max_len=None, device="cuda"):
+    def __init__(self, shape, weights, cap, max_len=None, device="cuda", kv_scales=None):
         self.shape = shape
         self.w = weights
         self.device = device
@@ -327,6 +330,9 @@ class Model:
         self.handle = h
         # KV cache and decode workspace
         tdt = torch.bfloat16 if dt == DLM_BF16 else torch.float32
+        if kv_scales is not None:
+            tdt = torch.uint8
+        self.kv_scales = kv_scales
         self.cap = cap
         self.k = [torch.zeros(s.hkv, cap, s.head_dim, dtype=tdt, device=device) for _ in range(s.n_layers)]
         # V is cached transposed in 32-position blocks, [hkv, cap/32, D, 32]
@@ -336,7 +342,9 @@ class Model:
         self._kptrs = (ctypes.c_void_p * s.n_layers)(*[t.data_ptr() for t in self.k])
         self._vptrs = (ctypes.c_void_p * s.n_layers)(*[t.data_ptr() for t in self.v])
         self.len_dev = torch.zeros(1, dtype=torch.int32, device=device)
-        self.kv = KV(self._kptrs, self._vptrs, cap, self.len_dev.data_ptr(), max_len or cap)
+        ks, vs = kv_scales if kv_scales is not None else (1.0, 1.0)
+        self.kv = KV(self._kptrs, self._vptrs, cap, self.len_dev.data_ptr(), max_len or cap,
+                     DLM_FP8_E4M3 if kv_scales is not None else dt, float(ks), float(vs))
         nb = L.dlm_decode_ws_bytes(self.handle, ctypes.byref(self.kv))
         if nb == 0:
             _check(-1, "dlm_decode_ws_bytes")

@@ -276,7 +276,7 @@ extern "C" int dlm_pack_activations(const void* x, int rows, int k, void* x_pack
 // ------------------------------------------------------------------ model
 struct GraphKey {
   std::tuple<int, float, int, int, int, const void*, const void*, const void*, const void*, const void*, const void*,
-             int, const void*>
+             int, const void*, int, float, float>
       t;
   bool operator<(const GraphKey& o) const { return t < o.t; }
 };
@@ -575,6 +575,11 @@ static int check_kv(const dlm_model* m, const dlm_kv* kv) {
   for (int l = 0; l < m->d.n_layers; ++l)
     DLM_REQUIRE(kv->k[l] && kv->v[l] && aligned16(kv->k[l]) && aligned16(kv->v[l]), DLM_ERR_ARG,
                 "kv layer %d: null or misaligned", l);
+  DLM_REQUIRE(kv->kv_dtype == m->d.dtype || (kv->kv_dtype == DLM_FP8_E4M3 && m->d.dtype == DLM_BF16),
+              DLM_ERR_DTYPE, "kv_dtype %d with a model of dtype %d", kv->kv_dtype, m->d.dtype);
+  if (kv->kv_dtype == DLM_FP8_E4M3)
+    DLM_REQUIRE(isfinite(kv->k_scale) && isfinite(kv->v_scale) && kv->k_scale > 0.f && kv->v_scale > 0.f,
+                DLM_ERR_ARG, "FP8 cache scales must be finite and positive");
   return DLM_OK;
 }
 
@@ -639,6 +644,9 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     e.cap = kv->cap;
     e.len_dev = kv->len_dev;
     e.rope_r = pow((double)d.rope_base, -2.0 / (double)D);
+    e.kv8 = kv->kv_dtype == DLM_FP8_E4M3;
+    e.k_inv = e.kv8 ? 1.0f / kv->k_scale : 1.0f;
+    e.v_inv = e.kv8 ? 1.0f / kv->v_scale : 1.0f;
     e.cont_dev = cont;
     if (bf) rc = gemm_bf16(pk + m->off_qkv[l], w.xn, m->n_qkv, d.d, MAP_QKV, e, m->pl_qkv, w.gemm_ws, st);
     else {
@@ -652,7 +660,8 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     if (last && last_kv_only) break;
     const float scale = 1.0f / sqrtf((float)D);
     if (bf) rc = attn_bf16(w.q, kv->k[l], kv->v[l], w.o, d.hq, d.hkv, D, d.block, nqb, kv->cap, scale, kv->len_dev,
-                           0, cont, model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st);
+                           0, cont, model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st,
+                           AttnKv{kv->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, kv->k_scale, kv->v_scale});
     else rc = attn_f32((const float*)w.q, (const float*)kv->k[l], (const float*)kv->v[l], (float*)w.o, d.hq, d.hkv,
                        D, B, kv->cap, scale, kv->len_dev, 0, cont, st);
     if (rc) return rc;
@@ -892,7 +901,7 @@ static int launch_block_graph(const dlm_model* m, const dlm_commit_rule* rule, c
   const void* kv0 = kv->k[0];
   key.t = std::make_tuple(rule->mode, rule->tau, rule->k, rule->forced_top1, rule->max_rounds, (const void*)tokens,
                           (const void*)state, ws, kv0, (const void*)kv->len_dev, (const void*)kv->v[0], pipelined,
-                          (const void*)prev_tokens);
+                          (const void*)prev_tokens, kv->kv_dtype, kv->k_scale, kv->v_scale);
   std::lock_guard<std::mutex> lock(mm->mu);
   auto it = mm->graphs.find(key);
   if (it == mm->graphs.end()) {

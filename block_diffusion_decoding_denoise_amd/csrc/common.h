@@ -52,6 +52,30 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- FP8 e4m3 (OCP)
+// e4m3 code (OCP: bias 7, 3 mantissa bits, largest 448, subnormal step 2^-9) of v rounded to
+// nearest, ties to even, saturating at 448.
+__device__ inline uint32_t e4m3_code(float v) {
+  const uint32_t sign = v < 0.f ? 0x80u : 0u;
+  const float a = fabsf(v);
+  float q;
+  if (a >= 448.f) {
+    q = 448.f;
+  } else {
+    int ex;
+    frexpf(a, &ex);
+    const int E = a > 0.f ? max(ex - 1, -6) : -6;
+    q = rintf(a * ldexpf(1.f, 3 - E)) * ldexpf(1.f, E - 3);    // exact power-of-two scalings
+    q = fminf(q, 448.f);
+  }
+  if (q == 0.f) return sign;
+  int ex;
+  frexpf(q, &ex);
+  const int E = ex - 1;
+  if (E < -6) return sign | (uint32_t)(q * 512.f);                                   // subnormal
+  return sign | ((uint32_t)(E + 7) << 3) | (uint32_t)(q * ldexpf(1.f, 3 - E) - 8.f);
+}
+
 // ---------------------------------------------------------------- buffer loads
 // Raw buffer loads: an offset at or beyond num_records returns zeros without touching memory,
 // so a prefetch ring can run past the end of a range with no branches.

@@ -70,6 +70,13 @@ __device__ inline void store_act(void* base, size_t idx, float v, int bf16) {
   else ((float*)base)[idx] = v;
 }
 
+// a K/V cache element: the stored (bf16 or f32) value, or for an FP8 cache the e4m3 code of
+// the bf16 value times the inverse cache scale
+__device__ inline void store_kv(const EpiParams& e, void* base, size_t idx, float v, float inv) {
+  if (e.kv8) ((uint8_t*)base)[idx] = (uint8_t)e4m3_code(bf2f(f2bf(v)) * inv);
+  else store_act(base, idx, v, e.bf16_out);
+}
+
 __device__ inline float load_act(const void* base, size_t idx, int bf16) {
   return bf16 ? bf2f(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
 }
@@ -126,8 +133,8 @@ __device__ inline void epi_qk_rope(const EpiParams& e, int m, int part, int head
   } else {
     if (L + m >= e.cap) return;   // a prefix length past the cache capacity writes nothing
     const size_t o = ((size_t)head * e.cap + (L + m)) * e.D + j;
-    store_act(e.k_cache, o, a2, e.bf16_out);
-    store_act(e.k_cache, o + e.D / 2, b2, e.bf16_out);
+    store_kv(e, e.k_cache, o, a2, e.k_inv);
+    store_kv(e, e.k_cache, o + e.D / 2, b2, e.k_inv);
   }
 }
 
@@ -136,7 +143,7 @@ __device__ inline void epi_v(const EpiParams& e, int m, int rel, float v) {
   const int L = prefix_len(e);
   if (L + m >= e.cap) return;
   const int head = rel / e.D, j = rel % e.D;
-  store_act(e.v_cache, vt_index(head, e.D, e.cap, L + m, j), v, e.bf16_out);
+  store_kv(e, e.v_cache, vt_index(head, e.D, e.cap, L + m, j), v, e.v_inv);
 }
 
 __device__ inline void epi_swiglu(const EpiParams& e, int m, int j, float g, float u) {

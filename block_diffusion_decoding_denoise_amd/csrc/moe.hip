@@ -62,29 +62,6 @@ __device__ inline int mx_shared_exp(float amax, int emax) {
   return max(-127, min(127, ex - 1 - emax));
 }
 
-// e4m3 code (OCP: bias 7, 3 mantissa bits, largest 448, subnormal step 2^-9) of v rounded to
-// nearest, ties to even, saturating at 448.
-__device__ inline uint32_t e4m3_code(float v) {
-  const uint32_t sign = v < 0.f ? 0x80u : 0u;
-  const float a = fabsf(v);
-  float q;
-  if (a >= 448.f) {
-    q = 448.f;
-  } else {
-    int ex;
-    frexpf(a, &ex);
-    const int E = a > 0.f ? max(ex - 1, -6) : -6;
-    q = rintf(a * ldexpf(1.f, 3 - E)) * ldexpf(1.f, E - 3);    // exact power-of-two scalings
-    q = fminf(q, 448.f);
-  }
-  if (q == 0.f) return sign;
-  int ex;
-  frexpf(q, &ex);
-  const int E = ex - 1;
-  if (E < -6) return sign | (uint32_t)(q * 512.f);                                   // subnormal
-  return sign | ((uint32_t)(E + 7) << 3) | (uint32_t)(q * ldexpf(1.f, 3 - E) - 8.f);
-}
-
 // SA: the byte of sa that holds the A scale (four row groups share one scale word)
 template <int SA = 0>
 __device__ inline f32x4_t mfma_mx(u32x4_t a_fp4, u32x4_t b_lo, u32x4_t b_hi, int sa, int sb, f32x4_t c) {

@@ -282,7 +282,10 @@ int dlm_ffn_gate_up(const dlm_model* m, int layer, const void* x_packed, void* a
 /* ------------------------------------------------------------------------------------
  * KV cache.  k[l]: device base of layer l's keys [hkv, cap, D]; v[l]: its values stored
  * transposed in 32-position blocks, [hkv, cap/32, D, 32] (as for dlm_block_attn); model
- * dtype; cap % 32 == 0.
+ * dtype, or FP8 for bf16 models (kv_dtype = DLM_FP8_E4M3: one e4m3 code per element, the
+ * stored value being k_scale (v_scale) times the code's value; the layers write the code of
+ * their bf16 k (v) divided by the scale, nearest-even, saturating at 448, and attend as
+ * dlm_block_attn does over such a cache); cap % 32 == 0.
  * len_dev: device int32 holding the committed prefix length L.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
@@ -291,6 +294,8 @@ typedef struct {
   int cap;
   int32_t* len_dev;
   int max_len;               /* largest L + block the caller will use (sizes workspaces) */
+  int kv_dtype;              /* the model dtype, or DLM_FP8_E4M3 (bf16 models) */
+  float k_scale, v_scale;    /* FP8 cache scales: finite and > 0 (ignored otherwise) */
 } dlm_kv;
 
 /* ------------------------------------------------------------------------------------

@@ -30,10 +30,22 @@ def _upload(w: synth.Weights):
     return {n: storage(w[n], dt) for n in w.names_dense()}
 
 
-def _gpu_model(shape, seed, cap, max_len=None):
+def _gpu_model(shape, seed, cap, max_len=None, kv_scales=None):
     dlm = _dlm()
     w = synth.Weights(shape, seed)
-    return dlm.Model(shape, _upload(w), cap=cap, max_len=max_len), w
+    return dlm.Model(shape, _upload(w), cap=cap, max_len=max_len, kv_scales=kv_scales), w
+
+
+def _cache_values(m, kv_scales):
+    """The GPU KV cache as float64 [hkv, cap, D] per layer (FP8 codes decoded and scaled)."""
+    dlm = _dlm()
+    if kv_scales is None:
+        ks = [t.float().cpu().numpy().astype(np.float64) for t in m.k]
+        vs = [dlm.v_cache_to_natural(t).float().cpu().numpy().astype(np.float64) for t in m.v]
+    else:
+        ks = [kv_scales[0] * oracle.e4m3_decode(t.cpu().numpy()) for t in m.k]
+        vs = [kv_scales[1] * oracle.e4m3_decode(dlm.v_cache_to_natural(t).cpu().numpy()) for t in m.v]
+    return ks, vs
 
 
 def test_tiny_fp32_full_trajectory():
@@ -91,7 +103,7 @@ def _valid_commit(rule_args, maxprob, open_rows, chosen):
     return sel
 
 
-def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1):
+def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_scales=None):
     """Run rounds one at a time; after each round recompute it with the oracle from the
     GPU's own round-start state and compare the statistics and the commit.
 
@@ -101,10 +113,11 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1):
     oracle's within their tolerance.  Such differences are counted, and the ones whose
     oracle top-2 gap is below 1e-3 are reported separately."""
     dlm = _dlm()
-    _say(f"lockstep {shape.name} d={shape.d} L={shape.n_layers} seed={seed}")
+    _say(f"lockstep {shape.name} d={shape.d} L={shape.n_layers} seed={seed} kv_scales={kv_scales}")
     cap = prompt_len + (n_blocks + 1) * shape.block
-    m, w = _gpu_model(shape, seed, cap)
-    om = OracleModel(shape, w, Prec(shape.dtype))
+    m, w = _gpu_model(shape, seed, cap, kv_scales=kv_scales)
+    prec = Prec(shape.dtype, kv_scales=kv_scales)
+    om = OracleModel(shape, w, prec)
     prompt = synth.prompt_ids(shape, prompt_len, seed)
     m.set_len(0)
     m.prefill(torch.from_numpy(prompt))
@@ -129,13 +142,12 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1):
             tokens = m.tokens.cpu().numpy().copy()
             pe_prev = m.view("pe", (B, d), torch.float32).cpu().numpy().astype(np.float64)
             L = int(m.len_dev.item())
-            kv = KVCache([t.float().cpu().numpy().astype(np.float64) for t in m.k],
-                         [dlm.v_cache_to_natural(t).float().cpu().numpy().astype(np.float64) for t in m.v], L)
+            kv = KVCache(*_cache_values(m, kv_scales), L)
             m.decode_round(rule)
             torch.cuda.synchronize()
             if r % check_every == 0:
                 res = oracle.denoise_round(om, kv, tokens.copy(), committed.copy(), None if r == 0 else pe_prev, r,
-                                           orule, Prec(shape.dtype), want_logits=True)
+                                           orule, prec, want_logits=True)
                 g = {n: m.view(n, (B,), dt).cpu().numpy() for n, dt in
                      (("lse", torch.float32), ("entropy", torch.float32), ("maxprob", torch.float32),
                       ("argmax", torch.int32))}
@@ -175,6 +187,45 @@ def test_small_bf16_lockstep():
     s = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
                           vocab=3001)
     _lockstep(s, 1234, 64, 2, (1, 0.0, 6, 0, 32))
+
+
+def test_small_bf16_fp8_cache_lockstep():
+    """The same lockstep with an FP8 e4m3 KV cache (power-of-two scales, so both sides quantise
+    the same bf16 values exactly alike)."""
+    s = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
+                          vocab=3001)
+    _lockstep(s, 1237, 64, 2, (1, 0.0, 6, 0, 32), kv_scales=(0.125, 0.0625))
+
+
+def test_prefill_fp8_cache_matches_oracle_cache():
+    """Prefill into an FP8 cache: the codes the layers write against the oracle's quantised
+    cache.  Layer 0 sees identical bf16 inputs, so its codes differ only where a k or v lies
+    within one bf16 unit of an e4m3 rounding boundary."""
+    s = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
+                          vocab=3001)
+    sc = (0.125, 0.0625)
+    m, w = _gpu_model(s, 1238, cap=128, kv_scales=sc)
+    prompt = synth.prompt_ids(s, 96, 8)
+    m.set_len(0)
+    m.prefill(torch.from_numpy(prompt))
+    torch.cuda.synchronize()
+    om = OracleModel(s, w, Prec("bf16", kv_scales=sc))
+    kv = KVCache.empty(s, 128)
+    oracle.prefill(om, kv, prompt, Prec("bf16", kv_scales=sc))
+    gks, gvs = _cache_values(m, sc)
+    for l in range(s.n_layers):
+        for g, o, scale in ((gks[l][:, :96], kv.k[l][:, :96], sc[0]), (gvs[l][:, :96], kv.v[l][:, :96], sc[1])):
+            step = scale * np.exp2(np.floor(np.log2(np.maximum(np.abs(o) / scale, 2.0 ** -6))) - 3)
+            i = np.unravel_index(np.argmax(np.abs(g - o) / step), g.shape)
+            _say(f"layer {l} scale {scale}: max |o| {np.abs(o).max():.4g}, differing {np.mean(g != o):.4f}, "
+                 f"worst at {i}: gpu {g[i]:.6g} oracle {o[i]:.6g} step {step[i]:.4g}")
+            if l == 0:
+                # identical inputs: a code differs only across a rounding boundary, by one step
+                assert np.all(np.abs(g - o) <= 1.01 * step), np.abs(g - o).max()
+                assert np.mean(g != o) < 1e-2, np.mean(g != o)
+            else:
+                # the bf16-cache test's tolerance for a later layer, plus one e4m3 step
+                assert np.all(np.abs(g - o) <= 3e-2 + 2e-2 * np.abs(o) + 1.01 * step), np.abs(g - o).max()
 
 
 def test_small_bf16_threshold_lockstep():

@@ -34,11 +34,11 @@ def _dlm():
     return dlm
 
 
-def _model(shape, seed, cap):
+def _model(shape, seed, cap, kv_scales=None):
     dlm = _dlm()
     w = synth.Weights(shape, seed)
     up = {n: storage(w[n], shape.dtype) for n in w.names_dense()}
-    return dlm.Model(shape, up, cap=cap), w
+    return dlm.Model(shape, up, cap=cap, kv_scales=kv_scales), w
 
 
 def _run(dlm, m, prompt, n_blocks, rule, pipelined):
@@ -58,17 +58,19 @@ SMALL = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq
 QWEN4B_2L = synth.small_shape(synth.QWEN4B, name="qwen4b-2-layers", n_layers=2)
 
 
-@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args", [
-    (SMALL, 1234, 64, 3, ("fixed_k", 6)),
-    (SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32)),
-    (SMALL, 1236, 96, 2, ("fixed_k", 32)),
-    (QWEN4B_2L, 1234, 256, 3, ("fixed_k", 6)),
-], ids=["small-k6", "small-threshold", "small-k32", "qwen4b-2l-k6"])
-def test_pipelined_bitexact_bf16(shape, seed, prompt_len, n_blocks, rule_args):
+@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args,kv_scales", [
+    (SMALL, 1234, 64, 3, ("fixed_k", 6), None),
+    (SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32), None),
+    (SMALL, 1236, 96, 2, ("fixed_k", 32), None),
+    (QWEN4B_2L, 1234, 256, 3, ("fixed_k", 6), None),
+    (SMALL, 1237, 64, 3, ("fixed_k", 6), (0.125, 0.0625)),
+    (QWEN4B_2L, 1238, 256, 2, ("fixed_k", 6), (0.25, 0.125)),
+], ids=["small-k6", "small-threshold", "small-k32", "qwen4b-2l-k6", "small-k6-fp8-cache", "qwen4b-2l-k6-fp8-cache"])
+def test_pipelined_bitexact_bf16(shape, seed, prompt_len, n_blocks, rule_args, kv_scales):
     dlm = _dlm()
     _say(f"pipelined vs separate commit passes: {shape.name} seed {seed} prompt {prompt_len} "
-         f"blocks {n_blocks} rule {rule_args}")
-    m, _ = _model(shape, seed, cap=prompt_len + 32 * n_blocks)
+         f"blocks {n_blocks} rule {rule_args} kv_scales {kv_scales}")
+    m, _ = _model(shape, seed, cap=prompt_len + 32 * n_blocks, kv_scales=kv_scales)
     rule = getattr(dlm.CommitRule, rule_args[0])(*rule_args[1:])
     prompt = synth.prompt_ids(shape, prompt_len, seed)
     t0, s0, k0, v0 = _run(dlm, m, prompt, n_blocks, rule, pipelined=False)
