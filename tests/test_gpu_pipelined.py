@@ -92,12 +92,13 @@ MOE_SMALL = synth.small_shape(synth.MOE16B, name="moe-small-pipelined", n_layers
 MOE_E256 = synth.small_shape(synth.MOE16B, name="moe-e256-2-layers", n_layers=2, vocab=4096)
 
 
-@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args", [
-    (MOE_SMALL, 1234, 64, 3, ("fixed_k", 6)),
-    (MOE_SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32)),
-    (MOE_E256, 1236, 64, 3, ("fixed_k", 6)),
-], ids=["moe-small-k6", "moe-small-threshold", "moe-e256-k6"])
-def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args):
+@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args,kv_scales", [
+    (MOE_SMALL, 1234, 64, 3, ("fixed_k", 6), None),
+    (MOE_SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32), None),
+    (MOE_E256, 1236, 64, 3, ("fixed_k", 6), None),
+    (MOE_SMALL, 1240, 64, 3, ("fixed_k", 6), (0.125, 0.125)),
+], ids=["moe-small-k6", "moe-small-threshold", "moe-e256-k6", "moe-small-k6-fp8-cache"])
+def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args, kv_scales):
     """MoE models: the 64-row fused pass routes the previous block's commit rows and round 0's
     rows together (up to 64 rows per expert, shared experts in two slots); every row's routing,
     expert products and slot outputs are those of the separate passes, so tokens, round states
@@ -109,7 +110,7 @@ def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args):
     w = synth.Weights(shape, seed)
     dev = {n: storage(w[n], "bf16") for n in w.names_dense() if not n.endswith(".router")}
     dev.update(moe_device_weights(w))
-    m = dlm.Model(shape, dev, cap=prompt_len + 32 * n_blocks)
+    m = dlm.Model(shape, dev, cap=prompt_len + 32 * n_blocks, kv_scales=kv_scales)
     rule = getattr(dlm.CommitRule, rule_args[0])(*rule_args[1:])
     prompt = synth.prompt_ids(shape, prompt_len, seed)
     t0, s0, k0, v0 = _run(dlm, m, prompt, n_blocks, rule, pipelined=False)
