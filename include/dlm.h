@@ -85,10 +85,10 @@ const char* dlm_last_error(void);
  *   once before first use (the kernels leave it zeroed again).
  *   FP8 cache (kv_dtype = DLM_FP8_E4M3, with dtype = DLM_BF16): k_cache and v_cache hold one
  *   OCP FP8 e4m3 code per element in the same layouts, and the stored key (value) is
- *   k_scale (v_scale) times the code's value; q and out stay bf16.  This is the FP8 KV cache
- *   the pages list among the long-context memory levers ([ORL-blog] "What shipped": the
- *   attention over the prefix cache is the part of a round that grows with context); the
- *   format, one e4m3 code per element with one scale per cache, is this library's reading.
+ *   k_scale (v_scale) times the code's value; q and out stay bf16.  [ORL-blog] "What shipped"
+ *   states that the engine keeps its KV cache in FP8 on Blackwell; it gives no element format
+ *   or scaling, and one e4m3 code per element with one scale per cache is this library's
+ *   reading.
  *   The caller writes the codes; NaN codes must not occur at positions below L + B.
  * ------------------------------------------------------------------------------------ */
 typedef struct {

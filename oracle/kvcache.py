@@ -1,10 +1,9 @@
 """FP8 KV cache: keys and values stored as e4m3 codes with one scale per cache.
 
-The pages name an FP8 KV cache among the memory levers of block decoding at long
-context ([ORL-blog] "What shipped": the attention over the prefix KV cache is
-the part of a round that grows with context; [ORL-card] "The paper's
-evaluation pipeline": block decoding against a prefix KV cache).  They fix no
-format.  The reading taken here is the plainest one: every stored K (V) element
+[ORL-blog] "What shipped" states that the engine keeps its KV cache in FP8 on
+Blackwell; [ORL-card] "The paper's evaluation pipeline" decodes blocks against
+a prefix KV cache.  No element format or scaling is given.  The reading taken
+here is the plainest one: every stored K (V) element
 is an OCP FP8 e4m3 code (bias 7, 3 mantissa bits, subnormals down to 2^-9,
 largest finite 448, codes 0x7F / 0xFF NaN, no infinities), and the cache as a
 whole has one float scale, k_scale (v_scale), so that the stored key is
