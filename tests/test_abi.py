@@ -110,3 +110,30 @@ def test_valid_call_without_device_is_unsupported():
     L = dlm.lib()
     r = dlm.CommitRule.threshold()
     assert L.dlm_commit(ctypes.byref(r), 32, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+
+
+def test_kv_cache_format_validation():
+    """The KV descriptor's format is checked on the host before anything is enqueued: a cache
+    in the model dtype or FP8 e4m3 (bf16 models) with finite positive scales is accepted; the
+    workspace query returns 0 for anything else and leaves a message."""
+    L = dlm.lib()
+    desc = dlm.ModelDesc(dlm.DLM_BF16, 2, 256, 4, 2, 64, 512, 1000, 32, 1e4, 1e-6, 0, 0, 0, 0)
+    layers = (dlm.LayerWeights * 2)()
+    for lw in layers:
+        for name, _ in dlm.LayerWeights._fields_[:9]:
+            setattr(lw, name, FAKE.value)
+    h = ctypes.c_void_p()
+    assert L.dlm_model_create(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, layers, FAKE, ctypes.byref(h)) == 0
+    ptrs = (ctypes.c_void_p * 2)(FAKE.value, FAKE.value)
+    try:
+        def ws(kv_dtype, ks=1.0, vs=1.0):
+            kv = dlm.KV(ptrs, ptrs, 256, FAKE.value, 256, kv_dtype, ks, vs)
+            return L.dlm_decode_ws_bytes(h, ctypes.byref(kv))
+        assert ws(dlm.DLM_BF16) > 0
+        assert ws(dlm.DLM_FP8_E4M3, 0.125, 0.5) == ws(dlm.DLM_BF16)    # same workspace either way
+        for bad in [(dlm.DLM_F32,), (dlm.DLM_MXFP4,), (dlm.DLM_FP8_E4M3, 0.0, 1.0), (dlm.DLM_FP8_E4M3, 1.0, -1.0),
+                    (dlm.DLM_FP8_E4M3, float("nan"), 1.0), (dlm.DLM_FP8_E4M3, 1.0, float("inf"))]:
+            assert ws(*bad) == 0, bad
+            assert L.dlm_last_error()
+    finally:
+        L.dlm_model_destroy(h)
