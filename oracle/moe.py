@@ -15,7 +15,12 @@ Microscaling formats instead of NVFP4:
     experts always added with weight 1.
 Every e2m1 x 2^e value is exact in float64, so the oracle decodes weights
 exactly.  Pinned by tests/test_oracle_moe.py (format tables, round trips, a
-top-k equal to all experts reducing to a dense mixture, one-hot routing).
+top-k equal to all experts reducing to a dense mixture, one-hot routing) and by
+tests/test_oracle_moe_expert.py: one expert and the whole sublayer (norm,
+router, top-k, shared expert, residual) against scalar-loop brute force with an
+independently enumerated e4m3 table, on MXFP4-exact weights; the same checks
+reject copies with gate and up swapped, the activation re-quantisation dropped,
+the shared expert dropped or the norm gain ignored.
 """
 from __future__ import annotations
 
