@@ -54,8 +54,9 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
 
 // ---------------------------------------------------------------- FP8 e4m3 (OCP)
 // e4m3 code (OCP: bias 7, 3 mantissa bits, largest 448, subnormal step 2^-9) of v rounded to
-// nearest, ties to even, saturating at 448.
+// nearest, ties to even, saturating at 448; NaN gives the NaN code 0x7F.
 __device__ inline uint32_t e4m3_code(float v) {
+  if (v != v) return 0x7Fu;
   const uint32_t sign = v < 0.f ? 0x80u : 0u;
   const float a = fabsf(v);
   float q;

@@ -49,8 +49,8 @@ struct EpiParams {
   const int32_t* len_dev; // prefix length L (device) ...
   int len_host;           // ... or host value when len_dev == nullptr
   double rope_r;          // base^(-2/D)
-  int kv8;                // the caches hold FP8 e4m3 codes of (bf16 value) * k_inv / v_inv
-  float k_inv, v_inv;
+  int kv8;                // the caches hold FP8 e4m3 codes of (bf16 value) / k_scale (v_scale)
+  float k_scale, v_scale;
   // SWIGLU
   void* act_out;          // [M, F]
   int F;

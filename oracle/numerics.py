@@ -43,8 +43,10 @@ class Prec:
     compute: np.float64 for parity, np.float32 for the CPU timing baseline.
     kv_scales: None (the KV cache holds the stored k and v), or (k_scale, v_scale) for an
              FP8 cache: the cache then holds scale * e4m3(value / scale), the value being the
-             bf16 k (v) after RoPE, rounded to nearest-even e4m3 with saturation
-             (oracle/kvcache.py states the format reading).
+             bf16 k (v) after RoPE, rounded to nearest-even e4m3 with saturation (NaN stays
+             NaN), the quotient value / scale being the single-precision quotient of the
+             stored bf16 value and the single-precision scale (the scale is a float of the
+             cache format; oracle/kvcache.py states the format reading).
     """
     storage: str = "f32"
     compute: type = np.float64
@@ -55,8 +57,9 @@ class Prec:
         if self.kv_scales is None:
             return x
         from .moe import e4m3_round
-        s = float(self.kv_scales[which])
-        return (s * e4m3_round(np.asarray(x, dtype=np.float64) / s)).astype(self.compute, copy=False)
+        s = np.float32(self.kv_scales[which])
+        quot = (np.asarray(x, dtype=np.float64).astype(np.float32) / s).astype(np.float64)
+        return (float(s) * e4m3_round(quot)).astype(self.compute, copy=False)
 
     def act(self, x: np.ndarray) -> np.ndarray:
         """Round an activation at a storage point."""

@@ -6,6 +6,8 @@ import os
 import numpy as np
 
 import synth
+import oracle
+from oracle import Prec
 from oracle import attention, e4m3_decode, e4m3_encode, attention_fp8_cache
 from oracle.moe import e4m3_round
 
@@ -133,3 +135,23 @@ def test_fp8_cache_layer_equals_bf16_cache_on_representable_values():
         kv.v[0][:, :L] = 2.0 * e4m3_decode(synth.e4m3_codes(4, "kv8.vprev", (1, L, 4)))
         outs.append(dense_layer(x, W, kv.k[0], kv.v[0], L, s, prec))
     np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_fp8_cache_quotient_is_single_precision():
+    """The code written for a cached value is that of the single-precision quotient of the
+    bf16 value and the cache scale (a float of the cache format).  For v = 0.02490234375 and
+    scale 1.7f the exact quotient lies just below the midpoint 0.0146484375 of two e4m3
+    values, while its single-precision rounding is the midpoint, which ties to the even code
+    0x08 (0.015625) instead of 0x07 (0.013671875)."""
+    import torch
+    v = np.array([0.02490234375])
+    s = float(np.float32(1.7))
+    q32 = (torch.tensor(v, dtype=torch.float32) / torch.tensor(s, dtype=torch.float32)).item()
+    assert q32 == 0.0146484375 and v[0] / s < 0.0146484375
+    prec = Prec("bf16", kv_scales=(1.7, 1.0))
+    stored = prec.kv_store(v, 0)
+    assert stored[0] == s * 0.015625
+    assert oracle.e4m3_encode(stored / s)[0] == 0x08
+    # NaN stays NaN (the encoder maps it to the NaN code)
+    assert np.isnan(prec.kv_store(np.array([np.nan]), 0)[0])
+    assert oracle.e4m3_encode(np.array([np.nan]))[0] == 0x7F
