@@ -133,6 +133,8 @@ def lib():
         "dlm_commit_pass": (i, [vp, P(KV), vp, vp, sz, vp]),
         "dlm_ffn_gate_up_ws_bytes": (sz, [vp]),
         "dlm_ffn_gate_up": (i, [vp, i, vp, vp, vp, sz, vp]),
+        "dlm_block_graph_key": (i, [vp, P(CommitRule), P(KV), vp, i, vp, vp, vp, P(ctypes.c_uint64), i]),
+        "dlm_model_graph_count": (i, [vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

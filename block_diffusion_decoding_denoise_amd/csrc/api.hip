@@ -274,12 +274,11 @@ extern "C" int dlm_pack_activations(const void* x, int rows, int k, void* x_pack
 }
 
 // ------------------------------------------------------------------ model
-struct GraphKey {
-  std::tuple<int, float, int, int, int, const void*, const void*, const void*, const void*, const void*, const void*,
-             int, const void*, int, float, float>
-      t;
-  bool operator<(const GraphKey& o) const { return t < o.t; }
-};
+// Everything a captured block graph bakes in: the rule, every buffer address the kernels
+// take (tokens, state, workspace, prefix length, each layer's K and V base), and the cache
+// geometry and format (capacity strides, the max_len-dependent attention split plan and
+// workspace offsets, FP8 scales).  A launch whose key differs captures a new graph.
+typedef std::vector<uint64_t> GraphKey;
 
 struct dlm_model {
   dlm_model_desc d;
@@ -645,8 +644,8 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     e.len_dev = kv->len_dev;
     e.rope_r = pow((double)d.rope_base, -2.0 / (double)D);
     e.kv8 = kv->kv_dtype == DLM_FP8_E4M3;
-    e.k_inv = e.kv8 ? 1.0f / kv->k_scale : 1.0f;
-    e.v_inv = e.kv8 ? 1.0f / kv->v_scale : 1.0f;
+    e.k_scale = e.kv8 ? kv->k_scale : 1.0f;
+    e.v_scale = e.kv8 ? kv->v_scale : 1.0f;
     e.cont_dev = cont;
     if (bf) rc = gemm_bf16(pk + m->off_qkv[l], w.xn, m->n_qkv, d.d, MAP_QKV, e, m->pl_qkv, w.gemm_ws, st);
     else {
@@ -891,6 +890,42 @@ extern "C" int dlm_ffn_gate_up(const dlm_model* m, int layer, const void* x_pack
                    ws, (hipStream_t)stream);
 }
 
+static void block_graph_key(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                            const int32_t* prev_tokens, int pipelined, const int32_t* tokens,
+                            const dlm_round_state* state, const void* ws, GraphKey* key) {
+  auto bits = [](float f) { uint32_t u; memcpy(&u, &f, 4); return (uint64_t)u; };
+  auto ptr = [](const void* p) { return (uint64_t)(uintptr_t)p; };
+  key->assign({(uint64_t)rule->mode, bits(rule->tau), (uint64_t)rule->k, (uint64_t)rule->forced_top1,
+               (uint64_t)rule->max_rounds, ptr(tokens), ptr(state), ptr(ws), ptr(kv->len_dev), (uint64_t)pipelined,
+               ptr(prev_tokens), (uint64_t)kv->kv_dtype, bits(kv->k_scale), bits(kv->v_scale), (uint64_t)kv->cap,
+               (uint64_t)kv->max_len, (uint64_t)m->d.n_layers});
+  for (int l = 0; l < m->d.n_layers; ++l) {
+    key->push_back(ptr(kv->k[l]));
+    key->push_back(ptr(kv->v[l]));
+  }
+}
+
+extern "C" int dlm_block_graph_key(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                                   const int32_t* prev_tokens, int pipelined, const int32_t* tokens,
+                                   const dlm_round_state* state, const void* ws, uint64_t* words, int max_words) {
+  int rc = check_kv(m, kv);
+  if (rc) return rc;
+  if ((rc = check_rule(rule))) return rc;
+  DLM_REQUIRE(words && max_words >= 0, DLM_ERR_ARG, "null key buffer");
+  GraphKey key;
+  block_graph_key(m, rule, kv, prev_tokens, pipelined, tokens, state, ws, &key);
+  DLM_REQUIRE((size_t)max_words >= key.size(), DLM_ERR_ARG, "key needs %zu words", key.size());
+  memcpy(words, key.data(), key.size() * sizeof(uint64_t));
+  return (int)key.size();
+}
+
+extern "C" int dlm_model_graph_count(const dlm_model* m) {
+  DLM_REQUIRE(m, DLM_ERR_ARG, "model is null");
+  dlm_model* mm = const_cast<dlm_model*>(m);
+  std::lock_guard<std::mutex> lock(mm->mu);
+  return (int)mm->graphs.size();
+}
+
 // Captures (once per key) and launches the graph of one block.
 static int launch_block_graph(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
                               const int32_t* prev_tokens, int pipelined, int32_t* tokens, dlm_round_state* state,
@@ -898,10 +933,7 @@ static int launch_block_graph(const dlm_model* m, const dlm_commit_rule* rule, c
   dlm_model* mm = const_cast<dlm_model*>(m);
   DecodeWs w = decode_layout(m, kv, (char*)ws);
   GraphKey key;
-  const void* kv0 = kv->k[0];
-  key.t = std::make_tuple(rule->mode, rule->tau, rule->k, rule->forced_top1, rule->max_rounds, (const void*)tokens,
-                          (const void*)state, ws, kv0, (const void*)kv->len_dev, (const void*)kv->v[0], pipelined,
-                          (const void*)prev_tokens, kv->kv_dtype, kv->k_scale, kv->v_scale);
+  block_graph_key(m, rule, kv, prev_tokens, pipelined, tokens, state, ws, &key);
   std::lock_guard<std::mutex> lock(mm->mu);
   auto it = mm->graphs.find(key);
   if (it == mm->graphs.end()) {

@@ -383,6 +383,18 @@ typedef struct {
 int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* ws, size_t ws_bytes,
                          dlm_decode_views* out);
 
+/* Graph cache diagnostics (host only, no device work).  dlm_block_graph_key writes the key
+ * under which dlm_decode_block (pipelined = 0) or dlm_decode_block_pipelined (pipelined = 1)
+ * caches its captured graph for these arguments into words[0 .. n) and returns n (or a
+ * negative status; DLM_ERR_ARG when max_words < n): the rule, the tokens, state, workspace and
+ * prefix-length addresses, every layer's K and V base, the cache capacity, max_len, format and
+ * scales.  Launches whose keys differ never share a graph.  dlm_model_graph_count returns the
+ * number of graphs the model holds. */
+int dlm_block_graph_key(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                        const int32_t* prev_tokens, int pipelined, const int32_t* tokens,
+                        const dlm_round_state* state, const void* ws, uint64_t* words, int max_words);
+int dlm_model_graph_count(const dlm_model* m);
+
 /* One round only (no commit pass), from the state held in ws (tests: lockstep parity).
  * round_index is the index of this round in the block (device state is used for the
  * commit; the host value only selects nothing and is accepted for logging). */

@@ -137,3 +137,50 @@ def test_kv_cache_format_validation():
             assert L.dlm_last_error()
     finally:
         L.dlm_model_destroy(h)
+
+
+def test_graph_key_covers_cache_geometry_and_every_layer():
+    """The key a block graph is cached under changes with the cache capacity, max_len, the FP8
+    scales and any layer's K or V base (host only: a stale graph would replay wrong strides or
+    write freed memory)."""
+    L = dlm.lib()
+    n_layers = 3
+    desc = dlm.ModelDesc(dlm.DLM_BF16, n_layers, 256, 4, 2, 64, 512, 1000, 32, 1e4, 1e-6, 0, 0, 0, 0)
+    layers = (dlm.LayerWeights * n_layers)()
+    for lw in layers:
+        for name, _ in dlm.LayerWeights._fields_[:9]:
+            setattr(lw, name, FAKE.value)
+    h = ctypes.c_void_p()
+    assert L.dlm_model_create(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, layers, FAKE, ctypes.byref(h)) == 0
+    rule = dlm.CommitRule.fixed_k(6)
+    words = (ctypes.c_uint64 * 256)()
+
+    def key(k_ptrs, v_ptrs, cap=512, max_len=512, kv_dtype=dlm.DLM_BF16, ks=1.0, vs=1.0, pipelined=0):
+        kp = (ctypes.c_void_p * n_layers)(*k_ptrs)
+        vp = (ctypes.c_void_p * n_layers)(*v_ptrs)
+        kv = dlm.KV(kp, vp, cap, FAKE.value, max_len, kv_dtype, ks, vs)
+        n = L.dlm_block_graph_key(h, ctypes.byref(rule), ctypes.byref(kv), None, pipelined, FAKE, FAKE, FAKE,
+                                  words, 256)
+        assert n > 0, L.dlm_last_error()
+        return tuple(words[:n])
+
+    try:
+        ks = [0x100000 * (i + 1) for i in range(n_layers)]
+        vs = [0x1000000 * (i + 1) for i in range(n_layers)]
+        base = key(ks, vs)
+        assert key(ks, vs) == base
+        assert key(ks, vs, cap=1024) != base
+        assert key(ks, vs, max_len=256) != base
+        assert key(ks[:2] + [0x900000], vs) != base          # the last layer's K reallocated
+        assert key(ks, [vs[0], 0x9000000, vs[2]]) != base     # a middle layer's V reallocated
+        assert key(ks, vs, kv_dtype=dlm.DLM_FP8_E4M3, ks=0.5, vs=0.5) != key(ks, vs, kv_dtype=dlm.DLM_FP8_E4M3,
+                                                                           ks=0.25, vs=0.5)
+        assert key(ks, vs, pipelined=1) != base
+        small = (ctypes.c_uint64 * 2)()
+        kv = dlm.KV((ctypes.c_void_p * n_layers)(*ks), (ctypes.c_void_p * n_layers)(*vs), 512, FAKE.value, 512,
+                    dlm.DLM_BF16, 1.0, 1.0)
+        assert L.dlm_block_graph_key(h, ctypes.byref(rule), ctypes.byref(kv), None, 0, FAKE, FAKE, FAKE, small,
+                                     2) == ARG
+        assert L.dlm_model_graph_count(h) == 0
+    finally:
+        L.dlm_model_destroy(h)
