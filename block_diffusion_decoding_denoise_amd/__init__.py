@@ -15,6 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdlm.so")
 
 DLM_F32, DLM_BF16, DLM_MXFP4, DLM_FP8_E4M3 = 0, 1, 2, 3
+DLM_LAYERS_PER_OP, DLM_LAYERS_FUSED = 0, 1
 THRESHOLD, FIXED_K = 0, 1
 FLAG_HIT_MAX_ROUNDS, FLAG_NONFINITE = 1, 2
 MAX_ROWS = 64
@@ -68,7 +69,7 @@ class ModelDesc(ctypes.Structure):
                 ("hkv", ctypes.c_int), ("head_dim", ctypes.c_int), ("ffn", ctypes.c_int), ("vocab", ctypes.c_int),
                 ("block", ctypes.c_int), ("rope_base", ctypes.c_float), ("eps", ctypes.c_float),
                 ("n_experts", ctypes.c_int), ("expert_ffn", ctypes.c_int), ("top_k", ctypes.c_int),
-                ("n_shared", ctypes.c_int)]
+                ("n_shared", ctypes.c_int), ("layer_path", ctypes.c_int)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -85,7 +86,7 @@ class KV(ctypes.Structure):
 class DecodeViews(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("x", "hn", "pe", "lse", "entropy", "maxprob", "argmax", "committed", "xn",
                                                "moe_logits", "moe_xq", "moe_xs", "moe_ids", "moe_wts", "moe_aq",
-                                               "moe_as", "moe_y", "moe_hits")]
+                                               "moe_as", "moe_y", "moe_hits", "sync_err")]
 
 
 # ------------------------------------------------------------------ loading
@@ -301,14 +302,15 @@ class Model:
     cache (bf16 models): uint8 codes, stored value = scale * e4m3(code).
     """
 
-    def __init__(self, shape, weights, cap, max_len=None, device="cuda", kv_scales=None):
+    def __init__(self, shape, weights, cap, max_len=None, device="cuda", kv_scales=None, fused_layers=False):
         self.shape = shape
         self.w = weights
         self.device = device
         s = shape
         dt = DLM_BF16 if s.dtype == "bf16" else DLM_F32
         self.desc = ModelDesc(dt, s.n_layers, s.d, s.hq, s.hkv, s.head_dim, s.ffn, s.vocab, s.block, s.rope_base,
-                              s.eps, s.n_experts, s.expert_ffn, s.top_k, s.n_shared)
+                              s.eps, s.n_experts, s.expert_ffn, s.top_k, s.n_shared,
+                              DLM_LAYERS_FUSED if fused_layers else DLM_LAYERS_PER_OP)
         L = lib()
         self._layers = (LayerWeights * s.n_layers)()
         for i in range(s.n_layers):

@@ -15,6 +15,7 @@
 #include "head.h"
 #include "small.h"
 #include "moe.h"
+#include "layer.h"
 
 #include <cstddef>
 
@@ -294,6 +295,10 @@ struct dlm_model {
   size_t packed_bytes;
   GemmPlan pl_sc, pl_qkv, pl_o, pl_gu, pl_dn, pl_router;
   int n_qkv;
+  // fused layer path (layer.hip): one launch per sublayer, XCD-local synchronisation; the
+  // QKV, attention-output and down matrices are then packed in its layouts
+  bool fused;
+  FusedDims fd;
   std::mutex mu;
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::vector<hipGraph_t> graph_objs;
@@ -309,6 +314,8 @@ static int check_model_desc(const dlm_model_desc* d) {
   DLM_REQUIRE(d->head_dim == 64 || d->head_dim == 128, DLM_ERR_SHAPE, "head_dim must be 64 or 128");
   DLM_REQUIRE(d->block <= 32, DLM_ERR_SHAPE, "block must be <= 32");
   DLM_REQUIRE(d->d % 32 == 0 && d->d <= 4096, DLM_ERR_SHAPE, "d must be a multiple of 32, <= 4096");
+  DLM_REQUIRE(d->layer_path == DLM_LAYERS_PER_OP || d->layer_path == DLM_LAYERS_FUSED, DLM_ERR_ARG,
+              "layer_path %d", d->layer_path);
   const bool moe = d->n_experts > 0;
   if (!moe) DLM_REQUIRE(d->ffn > 0 && d->ffn % 32 == 0, DLM_ERR_SHAPE, "ffn must be a positive multiple of 32");
   if (moe) {
@@ -359,6 +366,10 @@ static void layout_packed(dlm_model* m) {
     m->pl_gu = m->pl_dn = GemmPlan{1, 1, 0};
   }
   m->pl_router = d.n_experts ? gemm_plan_owned(d.n_experts, d.d) : GemmPlan{1, 1, 0};
+  m->fused = d.layer_path == DLM_LAYERS_FUSED &&
+             layer_fused_ok(d.dtype, d.n_experts, d.d, d.hq, d.hkv, D, d.ffn, d.block) &&
+             m->pl_gu.R == 2 * d.ffn / 256 && m->pl_gu.splits == 256;
+  if (m->fused) m->fd = fused_dims(d.d, d.ffn, d.hq, d.hkv, D);
 }
 
 extern "C" size_t dlm_packed_bytes(const dlm_model_desc* d) {
@@ -404,7 +415,8 @@ extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const d
   hipStream_t st = (hipStream_t)stream;
   const int D = d->head_dim;
   std::vector<int32_t> maps((size_t)m.n_qkv + 2 * (size_t)(d->ffn > 0 ? d->ffn : 0));
-  build_row_map(MAP_QKV, m.n_qkv, d->hq, d->hkv, D, d->ffn, maps.data());
+  if (m.fused) build_xqkv_row_map(d->hq, d->hkv, D, maps.data());
+  else build_row_map(MAP_QKV, m.n_qkv, d->hq, d->hkv, D, d->ffn, maps.data());
   if (d->n_experts == 0) build_row_map(MAP_GU, 2 * d->ffn, d->hq, d->hkv, D, d->ffn, maps.data() + m.n_qkv);
   int32_t* map_qkv = (int32_t*)row_map_ws;
   int32_t* map_gu = map_qkv + m.n_qkv;
@@ -422,6 +434,28 @@ extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const d
     const dlm_layer_weights& L = layers[l];
     const void* s3[3] = {L.wq, L.wk, L.wv};
     int r3[3] = {d->hq * D, d->hkv * D, d->hkv * D};
+    if (m.fused) {
+      // QKV with each XCD's head group in its workgroups' blocks; the attention-output and down
+      // matrices as 8 column slices (each XCD's contraction range) in the row-owned layout
+      const FusedDims& fd = m.fd;
+      if ((rc = pack_bf16_owned(s3, r3, 3, m.n_qkv, d->d, map_qkv, fd.rq, out + m.off_qkv[l], st))) return rc;
+      for (int x = 0; x < 8; ++x) {
+        const void* so[1] = {(const uint16_t*)L.wo + (size_t)x * fd.ko};
+        int ro[1] = {d->d};
+        if ((rc = pack_bf16_owned(so, ro, 1, d->d, fd.ko, nullptr, fd.ro,
+                                  out + m.off_o[l] + (size_t)x * d->d * fd.ko * 2, st, d->hq * D)))
+          return rc;
+        const void* sd[1] = {(const uint16_t*)L.wd + (size_t)x * fd.kd};
+        int rd[1] = {d->d};
+        if ((rc = pack_bf16_owned(sd, rd, 1, d->d, fd.kd, nullptr, fd.ro,
+                                  out + m.off_dn[l] + (size_t)x * d->d * fd.kd * 2, st, d->ffn)))
+          return rc;
+      }
+      const void* s2[2] = {L.wg, L.wu};
+      int r2[2] = {d->ffn, d->ffn};
+      if ((rc = pack_bf16_owned(s2, r2, 2, 2 * d->ffn, d->d, map_gu, m.pl_gu.R, out + m.off_gu[l], st))) return rc;
+      continue;
+    }
     rc = m.pl_qkv.R ? pack_bf16_owned(s3, r3, 3, m.n_qkv, d->d, map_qkv, m.pl_qkv.R, out + m.off_qkv[l], st)
                     : pack_bf16(s3, r3, 3, m.n_qkv, d->d, map_qkv, out + m.off_qkv[l], st);
     if (rc) return rc;
@@ -506,6 +540,14 @@ struct DecodeWs {
   void* attn_ws;
   void* head_ws;
   void* moe_ws;
+  // fused layer path: second residual buffer, the two sublayers' XCD partials, per-XCD normed
+  // rows, XCD barrier counters and the sync error word
+  float* x2;
+  float* pa;
+  float* pb;
+  uint16_t* xn8;
+  unsigned* bar;
+  int* err;
   size_t total;
 };
 
@@ -561,6 +603,18 @@ static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) 
                                        : 256);
   w.head_ws = take(head_ws_bytes(d.dtype, d.block, d.d, d.vocab));
   w.moe_ws = take(d.n_experts ? moe_ws_bytes(d) : 0);
+  w.x2 = w.pa = w.pb = nullptr;
+  w.xn8 = nullptr;
+  w.bar = nullptr;
+  w.err = nullptr;
+  if (m->fused) {
+    w.x2 = (float*)take((size_t)64 * d.d * 4);
+    w.pa = (float*)take((size_t)64 * 8 * d.d * 4);
+    w.pb = (float*)take((size_t)64 * 8 * d.d * 4);
+    w.xn8 = (uint16_t*)take((size_t)8 * 64 * d.d * 2);
+    w.bar = (unsigned*)take(8 * 64 * 4);
+    w.err = (int*)take(9 * 128);
+  }
   w.total = off;
   return w;
 }
@@ -605,6 +659,7 @@ extern "C" int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* 
   out->xn = w.xn;
   memset(&out->moe_logits, 0, sizeof(dlm_decode_views) - offsetof(dlm_decode_views, moe_logits));
   if (m->d.n_experts) moe_views(moe_dims(m->d), w.moe_ws, out);
+  out->sync_err = w.err;
   return DLM_OK;
 }
 
@@ -625,6 +680,45 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
   const char* pk = (const char*)m->packed;
   int rc;
   PartialSrc ps{};
+  if (m->fused) {
+    // x (w.x) -> attention sublayer -> (w.x2, pa) -> FFN sublayer -> (w.x, pb) per layer
+    const LayerBufs lb{w.xn8, (uint16_t*)w.q, (uint16_t*)w.o, (uint16_t*)w.act, w.attn_ws, w.bar, w.err};
+    const AttnKv kvf{kv->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, kv->k_scale, kv->v_scale};
+    for (int l = 0; l < d.n_layers; ++l) {
+      const dlm_layer_weights& L = m->layers[l];
+      const bool kv_only = last_kv_only && l == d.n_layers - 1;
+      EpiParams e = epi_zero();
+      e.kind = EPI_QKV_ROPE;
+      e.M = B;
+      e.bf16_out = 1;
+      e.k_cache = kv->k[l];
+      e.v_cache = kv->v[l];
+      e.hq = d.hq;
+      e.hkv = d.hkv;
+      e.D = D;
+      e.cap = kv->cap;
+      e.len_dev = kv->len_dev;
+      e.rope_r = pow((double)d.rope_base, -2.0 / (double)D);
+      e.kv8 = kvf.fp8;
+      e.k_scale = kvf.fp8 ? kv->k_scale : 1.0f;
+      e.v_scale = kvf.fp8 ? kv->v_scale : 1.0f;
+      const LayerIO ioa{w.x, l ? w.pb : nullptr, w.x2, w.pa};
+      if ((rc = fused_attn_sublayer(m->fd, nqb, (const uint16_t*)(pk + m->off_qkv[l]),
+                                    (const uint16_t*)(pk + m->off_o[l]), L.attn_norm, d.eps, ioa, lb, e,
+                                    model_attn_plan(m, kv), 1.0f / sqrtf((float)D), kvf, kv_only, cont, st)))
+        return rc;
+      if (kv_only) break;
+      const LayerIO iof{w.x2, w.pa, w.x, w.pb};
+      if ((rc = fused_ffn_sublayer(m->fd, nqb, (const uint16_t*)(pk + m->off_gu[l]),
+                                   (const uint16_t*)(pk + m->off_dn[l]), L.ffn_norm, d.eps, iof, lb, cont, st)))
+        return rc;
+    }
+    // the last FFN's 8 XCD partials are added into x by the final norm, in XCD order
+    ps.slots = w.pb;
+    ps.nslot = 8;
+    *pending = ps;
+    return DLM_OK;
+  }
   for (int l = 0; l < d.n_layers; ++l) {
     const dlm_layer_weights& L = m->layers[l];
     const bool last = l == d.n_layers - 1;

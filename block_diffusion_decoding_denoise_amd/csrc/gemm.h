@@ -101,8 +101,10 @@ int gemm_f32(const F32Mats& W, const float* X, int N, int K, int map_kind, const
 // Pack rows row_map[i] of the virtual concatenation of up to 3 bf16 matrices into dst.
 int pack_bf16(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
               const int32_t* row_map_dev, void* dst, hipStream_t st);
-// The same rows in the row-owned layout of a plan with R rows per workgroup.
+// The same rows in the row-owned layout of a plan with R rows per workgroup.  ld: row stride
+// of the sources in elements (0: k); with ld > k the k columns at each source pointer are a
+// column slice of a wider matrix.
 int pack_bf16_owned(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
-                    const int32_t* row_map_dev, int R, void* dst, hipStream_t st);
+                    const int32_t* row_map_dev, int R, void* dst, hipStream_t st, int ld = 0);
 
 }  // namespace dlm

@@ -26,6 +26,7 @@
 //        accumulators held by one lane; v rows keep their order.
 //   GU:  p = 2i -> gate row 16t + i, p = 2i+1 -> up row 16t + i, so SwiGLU takes a pair.
 #include "gemm.h"
+#include "epilogue.h"
 
 // Optional per-workgroup timestamps for kernel studies (compiled out unless defined).
 #ifndef DLM_TRACE_POINT
@@ -36,49 +37,12 @@
 
 namespace dlm {
 
-// ------------------------------------------------------------------ row maps
-__host__ __device__ inline int qkv_logical(int prow, int hq, int hkv, int D) {
-  const int Nq = hq * D, Nk = hkv * D;
-  if (prow >= Nq + Nk) return prow;
-  const int base = prow < Nq ? 0 : Nq;
-  const int rel = prow - base;
-  const int head = rel / D, within = rel % D;
-  const int t = within / 32, r = within % 32;
-  return base + head * D + 16 * t + r / 2 + (r % 2) * (D / 2);
-}
-
-__host__ __device__ inline int gu_logical(int prow, int F) {
-  const int t = prow / 32, r = prow % 32;
-  return (r % 2) * F + 16 * t + r / 2;
-}
-
 void build_row_map(int kind, int n_rows, int hq, int hkv, int D, int F, int32_t* out) {
   for (int p = 0; p < n_rows; ++p) {
     if (kind == MAP_QKV) out[p] = qkv_logical(p, hq, hkv, D);
     else if (kind == MAP_GU) out[p] = gu_logical(p, F);
     else out[p] = p;
   }
-}
-
-// ------------------------------------------------------------------ epilogues
-__device__ inline int prefix_len(const EpiParams& e) {
-  return e.len_dev ? *e.len_dev : e.len_host;
-}
-
-__device__ inline void store_act(void* base, size_t idx, float v, int bf16) {
-  if (bf16) ((uint16_t*)base)[idx] = f2bf(v);
-  else ((float*)base)[idx] = v;
-}
-
-// a K/V cache element: the stored (bf16 or f32) value, or for an FP8 cache the e4m3 code of
-// the bf16 value divided by the cache scale (an IEEE single-precision quotient)
-__device__ inline void store_kv(const EpiParams& e, void* base, size_t idx, float v, float scale) {
-  if (e.kv8) ((uint8_t*)base)[idx] = (uint8_t)e4m3_code(bf2f(f2bf(v)) / scale);
-  else store_act(base, idx, v, e.bf16_out);
-}
-
-__device__ inline float load_act(const void* base, size_t idx, int bf16) {
-  return bf16 ? bf2f(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
 }
 
 // single logical output n of row m (identity-mapped kinds)
@@ -98,57 +62,6 @@ __device__ inline void epi_single(const EpiParams& e, int m, int n, float v) {
     }
     default: break;
   }
-}
-
-// rotate-half RoPE of the pair (j, j + D/2) of a q (part 0) or k (part 1) head.  The angle
-// pos * base^(-2j/D) is formed in double (base^(-2j/D) = r^j with r = base^(-2/D) from the
-// host, by repeated squaring) and reduced to [-pi, pi] in double; only the final sine and
-// cosine of the reduced angle are single precision.
-__device__ inline double ipow(double r, int j) {
-  double out = 1.0;
-  while (j) {
-    if (j & 1) out *= r;
-    r *= r;
-    j >>= 1;
-  }
-  return out;
-}
-
-__device__ inline void epi_qk_rope(const EpiParams& e, int m, int part, int head, int j, float a,
-                                   float b) {
-  const int L = prefix_len(e);
-  const int pos = L + m;
-  const double ang = (double)pos * ipow(e.rope_r, j);
-  const double two_pi = 6.283185307179586476925286766559;
-  const double red = fma(-rint(ang / two_pi), two_pi, ang);
-  float sn, cs;
-  __sincosf((float)red, &sn, &cs);
-  const float a2 = a * cs - b * sn;
-  const float b2 = b * cs + a * sn;
-  if (part == 0) {
-    const size_t o = (size_t)m * e.hq * e.D + (size_t)head * e.D + j;
-    // (q rows are always in range; cache rows are guarded below)
-    store_act(e.q_out, o, a2, e.bf16_out);
-    store_act(e.q_out, o + e.D / 2, b2, e.bf16_out);
-  } else {
-    if (L + m >= e.cap) return;   // a prefix length past the cache capacity writes nothing
-    const size_t o = ((size_t)head * e.cap + (L + m)) * e.D + j;
-    store_kv(e, e.k_cache, o, a2, e.k_scale);
-    store_kv(e, e.k_cache, o + e.D / 2, b2, e.k_scale);
-  }
-}
-
-// the V cache is stored transposed in 32-key blocks (vt_index)
-__device__ inline void epi_v(const EpiParams& e, int m, int rel, float v) {
-  const int L = prefix_len(e);
-  if (L + m >= e.cap) return;
-  const int head = rel / e.D, j = rel % e.D;
-  store_kv(e, e.v_cache, vt_index(head, e.D, e.cap, L + m, j), v, e.v_scale);
-}
-
-__device__ inline void epi_swiglu(const EpiParams& e, int m, int j, float g, float u) {
-  const float s = g / (1.0f + expf(-g));
-  store_act(e.act_out, e.bf16_out ? xpk_index_m(m, j, e.F) : (size_t)m * e.F + j, s * u, e.bf16_out);
 }
 
 // pair of packed rows (p, p+1), p even
@@ -648,6 +561,7 @@ struct PackP {
   const uint16_t* src[3];
   int rows[3];
   int n_src, k, KT;
+  int ld;              // row stride of the sources in elements (k unless a column slice is packed)
   const int32_t* map;
   uint16_t* dst;
 };
@@ -657,7 +571,7 @@ __global__ __launch_bounds__(64) void pack_kernel(PackP p) {
   int row = p.map ? p.map[t * 32 + (lane & 31)] : t * 32 + (lane & 31);
   int i = 0;
   while (i < p.n_src - 1 && row >= p.rows[i]) { row -= p.rows[i]; ++i; }
-  const uint16_t* s = p.src[i] + (size_t)row * p.k + kt * 16 + 8 * (lane >> 5);
+  const uint16_t* s = p.src[i] + (size_t)row * p.ld + kt * 16 + 8 * (lane >> 5);
   u32x4_t v = *(const u32x4_t*)s;
   *(u32x4_t*)(p.dst + ((size_t)blockIdx.x * 64 + lane) * 8) = v;
 }
@@ -678,12 +592,12 @@ __global__ __launch_bounds__(256) void pack_owned_kernel(PackP p, int R, long lo
   int row = p.map ? p.map[prow] : prow;
   int src = 0;
   while (src < p.n_src - 1 && row >= p.rows[src]) { row -= p.rows[src]; ++src; }
-  const uint16_t* sp = p.src[src] + (size_t)row * p.k + kt * 16 + 8 * h;
+  const uint16_t* sp = p.src[src] + (size_t)row * p.ld + kt * 16 + 8 * h;
   *(u32x4_t*)(p.dst + (size_t)c * 8) = *(const u32x4_t*)sp;
 }
 
 int pack_bf16_owned(const void* const* srcs, const int* src_rows, int n_src, int n_rows, int k,
-                    const int32_t* row_map_dev, int R, void* dst, hipStream_t st) {
+                    const int32_t* row_map_dev, int R, void* dst, hipStream_t st, int ld) {
   PackP p;
   for (int i = 0; i < 3; ++i) {
     p.src[i] = i < n_src ? (const uint16_t*)srcs[i] : nullptr;
@@ -692,6 +606,7 @@ int pack_bf16_owned(const void* const* srcs, const int* src_rows, int n_src, int
   p.n_src = n_src;
   p.k = k;
   p.KT = k / 16;
+  p.ld = ld > 0 ? ld : k;
   p.map = row_map_dev;
   p.dst = (uint16_t*)dst;
   if (R <= 0 || n_rows % R || R % 2) return fail(DLM_ERR_SHAPE, "pack: bad row-owned layout");
@@ -710,6 +625,7 @@ int pack_bf16(const void* const* srcs, const int* src_rows, int n_src, int n_row
   p.n_src = n_src;
   p.k = k;
   p.KT = k / 16;
+  p.ld = k;
   p.map = row_map_dev;
   p.dst = (uint16_t*)dst;
   hipLaunchKernelGGL(pack_kernel, dim3((n_rows / 32) * p.KT), dim3(64), 0, st, p);

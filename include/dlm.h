@@ -231,7 +231,15 @@ typedef struct {
   int n_layers, d, hq, hkv, head_dim, ffn, vocab, block;
   float rope_base, eps;
   int n_experts, expert_ffn, top_k, n_shared;  /* 0 for dense models */
+  int layer_path;            /* DLM_LAYERS_PER_OP (0): one kernel per step of a layer;
+                                DLM_LAYERS_FUSED (1): one launch per sublayer with XCD-local
+                                synchronisation, for dense bf16 models with 8 kv heads of 4 query
+                                heads of 128, 32-row blocks, d % 512 == 0 and ffn % 256 == 0
+                                (other models take the per-op kernels).  The packed layout
+                                depends on it: pack and create with the same value. */
 } dlm_model_desc;
+
+enum { DLM_LAYERS_PER_OP = 0, DLM_LAYERS_FUSED = 1 };
 
 typedef struct {
   const void* attn_norm;     /* [d] */
@@ -379,6 +387,11 @@ typedef struct {
   float* moe_y;
   int32_t* moe_hits;   /* [n_layers]: running count, per layer, of the distinct experts (shared
                           included) each routed-expert FFN used since the workspace was zeroed */
+  int32_t* sync_err;   /* models on the fused layer path, 288 words: word 0 is 0 unless an
+                          XCD-local barrier gave up waiting (bit 0) or a workgroup did not share
+                          the XCD of its group, blockIdx % 8 (bit 1) -- then the results are not
+                          to be trusted; word 32 (1 + g) holds the XCC id group g ran on in the
+                          last launch.  NULL for other models */
 } dlm_decode_views;
 int dlm_decode_views_get(const dlm_model* m, const dlm_kv* kv, void* ws, size_t ws_bytes,
                          dlm_decode_views* out);

@@ -1,0 +1,123 @@
+"""GPU: the fused layer path (one launch per sublayer, XCD-local synchronisation) against the
+oracle, on the smallest model that takes it (8 kv heads, one per XCD, 4 query heads of 128
+each), and its synchronisation health."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+from oracle import Prec, OracleModel, KVCache
+from tests.gpu_util import require_gpu
+from tests.test_gpu_model import _lockstep, _gpu_model, _cache_values
+
+pytestmark = pytest.mark.gpu
+
+FUSED_SMALL = synth.small_shape(synth.QWEN4B, name="fused-small", n_layers=2, d=512, ffn=1024, vocab=3001)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dlm():
+    require_gpu()
+    import block_diffusion_decoding_denoise_amd as dlm
+    dlm.lib()
+    return dlm
+
+
+def _sync_err(m):
+    """0 when no XCD barrier timed out and every workgroup group (blockIdx % 8) ran on one XCD,
+    the 8 groups on 8 different XCDs; else a description."""
+    w = m.view("sync_err", (288,), torch.int32).cpu().numpy()
+    groups = w[32::32].tolist()
+    if w[0] != 0:
+        return f"sync flags {w[0]} (1: a barrier timed out, 2: a workgroup off its group's XCD)"
+    if len(set(groups)) != 8:
+        return f"groups share an XCD: {groups}"
+    _say(f"group -> XCC in the last launch: {groups}")
+    return 0
+
+
+def test_fused_path_taken_and_sync_clean():
+    """The model takes the fused path (its decode workspace exposes the sync word), and a
+    prefill plus two decoded blocks leave it at zero: no XCD barrier gave up and every
+    workgroup ran on the XCD its index implies."""
+    dlm = _dlm()
+    m, _ = _gpu_model(FUSED_SMALL, 1250, cap=128, fused_layers=True)
+    assert m.views.sync_err
+    m0, _ = _gpu_model(FUSED_SMALL, 1250, cap=128)
+    assert not m0.views.sync_err                 # the per-op path has no XCD synchronisation
+    prompt = synth.prompt_ids(FUSED_SMALL, 64, 1250)
+    toks, states = m.generate(torch.from_numpy(prompt), 2, dlm.CommitRule.fixed_k(6), pipelined=True)
+    torch.cuda.synchronize()
+    assert _sync_err(m) == 0
+    assert [st["round"] for st in states] == [6, 6]
+
+
+def test_fused_lockstep_fixed_k():
+    counts = _lockstep(FUSED_SMALL, 1251, 64, 2, (1, 0.0, 6, 0, 32), fused_layers=True)
+    assert counts["rounds"] == 12
+
+
+def test_fused_lockstep_threshold():
+    counts = _lockstep(FUSED_SMALL, 1252, 32, 1, (0, 0.9, 1, 1, 32), check_every=7, fused_layers=True)
+    assert counts["rounds"] >= 4
+
+
+def test_fused_lockstep_fp8_cache_non_power_of_two_scales():
+    """An FP8 cache with scales that are not powers of two: the codes are those of the
+    single-precision quotient on both sides."""
+    _lockstep(FUSED_SMALL, 1253, 64, 1, (1, 0.0, 6, 0, 32), kv_scales=(0.07, 0.11), fused_layers=True)
+
+
+def test_fused_prefill_matches_oracle_cache():
+    dlm = _dlm()
+    s = FUSED_SMALL
+    m, w = _gpu_model(s, 1254, cap=192, fused_layers=True)
+    prompt = synth.prompt_ids(s, 160, 9)
+    m.set_len(0)
+    m.prefill(torch.from_numpy(prompt))
+    torch.cuda.synchronize()
+    assert int(m.len_dev.item()) == 160 and _sync_err(m) == 0
+    om = OracleModel(s, w, Prec("bf16"))
+    kv = KVCache.empty(s, 192)
+    oracle.prefill(om, kv, prompt, Prec("bf16"))
+    gks, gvs = _cache_values(m, None)
+    for l in range(s.n_layers):
+        for g, o in ((gks[l][:, :160], kv.k[l][:, :160]), (gvs[l][:, :160], kv.v[l][:, :160])):
+            np.testing.assert_allclose(g, o, atol=3e-2, rtol=2e-2)
+            if l == 0:
+                ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(o), 1e-30))) - 7)
+                assert np.mean(np.abs(g - o) > 1.01 * ulp) < 1e-3
+
+
+def test_graph_recapture_when_a_later_layer_cache_moves():
+    """Reallocating a later layer's K/V (same capacity) must not replay the graph captured with
+    the old pointers: the next block writes the new tensors, the model holds a second graph,
+    and the tokens equal those of the unmoved run."""
+    dlm = _dlm()
+    s = FUSED_SMALL
+    m, _ = _gpu_model(s, 1255, cap=128, fused_layers=True)
+    prompt = torch.from_numpy(synth.prompt_ids(s, 64, 1255))
+    rule = dlm.CommitRule.fixed_k(11)
+    t_ref, _ = m.generate(prompt, 2, rule)
+    torch.cuda.synchronize()
+    assert dlm.lib().dlm_model_graph_count(m.handle) == 1
+    old_k, old_v = m.k[1], m.v[1]
+    m.k[1] = torch.zeros_like(old_k)
+    m.v[1] = torch.zeros_like(old_v)
+    m._kptrs[1] = m.k[1].data_ptr()
+    m._vptrs[1] = m.v[1].data_ptr()
+    old_k.zero_()
+    t_new, _ = m.generate(prompt, 2, rule)
+    torch.cuda.synchronize()
+    assert torch.equal(t_ref, t_new)
+    assert dlm.lib().dlm_model_graph_count(m.handle) == 2
+    assert m.k[1][:, :128].abs().sum().item() > 0        # the moved cache received the K/V
+    assert old_k.abs().sum().item() == 0                   # the old one was not written
+    assert _sync_err(m) == 0

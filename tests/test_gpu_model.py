@@ -30,10 +30,10 @@ def _upload(w: synth.Weights):
     return {n: storage(w[n], dt) for n in w.names_dense()}
 
 
-def _gpu_model(shape, seed, cap, max_len=None, kv_scales=None):
+def _gpu_model(shape, seed, cap, max_len=None, kv_scales=None, fused_layers=False):
     dlm = _dlm()
     w = synth.Weights(shape, seed)
-    return dlm.Model(shape, _upload(w), cap=cap, max_len=max_len, kv_scales=kv_scales), w
+    return dlm.Model(shape, _upload(w), cap=cap, max_len=max_len, kv_scales=kv_scales, fused_layers=fused_layers), w
 
 
 def _cache_values(m, kv_scales):
@@ -103,7 +103,8 @@ def _valid_commit(rule_args, maxprob, open_rows, chosen):
     return sel
 
 
-def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_scales=None):
+def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_scales=None, check_rounds=None,
+              cache_layers=True, fused_layers=False):
     """Run rounds one at a time; after each round recompute it with the oracle from the
     GPU's own round-start state and compare the statistics and the commit.
 
@@ -115,9 +116,9 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
     dlm = _dlm()
     _say(f"lockstep {shape.name} d={shape.d} L={shape.n_layers} seed={seed} kv_scales={kv_scales}")
     cap = prompt_len + (n_blocks + 1) * shape.block
-    m, w = _gpu_model(shape, seed, cap, kv_scales=kv_scales)
+    m, w = _gpu_model(shape, seed, cap, kv_scales=kv_scales, fused_layers=fused_layers)
     prec = Prec(shape.dtype, kv_scales=kv_scales)
-    om = OracleModel(shape, w, prec)
+    om = OracleModel(shape, w, prec, cache_layers=cache_layers)
     prompt = synth.prompt_ids(shape, prompt_len, seed)
     m.set_len(0)
     m.prefill(torch.from_numpy(prompt))
@@ -129,7 +130,8 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
         tol_l, tol_e = 2e-2, 1e-2
     else:
         tol_l, tol_e = 1e-4, 1e-4
-    counts = {"rounds": 0, "argmax_diff": 0, "argmax_diff_gap_lt_1e-3": 0, "commit_diff": 0}
+    counts = {"rounds": 0, "argmax_diff": 0, "argmax_diff_gap_lt_1e-3": 0, "commit_diff": 0, "worst_pe_rel": 0.0,
+              "worst_lse_abs": 0.0}
     for blk in range(n_blocks):
         m.decode_begin()
         r = 0
@@ -145,7 +147,8 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
             kv = KVCache(*_cache_values(m, kv_scales), L)
             m.decode_round(rule)
             torch.cuda.synchronize()
-            if r % check_every == 0:
+            if (check_rounds is None and r % check_every == 0) or (check_rounds is not None and r in check_rounds):
+                _say(f"  block {blk} round {r}: oracle recompute at prefix {L}")
                 res = oracle.denoise_round(om, kv, tokens.copy(), committed.copy(), None if r == 0 else pe_prev, r,
                                            orule, prec, want_logits=True)
                 g = {n: m.view(n, (B,), dt).cpu().numpy() for n, dt in
@@ -168,7 +171,13 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
                         counts["argmax_diff_gap_lt_1e-3"] += int(ref["top2_gap"][i] < 1e-3)
                 num = np.linalg.norm(g_pe[open_rows] - ref["pe"][open_rows], axis=1)
                 den = np.linalg.norm(ref["pe"][open_rows], axis=1)
-                assert np.all(num / den < 10 * tol_e), (num / den).max()
+                counts["worst_pe_rel"] = max(counts["worst_pe_rel"], float((num / den).max()))
+                counts["worst_lse_abs"] = max(counts["worst_lse_abs"],
+                                              float(np.abs(g["lse"][open_rows] - ref["lse"][open_rows]).max()))
+                # p.E moves with the logits: with logit errors e_v (the lse bound tol_l applies to
+                # them) the row's relative p.E error is about the p-weighted RMS of e_v, plus the
+                # head's own bf16 rounding of p (about 1e-3); 2 tol_l bounds both
+                assert np.all(num / den < 2 * tol_l), (num / den).max()
                 g_now = set(np.nonzero(g_committed != committed)[0].tolist())
                 # the commit kernel applies the rule exactly to the GPU's own statistics ...
                 assert g_now == _valid_commit(rule_args, g["maxprob"], list(open_rows), g_now) or \

@@ -34,11 +34,11 @@ def _dlm():
     return dlm
 
 
-def _model(shape, seed, cap, kv_scales=None):
+def _model(shape, seed, cap, kv_scales=None, fused_layers=False):
     dlm = _dlm()
     w = synth.Weights(shape, seed)
     up = {n: storage(w[n], shape.dtype) for n in w.names_dense()}
-    return dlm.Model(shape, up, cap=cap, kv_scales=kv_scales), w
+    return dlm.Model(shape, up, cap=cap, kv_scales=kv_scales, fused_layers=fused_layers), w
 
 
 def _run(dlm, m, prompt, n_blocks, rule, pipelined):
@@ -56,21 +56,28 @@ SMALL = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq
 # the 4B layer shapes (row-owned gate/up with 3 sub-tiles, QKV with 24 rows per workgroup,
 # stream-K attention-output and down projections with their real partial counts)
 QWEN4B_2L = synth.small_shape(synth.QWEN4B, name="qwen4b-2-layers", n_layers=2)
+# the smallest model on the fused layer path (8 kv heads, one per XCD, 4 query heads of 128 each)
+FUSED_SMALL = synth.small_shape(synth.QWEN4B, name="fused-small", n_layers=2, d=512, ffn=1024, vocab=3001)
 
 
-@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args,kv_scales", [
-    (SMALL, 1234, 64, 3, ("fixed_k", 6), None),
-    (SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32), None),
-    (SMALL, 1236, 96, 2, ("fixed_k", 32), None),
-    (QWEN4B_2L, 1234, 256, 3, ("fixed_k", 6), None),
-    (SMALL, 1237, 64, 3, ("fixed_k", 6), (0.125, 0.0625)),
-    (QWEN4B_2L, 1238, 256, 2, ("fixed_k", 6), (0.25, 0.125)),
-], ids=["small-k6", "small-threshold", "small-k32", "qwen4b-2l-k6", "small-k6-fp8-cache", "qwen4b-2l-k6-fp8-cache"])
-def test_pipelined_bitexact_bf16(shape, seed, prompt_len, n_blocks, rule_args, kv_scales):
+@pytest.mark.parametrize("shape,seed,prompt_len,n_blocks,rule_args,kv_scales,fused", [
+    (SMALL, 1234, 64, 3, ("fixed_k", 6), None, False),
+    (SMALL, 1235, 32, 2, ("threshold", 0.5, True, 32), None, False),
+    (SMALL, 1236, 96, 2, ("fixed_k", 32), None, False),
+    (QWEN4B_2L, 1234, 256, 3, ("fixed_k", 6), None, False),
+    (SMALL, 1237, 64, 3, ("fixed_k", 6), (0.125, 0.0625), False),
+    (QWEN4B_2L, 1238, 256, 2, ("fixed_k", 6), (0.25, 0.125), False),
+    (FUSED_SMALL, 1241, 64, 3, ("fixed_k", 6), None, True),
+    (FUSED_SMALL, 1242, 32, 2, ("threshold", 0.5, True, 32), None, True),
+    (FUSED_SMALL, 1243, 64, 2, ("fixed_k", 6), (0.07, 0.11), True),
+    (QWEN4B_2L, 1245, 256, 3, ("fixed_k", 6), None, True),
+], ids=["small-k6", "small-threshold", "small-k32", "qwen4b-2l-k6", "small-k6-fp8-cache", "qwen4b-2l-k6-fp8-cache",
+        "fused-small-k6", "fused-small-threshold", "fused-small-k6-fp8-cache", "fused-qwen4b-2l-k6"])
+def test_pipelined_bitexact_bf16(shape, seed, prompt_len, n_blocks, rule_args, kv_scales, fused):
     dlm = _dlm()
     _say(f"pipelined vs separate commit passes: {shape.name} seed {seed} prompt {prompt_len} "
-         f"blocks {n_blocks} rule {rule_args} kv_scales {kv_scales}")
-    m, _ = _model(shape, seed, cap=prompt_len + 32 * n_blocks, kv_scales=kv_scales)
+         f"blocks {n_blocks} rule {rule_args} kv_scales {kv_scales} fused layers {fused}")
+    m, _ = _model(shape, seed, cap=prompt_len + 32 * n_blocks, kv_scales=kv_scales, fused_layers=fused)
     rule = getattr(dlm.CommitRule, rule_args[0])(*rule_args[1:])
     prompt = synth.prompt_ids(shape, prompt_len, seed)
     t0, s0, k0, v0 = _run(dlm, m, prompt, n_blocks, rule, pipelined=False)
@@ -122,9 +129,10 @@ def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args, kv
         assert torch.equal(v0[l], v1[l]), f"layer {l} values"
 
 
-@pytest.mark.parametrize("shape,seed,prompt_len", [(SMALL, 1237, 96), (QWEN4B_2L, 1238, 64), (MOE_SMALL, 1239, 160)],
-                         ids=["small-3blocks", "qwen4b-2l", "moe-small-5blocks"])
-def test_prefill_pairs_bitexact(shape, seed, prompt_len):
+@pytest.mark.parametrize("shape,seed,prompt_len,fused", [(SMALL, 1237, 96, False), (QWEN4B_2L, 1238, 64, False),
+                                                         (MOE_SMALL, 1239, 160, False), (FUSED_SMALL, 1244, 160, True)],
+                         ids=["small-3blocks", "qwen4b-2l", "moe-small-5blocks", "fused-small-5blocks"])
+def test_prefill_pairs_bitexact(shape, seed, prompt_len, fused):
     """dlm_prefill forwards two prompt blocks per 64-row pass: the cache equals the one built
     block by block (one prefill call per block), bitwise."""
     dlm = _dlm()
@@ -136,7 +144,7 @@ def test_prefill_pairs_bitexact(shape, seed, prompt_len):
         dev.update(moe_device_weights(w))
         m = dlm.Model(shape, dev, cap=prompt_len + 32)
     else:
-        m, _ = _model(shape, seed, cap=prompt_len + 32)
+        m, _ = _model(shape, seed, cap=prompt_len + 32, fused_layers=fused)
     prompt = torch.from_numpy(synth.prompt_ids(shape, prompt_len, seed))
     m.set_len(0)
     m.prefill(prompt)
