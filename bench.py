@@ -1,15 +1,22 @@
 """Benchmark: bs=1 block-diffusion decode of the Qwen3-4B-shaped random-init model on one GPU.
 
-A step is one block: ceil(32 / k) denoising rounds (self-conditioning input, 36 layers,
-fused head statistics, commit) plus one commit pass that writes a block's K/V, as one replay
-of the library's captured graph.  By default blocks are pipelined: each block's round 0 also
-carries the pending commit pass of the block before it (dlm_decode_block_pipelined, one
-64-row forward), so a block streams the weights ceil(32 / k) times; --separate-commit runs
-every block with its own commit pass instead (dlm_decode_block).  The timed region runs
---steps consecutive blocks after a 256-token prompt (prefill excluded, timed on its own), with
-the block's token readback queued after each block.  The headline k runs on every seed of
---seeds (a new model and prompt each; the value is the median), the other k values and legs on
---seed.  Prints one JSON line.
+The workload is the generation of 4096 new tokens after a 256-token prompt: 128 blocks of 32,
+block b decoded at prefix 256 + 32 b (256 .. 4320, mean 2288).  A step is one block:
+ceil(32 / k) denoising rounds (self-conditioning input, 36 layers, fused head statistics,
+commit) plus the commit pass that writes a block's K/V, as one replay of the library's
+captured graph.  By default blocks are pipelined: each block's round 0 also carries the
+pending commit pass of the block before it (dlm_decode_block_pipelined, one 64-row forward),
+so a block streams the weights ceil(32 / k) times; --separate-commit runs every block with its
+own commit pass instead (dlm_decode_block).
+
+The timed region runs exactly --steps blocks, spread evenly over the 128 blocks of the
+generation (step i decodes block floor((i + 1/2) 128 / steps) at that block's prefix; with
+--steps 128 every block once), so the time per block, the tokens/s and the roofline fraction
+are those of the whole 4096-token generation whatever --steps is; the prefix is set on the
+device before each block and the block's token readback is queued after it.  A second leg
+decodes the 128 blocks in order, as one generation (full_generation).  Prefill is timed on its
+own.  The headline k runs on every seed of --seeds (a new model and prompt each; the value is
+the median), the other k values and legs on --seed.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -286,7 +293,9 @@ def run_moe(args, torch, dlm, synth, np):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128, help="timed blocks (128 = 4096 new tokens)")
+    ap.add_argument("--steps", type=int, default=128,
+                    help="timed blocks, spread evenly over the 128 blocks of the 4096-token generation")
+    ap.add_argument("--new-tokens", type=int, default=4096, help="tokens of the generation the steps sample")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--k", type=int, default=6, help="commits per round of the headline number")
     ap.add_argument("--k-list", default="1,2,6,11", help="other k values also timed (empty to skip)")
@@ -305,6 +314,10 @@ def main():
                     help="decode every block with its own commit pass instead of pipelining it")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel leg plus a 256 MiB device copy (for counter runs)")
+    ap.add_argument("--fused-layers", action="store_true",
+                    help="decode with the fused layer kernels (one launch per sublayer)")
+    ap.add_argument("--no-full", action="store_true", help="skip the in-order 128-block generation leg")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny fp32 model leg")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -320,8 +333,13 @@ def main():
     dlm.lib()
     shape = synth.QWEN4B
     B = shape.block
-    n_new = args.steps * B
-    cap = args.prompt + (max(args.steps, args.warmup) + 1) * B
+    NB = args.new_tokens // B                    # blocks of the generation
+    n_new = args.steps * B                       # tokens decoded in the timed region
+    # step i decodes block blocks[i] (evenly spread over the generation; all of them in order
+    # when --steps equals the block count)
+    blocks = [min(NB - 1, int((i + 0.5) * NB / args.steps)) if args.steps < NB else i % NB
+              for i in range(args.steps)]
+    cap = args.prompt + (NB + 2) * B
     t0 = time.time()
     w = synth.Weights(shape, args.seed)
     names = w.names_dense()
@@ -330,16 +348,23 @@ def main():
         a = w[n]
         dev_w[n] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
     log(f"weights drawn and uploaded in {time.time() - t0:.1f}s")
-    model = dlm.Model(shape, dev_w, cap=cap)
+    model = dlm.Model(shape, dev_w, cap=cap, fused_layers=args.fused_layers)
     prompt = torch.from_numpy(synth.prompt_ids(shape, args.prompt, args.seed))
-    host_tok = torch.empty(args.steps, B, dtype=torch.int32).pin_memory()
+    host_tok = torch.empty(max(args.steps, NB), B, dtype=torch.int32).pin_memory()
+    # device-side prefix of each timed block: the pending commit pass of the block before it
+    # (pipelined) lands at [L - B, L), so the pipelined decode of block b starts at L_b - B
+    L_of = [args.prompt + B * b for b in blocks]
+    len_seq = torch.tensor([L - B if not args.separate_commit else L for L in L_of], dtype=torch.int32,
+                           device="cuda")
 
     pipelined = not args.separate_commit
     bufs = [torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(2)]
 
     prefill_ms = []
 
-    def run(k, steps, warmup):
+    def run(k, steps, warmup, in_order=False):
+        """Time `steps` blocks at fixed k: the sampled blocks of the generation (each at its own
+        prefix), or (in_order) the generation's first `steps` blocks one after the other."""
         rule = dlm.CommitRule.fixed_k(k)
         model.set_len(0)
         torch.cuda.synchronize()
@@ -372,6 +397,8 @@ def main():
         t_host = time.perf_counter()
         ev0.record()
         for i in range(steps):
+            if not in_order:
+                model.len_dev.copy_(len_seq[i:i + 1])          # this block's prefix (device copy)
             if pipelined:
                 cur = bufs[1] if prev is bufs[0] else bufs[0]
                 model.decode_block_pipelined(rule, prev, cur)
@@ -393,29 +420,41 @@ def main():
     ks = [args.k] + [int(x) for x in args.k_list.split(",") if x and int(x) != args.k]
     if args.roofline_only:
         ks = []
-    for k in ks:
-        sec, wall, R = run(k, args.steps, args.warmup)
-        L_mean = args.prompt + B * (args.steps - 1) / 2
+    def block_bytes(L, R, kv_elem_bytes=2):
         if pipelined:
             # R weight streams per block: round 0 moves the previous block's commit rows with
             # the same weights (its keys reach prefix + 2 B, as the rounds' do)
-            rb = sum(algorithmic_bytes(shape, args.prompt + B * i) * R for i in range(args.steps))
-        else:
-            rb = sum(algorithmic_bytes(shape, args.prompt + B * i) * R + commit_pass_bytes(shape, args.prompt + B * i)
-                     for i in range(args.steps))
+            return algorithmic_bytes(shape, L, kv_elem_bytes=kv_elem_bytes) * R
+        return algorithmic_bytes(shape, L) * R + commit_pass_bytes(shape, L)
+
+    for k in ks:
+        sec, wall, R = run(k, args.steps, args.warmup)
+        L_mean = sum(L_of) / len(L_of)
+        rb = sum(block_bytes(L, R) for L in L_of)
         results[k] = {"tok_s": n_new / sec, "rounds_s": args.steps * R / sec, "ms_per_block": 1e3 * sec / args.steps,
                       "hbm_frac": rb / sec / HBM_PEAK, "rounds_per_block": R, "tpf": B / R, "wall_s": wall,
                       "bytes_per_block": rb / args.steps, "mean_prefix": L_mean}
         log(f"k={k}: {results[k]['tok_s']:.0f} tok/s, {results[k]['rounds_s']:.0f} rounds/s, "
             f"{results[k]['ms_per_block']:.2f} ms/block, {100 * results[k]['hbm_frac']:.1f}% of 8 TB/s")
 
+    # ---- the headline k over the whole generation in order (128 blocks, each at its prefix)
+    full = None
+    if ks and not args.no_full:
+        sec, wall, R = run(args.k, NB, args.warmup, in_order=True)
+        rb = sum(block_bytes(args.prompt + B * b, R) for b in range(NB))
+        full = {"k": args.k, "blocks": NB, "new_tokens": NB * B, "tok_s": round(NB * B / sec, 1),
+                "rounds_s": round(NB * R / sec, 1), "ms_per_block": round(1e3 * sec / NB, 3),
+                "hbm_frac": round(rb / sec / HBM_PEAK, 4), "mean_prefix": args.prompt + B * (NB - 1) / 2,
+                "wall_s": round(wall, 3)}
+        log(f"k={args.k} full {NB}-block generation: {full['tok_s']:.0f} tok/s, {full['ms_per_block']:.2f} ms/block")
+
     # ---- the headline k with an FP8 e4m3 KV cache (same weights, prompt and rule)
     fp8_cache = None
     if ks and pipelined and not args.no_fp8_cache:
         bf16_model = model
-        model = dlm.Model(shape, dev_w, cap=cap, kv_scales=FP8_CACHE_SCALES)
+        model = dlm.Model(shape, dev_w, cap=cap, kv_scales=FP8_CACHE_SCALES, fused_layers=args.fused_layers)
         sec, wall, R = run(args.k, args.steps, args.warmup)
-        rb = sum(algorithmic_bytes(shape, args.prompt + B * i, kv_elem_bytes=1) * R for i in range(args.steps))
+        rb = sum(block_bytes(L, R, kv_elem_bytes=1) for L in L_of)
         fp8_cache = {"k": args.k, "kv_scales": list(FP8_CACHE_SCALES), "tok_s": round(n_new / sec, 1),
                      "ms_per_block": round(1e3 * sec / args.steps, 3), "hbm_frac": round(rb / sec / HBM_PEAK, 4),
                      "bytes_per_block": rb / args.steps}
@@ -503,7 +542,7 @@ def main():
         for n in names:
             dev_w[n] = torch.from_numpy(ws[n].view(np.int16)).view(torch.bfloat16).to("cuda")
         del ws
-        model = dlm.Model(shape, dev_w, cap=cap)
+        model = dlm.Model(shape, dev_w, cap=cap, fused_layers=args.fused_layers)
         prompt = torch.from_numpy(synth.prompt_ids(shape, args.prompt, sd))
         sec, _, _ = run(args.k, args.steps, args.warmup)
         per_seed[str(sd)] = n_new / sec
@@ -550,14 +589,81 @@ def main():
         log(f"cpu oracle: {cpu_tok_s:.3f} tok/s ({t_round:.1f} s/round)")
         del res
 
+    # ---- the tiny fp32 model: prompt 64, 4 blocks, threshold 0.9 with forced top-1, 32 rounds at
+    # most (random weights: every round commits its top-1 only, so 32 rounds per block)
+    tiny = None
+    if not args.no_tiny:
+        ts = synth.TINY
+        tw = synth.Weights(ts, args.seed)
+        tdev = {n: torch.from_numpy(np.ascontiguousarray(tw[n])).cuda() for n in tw.names_dense()}
+        tm = dlm.Model(ts, tdev, cap=64 + 5 * 32)
+        tprompt = torch.from_numpy(synth.prompt_ids(ts, 64, args.seed))
+        trule = dlm.CommitRule.threshold(0.9, True, 32)
+        tm.generate(tprompt, 4, trule)                 # captures the graph
+        torch.cuda.synchronize()
+        tm.set_len(0)
+        tm.prefill(tprompt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(4):
+            tm.decode_block(trule)
+        e1.record()
+        torch.cuda.synchronize()
+        tsec = e0.elapsed_time(e1) / 1e3
+        rounds = 4 * 32
+        tiny = {"workload": "tiny fp32 (2 layers, d 256, vocab 4096), prompt 64, 4 blocks of 32, threshold 0.9 "
+                            "with forced top-1, max 32 rounds", "rounds_s": round(rounds / tsec, 1),
+                "tok_s": round(4 * 32 / tsec, 1), "ms_per_block": round(1e3 * tsec / 4, 3),
+                "rounds_per_block": dlm.state_dict(tm.state)["round"]}
+        tm.close()
+        log(f"tiny fp32: {tiny['rounds_s']:.0f} rounds/s, {tiny['ms_per_block']:.2f} ms/block")
+
+    # ---- the CPU oracle on one core: one round of a 1-layer and of a 2-layer cut of the same
+    # model at prefix 256 (numpy float32), extrapolated to the 36-layer round
+    cpu1 = None
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_limits
+            import oracle
+            from oracle import OracleModel, KVCache, Prec, CommitRule as OCR
+            prec = Prec("bf16", np.float32)
+            t = {}
+            with threadpool_limits(limits=1):
+                for nl in (1, 2):
+                    sh = synth.small_shape(shape, n_layers=nl)
+                    om = OracleModel(sh, w, prec, cache_layers=False)
+                    kv = KVCache.empty(sh, args.prompt + 2 * B, np.float32)
+                    kv.length = args.prompt
+                    t0 = time.perf_counter()
+                    oracle.denoise_round(om, kv, np.zeros(B, np.int32), np.zeros(B, np.uint8), None, 0,
+                                         OCR(1, 0.9, args.k, False, 32), prec)
+                    t[nl] = time.perf_counter() - t0
+            per_layer = t[2] - t[1]
+            t_round = t[1] + (shape.n_layers - 1) * per_layer
+            R = math.ceil(B / args.k)
+            cpu1 = {"value": round(B / (R * t_round * (1 + 0.9 / R)), 4), "unit": "tokens/s", "cores": 1,
+                    "kind": "oracle",
+                    "sample": f"one round of a 1-layer and of a 2-layer cut of the model at prefix {args.prompt} on "
+                              f"one core ({t[1]:.2f} s and {t[2]:.2f} s), extrapolated to 36 layers "
+                              f"({t_round:.1f} s/round) and to a {R}-round block plus a commit pass of 0.9 round"}
+            log(f"cpu oracle, 1 core: {cpu1['value']:.4f} tok/s ({t_round:.1f} s/round)")
+        except Exception as ex:        # noqa: BLE001 -- the baseline leg must not sink the line
+            log(f"cpu oracle 1-core leg skipped: {ex}")
+
     h = results[args.k]
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": h["ms_per_block"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"qwen3-4b-shaped random-init block decode, bs=1, block 32, fixed k={args.k}, "
-                               f"prompt {args.prompt}, {n_new} new tokens",
-                   "k": args.k, "block": B, "prompt": args.prompt, "new_tokens": n_new, "layers": s.n_layers,
+                               f"prompt {args.prompt}, {NB * B} new tokens (blocks at prefixes {args.prompt}.."
+                               f"{args.prompt + B * NB}, mean {args.prompt + B * (NB - 1) / 2:.0f}); "
+                               f"{args.steps} timed blocks spread evenly over them (mean prefix "
+                               f"{h['mean_prefix']:.0f})",
+                   "k": args.k, "block": B, "prompt": args.prompt, "new_tokens": NB * B, "timed_blocks": args.steps,
+                   "mean_prefix": h["mean_prefix"], "layers": s.n_layers,
+                   "layer_kernels": "fused (one launch per sublayer)" if args.fused_layers else "per op",
                    "commit_pass": "pipelined into the next block's round 0" if pipelined else "separate",
                    "d": s.d, "ffn": s.ffn, "vocab": s.vocab},
         "rounds_per_s": h["rounds_s"], "hbm_frac_step": h["hbm_frac"], "tpf": h["tpf"],
@@ -568,7 +674,8 @@ def main():
         "hbm_stream_measured": stream, "ops": ops, "fp8_cache": fp8_cache,
         "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
                   for k, r in results.items()},
-        "roofline": roofline, "cpu_baseline": cpu, "moe": moe,
+        "roofline": roofline, "cpu_baseline": cpu, "cpu_baseline_1core": cpu1, "moe": moe,
+        "full_generation": full, "tiny_fp32": tiny,
     }
     print(json.dumps(line), flush=True)
     if model is not None:
