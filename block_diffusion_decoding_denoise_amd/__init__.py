@@ -135,6 +135,8 @@ def lib():
         "dlm_ffn_gate_up_ws_bytes": (sz, [vp]),
         "dlm_ffn_gate_up": (i, [vp, i, vp, vp, vp, sz, vp]),
         "dlm_block_graph_key": (i, [vp, P(CommitRule), P(KV), vp, i, vp, vp, vp, P(ctypes.c_uint64), i]),
+        "dlm_block_attn_noalloc_max_bytes": (sz, []),
+        "dlm_block_attn_noalloc": (i, [P(AttnDesc), vp, vp, vp, vp, vp]),
         "dlm_model_graph_count": (i, [vp]),
     }
     for name, (res, args) in sig.items():
@@ -202,6 +204,25 @@ def block_attn(q, k_cache, v_cache, prefix_len, out=None, prefix_len_dev=None, m
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(lib().dlm_block_attn(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(ws),
                                 ws.numel(), _stream()), "dlm_block_attn")
+    return out
+
+
+def block_attn_noalloc(q, k_cache, v_cache, prefix_len, out=None, prefix_len_dev=None, max_prefix_len=None,
+                       scale=None, kv_scales=None):
+    """block_attn through dlm_block_attn_noalloc: no workspace (the library's per-GPU scratch)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    B, hq, D = q.shape
+    hkv, cap, _ = k_cache.shape
+    fp8 = k_cache.dtype == torch.uint8
+    ks, vs = kv_scales if kv_scales is not None else (1.0, 1.0)
+    d = AttnDesc(_dtype_code(q), hq, hkv, D, B, cap, scale if scale is not None else D ** -0.5,
+                 int(prefix_len), _ptr(prefix_len_dev), int(max_prefix_len if max_prefix_len is not None else prefix_len),
+                 DLM_FP8_E4M3 if fp8 else _dtype_code(q), float(ks), float(vs))
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().dlm_block_attn_noalloc(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                        _stream()), "dlm_block_attn_noalloc")
     return out
 
 

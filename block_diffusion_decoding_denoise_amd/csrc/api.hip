@@ -94,6 +94,9 @@ extern "C" size_t dlm_block_attn_ws_bytes(const dlm_attn_desc* d) {
   return attn_ws_bytes(d->hq, d->hkv, d->head_dim, attn_plan(d->hq, d->hkv, d->head_dim, d->block, maxL));
 }
 
+static int block_attn_enqueue(const dlm_attn_desc* d, const void* q, const void* k, const void* v, void* out,
+                              void* ws, void* stream);
+
 extern "C" int dlm_block_attn(const dlm_attn_desc* d, const void* q, const void* k, const void* v, void* out,
                               void* ws, size_t ws_bytes, void* stream) {
   int rc = check_attn(d);
@@ -104,6 +107,56 @@ extern "C" int dlm_block_attn(const dlm_attn_desc* d, const void* q, const void*
   DLM_REQUIRE(ws || need == 0, DLM_ERR_ARG, "null workspace");
   DLM_REQUIRE(ws_bytes >= need, DLM_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   DLM_DEVICE_CHECK();
+  return block_attn_enqueue(d, q, k, v, out, ws, stream);
+}
+
+// ------------------------------------------------------------------ allocation-free attention
+// The split partials of dlm_block_attn_noalloc live in this file-scope device array (one copy
+// per GPU, held until the process ends).  Host code never uses the array's name as an address:
+// each device's copy is found once with hipGetSymbolAddress and that pointer is passed to the
+// kernels.  The kernels overwrite every partial they later read, so nothing is cleared.
+static constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+static void* attn_scratch_ptr(int* rc) {
+  constexpr int kMaxDev = 64;
+  static void* ptr[kMaxDev];
+  static hipError_t err[kMaxDev];
+  static std::once_flag once[kMaxDev];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    *rc = fail(DLM_ERR_HIP, "no current device in [0, %d)", kMaxDev);
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev]() { err[dev] = hipGetSymbolAddress(&ptr[dev], HIP_SYMBOL(scratch)); });
+  if (err[dev] != hipSuccess || ptr[dev] == nullptr) {
+    *rc = fail(DLM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+               err[dev] != hipSuccess ? hipGetErrorString(err[dev]) : "null address");
+    return nullptr;
+  }
+  return ptr[dev];
+}
+
+extern "C" size_t dlm_block_attn_noalloc_max_bytes(void) { return kAttnScratchBytes; }
+
+extern "C" int dlm_block_attn_noalloc(const dlm_attn_desc* d, const void* q, const void* k, const void* v, void* out,
+                                      void* stream) {
+  int rc = check_attn(d);
+  if (rc) return rc;
+  DLM_REQUIRE(q && k && v && out, DLM_ERR_ARG, "null tensor");
+  DLM_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), DLM_ERR_ARG, "tensors must be 16-byte aligned");
+  const size_t need = dlm_block_attn_ws_bytes(d);
+  DLM_REQUIRE(need <= kAttnScratchBytes, DLM_ERR_WORKSPACE,
+              "this attention needs %zu bytes of split scratch; the allocation-free call holds %zu "
+              "(use dlm_block_attn with a workspace)", need, kAttnScratchBytes);
+  DLM_DEVICE_CHECK();
+  void* ws = attn_scratch_ptr(&rc);
+  if (!ws) return rc;
+  return block_attn_enqueue(d, q, k, v, out, ws, stream);
+}
+
+static int block_attn_enqueue(const dlm_attn_desc* d, const void* q, const void* k, const void* v, void* out,
+                              void* ws, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (d->dtype == DLM_F32)
     return attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, d->hq, d->hkv, d->head_dim,

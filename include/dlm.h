@@ -81,8 +81,8 @@ const char* dlm_last_error(void);
  *   L is desc->prefix_len, or *desc->prefix_len_dev when that device pointer is non-null
  *   (so a captured graph can replay with a growing prefix).  Shapes: D in {64, 128},
  *   hq % hkv == 0, 1 <= B <= 64, L + B <= cap.
- *   ws: device scratch of at least dlm_block_attn_ws_bytes(desc) bytes; must be zeroed
- *   once before first use (the kernels leave it zeroed again).
+ *   ws: device scratch of at least dlm_block_attn_ws_bytes(desc) bytes (the key splits'
+ *   partial outputs; no zeroing needed: every partial read was written by the same call).
  *   FP8 cache (kv_dtype = DLM_FP8_E4M3, with dtype = DLM_BF16): k_cache and v_cache hold one
  *   OCP FP8 e4m3 code per element in the same layouts, and the stored key (value) is
  *   k_scale (v_scale) times the code's value; q and out stay bf16.  [ORL-blog] "What shipped"
@@ -105,6 +105,18 @@ typedef struct {
 size_t dlm_block_attn_ws_bytes(const dlm_attn_desc* desc);
 int dlm_block_attn(const dlm_attn_desc* desc, const void* q, const void* k_cache,
                    const void* v_cache, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* dlm_block_attn_noalloc -- dlm_block_attn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, with the split partials in a scratch area the library holds on
+ * each GPU it runs on (dlm_block_attn_noalloc_max_bytes() bytes, 16 MiB, kept until the process
+ * ends); no allocating call is made.  Arguments and errors as dlm_block_attn, without the
+ * workspace; DLM_ERR_WORKSPACE when dlm_block_attn_ws_bytes(desc) exceeds the scratch (at
+ * 32 / 8 heads of 128 and 32 queries the largest plan needs 8,650,752 bytes).  All calls on one GPU
+ * share its scratch: calls that overlap in time on one GPU (concurrent streams) race. */
+size_t dlm_block_attn_noalloc_max_bytes(void);
+int dlm_block_attn_noalloc(const dlm_attn_desc* desc, const void* q, const void* k_cache,
+                           const void* v_cache, void* out, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * dlm_head_rowstats -- tied-embedding head fused with per-row statistics and the p.E
