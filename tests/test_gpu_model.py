@@ -1,4 +1,5 @@
 """GPU parity of the whole round, the block loop, the commit pass and prefill."""
+import contextlib
 import sys
 
 import numpy as np
@@ -103,8 +104,36 @@ def _valid_commit(rule_args, maxprob, open_rows, chosen):
     return sel
 
 
+@contextlib.contextmanager
+def _kernel_arithmetic():
+    """Inside the block the oracle's attention is the error model of the library's bf16
+    attention kernel (tests/parity.py): the oracle's model then deviates from the plain
+    oracle by what a correct kernel's roundings alone move it."""
+    import oracle.block as ob
+    from tests.parity import kernel_attention_model
+    saved = ob.attention
+    ob.attention = kernel_attention_model
+    try:
+        yield
+    finally:
+        ob.attention = saved
+
+
+def _kernel_model_hidden(om, kv, tokens, committed, pe_prev, prec):
+    """The final hidden state of a round under the kernel-arithmetic error model."""
+    from oracle.loop import selfcond, forward_block, final_hidden
+    kv = kv.copy()
+    with _kernel_arithmetic():
+        x = selfcond(om, tokens, committed, pe_prev, prec)
+        return final_hidden(om, forward_block(om, x, kv, kv.length, prec), prec)
+
+
+def _rel_rows(a, b):
+    return np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)
+
+
 def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_scales=None, check_rounds=None,
-              cache_layers=True, fused_layers=False):
+              cache_layers=True, fused_layers=False, trunk_model=False):
     """Run rounds one at a time; after each round recompute it with the oracle from the
     GPU's own round-start state and compare the statistics and the commit.
 
@@ -112,7 +141,15 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
     oracle logit is within the logit tolerance of the row's maximum is a valid argmax, and
     a commit set is valid when it is the rule applied to maxprob values that agree with the
     oracle's within their tolerance.  Such differences are counted, and the ones whose
-    oracle top-2 gap is below 1e-3 are reported separately."""
+    oracle top-2 gap is below 1e-3 are reported separately.
+
+    trunk_model (deep models): the attention kernel rounds its probabilities to bf16 before
+    P V, which the oracle does not, and through tens of layers the hidden state moves by a
+    few 1e-2 of its norm; a max logit then moves by several tol_l while lse (a sum over the
+    vocabulary) does not.  The round is then checked in two stages: the final hidden state
+    against the oracle's, within twice what the kernel-arithmetic error model deviates by
+    (plus 1e-3), and the head statistics against the oracle's head applied to the GPU's own
+    hidden state, at the tolerances below."""
     dlm = _dlm()
     _say(f"lockstep {shape.name} d={shape.d} L={shape.n_layers} seed={seed} kv_scales={kv_scales}")
     cap = prompt_len + (n_blocks + 1) * shape.block
@@ -131,7 +168,7 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
     else:
         tol_l, tol_e = 1e-4, 1e-4
     counts = {"rounds": 0, "argmax_diff": 0, "argmax_diff_gap_lt_1e-3": 0, "commit_diff": 0, "worst_pe_rel": 0.0,
-              "worst_lse_abs": 0.0}
+              "worst_lse_abs": 0.0, "worst_trunk_rel": 0.0, "worst_trunk_rel_model": 0.0}
     for blk in range(n_blocks):
         m.decode_begin()
         r = 0
@@ -144,10 +181,11 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
             tokens = m.tokens.cpu().numpy().copy()
             pe_prev = m.view("pe", (B, d), torch.float32).cpu().numpy().astype(np.float64)
             L = int(m.len_dev.item())
-            kv = KVCache(*_cache_values(m, kv_scales), L)
+            check = (check_rounds is None and r % check_every == 0) or (check_rounds is not None and r in check_rounds)
+            kv = KVCache(*_cache_values(m, kv_scales), L) if check else None
             m.decode_round(rule)
             torch.cuda.synchronize()
-            if (check_rounds is None and r % check_every == 0) or (check_rounds is not None and r in check_rounds):
+            if check:
                 _say(f"  block {blk} round {r}: oracle recompute at prefix {L}")
                 res = oracle.denoise_round(om, kv, tokens.copy(), committed.copy(), None if r == 0 else pe_prev, r,
                                            orule, prec, want_logits=True)
@@ -158,6 +196,26 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
                 g_committed = m.view("committed", (B,), torch.uint8).cpu().numpy()
                 open_rows = np.nonzero(committed == 0)[0]
                 ref = res.stats
+                if trunk_model:
+                    g_hn = m.view("hn", (B, d), torch.bfloat16).float().cpu().numpy().astype(np.float64)
+                    hn_model = _kernel_model_hidden(om, kv, tokens, committed, None if r == 0 else pe_prev, prec)
+                    e_gpu = _rel_rows(g_hn[open_rows], res.hn[open_rows]).max()
+                    e_model = _rel_rows(hn_model[open_rows], res.hn[open_rows]).max()
+                    _say(f"    final hidden state: GPU vs oracle {e_gpu:.3e}, kernel-arithmetic model vs oracle "
+                         f"{e_model:.3e}, GPU vs model {_rel_rows(g_hn[open_rows], hn_model[open_rows]).max():.3e}")
+                    counts["worst_trunk_rel"] = max(counts["worst_trunk_rel"], float(e_gpu))
+                    counts["worst_trunk_rel_model"] = max(counts["worst_trunk_rel_model"], float(e_model))
+                    assert e_gpu <= 2 * e_model + 1e-3, (e_gpu, e_model)
+                    ref = oracle.head_rowstats(g_hn, om.emb_stored(), committed, prec, want_logits=True)
+                dmp = np.abs(g["maxprob"][open_rows] / ref["maxprob"][open_rows] - 1)
+                if dmp.max() > tol_l:
+                    for i in open_rows[np.argsort(-dmp)[:4]]:
+                        lg = ref["logits"][i]
+                        _say(f"    row {i}: lse gpu {g['lse'][i]:.5f} ref {ref['lse'][i]:.5f}; maxprob gpu "
+                             f"{g['maxprob'][i]:.6g} ref {ref['maxprob'][i]:.6g}; argmax gpu {g['argmax'][i]} ref "
+                             f"{ref['argmax'][i]}; ref logit there {lg[g['argmax'][i]]:.5f}, ref max {lg.max():.5f}, "
+                             f"gpu max logit {g['lse'][i] + np.log(g['maxprob'][i]):.5f}; top2 gap "
+                             f"{ref['top2_gap'][i]:.3g}")
                 np.testing.assert_allclose(g["lse"][open_rows], ref["lse"][open_rows], atol=tol_l, rtol=0)
                 np.testing.assert_allclose(g["entropy"][open_rows], ref["entropy"][open_rows], rtol=tol_e,
                                            atol=tol_e * 1e-2)

@@ -9,13 +9,9 @@ import pytest
 
 import oracle
 import synth
-from tests.parity import attention_ok, attention_errors
+from tests.parity import attention_ok, attention_errors, kernel_attention_model, split_bounds
 
 B, HQ, HKV, D = 32, 4, 1, 128
-
-
-def _bf16(x):
-    return oracle.bf16_round(x)
 
 
 def _inputs(L, seed):
@@ -25,35 +21,10 @@ def _inputs(L, seed):
     return q, k, v
 
 
-def _split_bounds(N, nsplit_max=32, unit=64):
-    chunk = -(-N // (nsplit_max * unit)) * unit
-    return [(s, min(N, s + chunk)) for s in range(0, N, chunk)]
-
-
 def _emulated_bf16_path(q, k, v, drop=None):
-    """The error model of the library's bf16 attention, emulated in numpy: per key split,
-    probabilities exp(s - m) rounded to bf16 before P V, the split's normalised output
-    stored in bf16, splits merged by their (max, sum) in float32, the result rounded to
-    bf16.  drop: index of a split left out of the merge (the failure to catch)."""
-    N = k.shape[1]
-    scale = 1.0 / math.sqrt(D)
-    out = np.zeros_like(q)
-    for h in range(HQ):
-        s_all = (q[:, h, :] @ k[0].T) * scale
-        parts = []
-        for si, (c0, c1) in enumerate(_split_bounds(N)):
-            if si == drop:
-                continue
-            s = s_all[:, c0:c1]
-            m = s.max(axis=1, keepdims=True)
-            e = np.exp(s - m)
-            o = (_bf16(e) @ v[0, c0:c1]) / e.sum(axis=1, keepdims=True)
-            parts.append((_bf16(o), m[:, 0], e.sum(axis=1)))
-        M = np.max([p[1] for p in parts], axis=0)
-        w = [p[2] * np.exp(p[1] - M) for p in parts]
-        num = sum(wi[:, None] * p[0] for wi, p in zip(w, parts))
-        out[:, h, :] = _bf16(num / sum(w)[:, None])
-    return out
+    """The library's bf16 roundings on the oracle's inputs, the combined output rounded to
+    bf16 as the library stores it."""
+    return oracle.bf16_round(kernel_attention_model(q, k, v, 1.0 / math.sqrt(D), drop=drop))
 
 
 @pytest.mark.parametrize("L", [512, 4096, 32768])
@@ -70,7 +41,7 @@ def test_criterion_accepts_the_bf16_roundings(L):
 def test_criterion_rejects_a_dropped_split(L):
     q, k, v = _inputs(L, 1251)
     ref = oracle.attention(q, k, v, 1.0 / math.sqrt(D))
-    n = len(_split_bounds(L + B))
+    n = len(split_bounds(L + B))
     assert n >= 22
     for drop in (0, n // 2, n - 2):
         assert not attention_ok(_emulated_bf16_path(q, k, v, drop=drop), ref), drop
@@ -81,7 +52,7 @@ def test_criterion_rejects_zero_and_scaled_outputs():
     ref = oracle.attention(q, k, v, 1.0 / math.sqrt(D))
     assert not attention_ok(np.zeros_like(ref), ref)
     assert not attention_ok(ref * 1.03, ref)            # a 3 % value-scale error (e.g. an FP8 scale)
-    assert attention_ok(_bf16(ref), ref)
+    assert attention_ok(oracle.bf16_round(ref), ref)
 
 
 def test_criterion_rejects_a_wrong_kv_head():
