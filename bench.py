@@ -360,20 +360,13 @@ def main():
     pipelined = not args.separate_commit
     bufs = [torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(2)]
 
-    prefill_ms = []
-
     def run(k, steps, warmup, in_order=False):
         """Time `steps` blocks at fixed k: the sampled blocks of the generation (each at its own
         prefix), or (in_order) the generation's first `steps` blocks one after the other."""
         rule = dlm.CommitRule.fixed_k(k)
         model.set_len(0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
         model.prefill(prompt)
-        e1.record()
         torch.cuda.synchronize()
-        prefill_ms.append(e0.elapsed_time(e1))
         prev = None
         if pipelined:
             # at least three warmup blocks: every graph the timed loop replays (first block,
@@ -463,6 +456,33 @@ def main():
         del model
         model = bf16_model
         torch.cuda.empty_cache()
+
+    # ---- prefill of the prompt: the wide forwards of dlm_prefill (up to 256 rows each) against
+    # 64- and 32-row forwards (dlm_prefill_rows), warm calls, median of 3, HIP events
+    def time_prefill(max_rows):
+        ts = []
+        for _ in range(4):
+            model.set_len(0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            model.prefill(prompt, max_rows=max_rows)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts[1:])[1]
+    D = shape.head_dim
+    per_layer = (shape.hq + 2 * shape.hkv) * D * shape.d + shape.d * shape.hq * D + 3 * shape.ffn * shape.d
+    qkv_last = (shape.hq + 2 * shape.hkv) * D * shape.d
+    prefill_gemm_flop = 2 * args.prompt * ((shape.n_layers - 1) * per_layer + qkv_last)
+    pf = {r: time_prefill(r) for r in (256, 64, 32)}
+    prefill = {"tokens": args.prompt, "ms": round(pf[256], 3), "tok_s": round(args.prompt / (pf[256] / 1e3), 1),
+               "gemm_tflop_s": round(prefill_gemm_flop / (pf[256] / 1e3) / 1e12, 1),
+               "ms_64_rows": round(pf[64], 3), "ms_32_rows": round(pf[32], 3),
+               "how": "dlm_prefill (forwards of up to 256 rows), warm, median of 3; also 64- and 32-row "
+                      "forwards (dlm_prefill_rows); gemm_tflop_s counts the projections' 2 x params x tokens"}
+    log(f"prefill {args.prompt} tokens: {pf[256]:.2f} ms wide ({prefill['gemm_tflop_s']} TFLOP/s in the "
+        f"projections), {pf[64]:.2f} ms in 64-row forwards, {pf[32]:.2f} ms in 32-row forwards")
 
     # ---- dominant kernel: the FFN gate/up projection + SwiGLU, the round's largest weight
     # stream, launched alone exactly as inside the round (dlm_ffn_gate_up: same kernel, plan
@@ -668,9 +688,7 @@ def main():
                    "d": s.d, "ffn": s.ffn, "vocab": s.vocab},
         "rounds_per_s": h["rounds_s"], "hbm_frac_step": h["hbm_frac"], "tpf": h["tpf"],
         "value_per_seed": {k: round(v, 2) for k, v in per_seed.items()},
-        "prefill": {"tokens": args.prompt, "ms": round(prefill_ms[0], 3),
-                    "tok_s": round(args.prompt / (prefill_ms[0] / 1e3), 1),
-                    "how": "64-row forwards over pairs of 32-token prompt blocks, HIP events, first leg"},
+        "prefill": prefill,
         "hbm_stream_measured": stream, "ops": ops, "fp8_cache": fp8_cache,
         "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
                   for k, r in results.items()},

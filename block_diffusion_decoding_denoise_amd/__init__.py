@@ -128,6 +128,7 @@ def lib():
         "dlm_decode_block": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, sz, vp]),
         "dlm_decode_block_pipelined": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, vp, sz, vp]),
         "dlm_prefill": (i, [vp, vp, i, P(KV), vp, sz, vp]),
+        "dlm_prefill_rows": (i, [vp, vp, i, P(KV), vp, sz, i, vp]),
         "dlm_decode_views_get": (i, [vp, P(KV), vp, sz, P(DecodeViews)]),
         "dlm_decode_round": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, sz, vp]),
         "dlm_decode_begin": (i, [vp, P(KV), vp, vp, vp, sz, vp]),
@@ -417,10 +418,16 @@ class Model:
     def set_len(self, n):
         self.len_dev.fill_(int(n))
 
-    def prefill(self, ids):
+    def prefill(self, ids, max_rows=None):
+        """Append the prompt's K/V (dlm_prefill; with max_rows, dlm_prefill_rows: at most that
+        many rows per forward)."""
         ids = ids.to(device=self.device, dtype=torch.int32).contiguous()
-        _check(lib().dlm_prefill(self.handle, _ptr(ids), ids.numel(), ctypes.byref(self.kv), _ptr(self.ws),
-                                 self.ws.numel(), _stream()), "dlm_prefill")
+        if max_rows is None:
+            _check(lib().dlm_prefill(self.handle, _ptr(ids), ids.numel(), ctypes.byref(self.kv), _ptr(self.ws),
+                                     self.ws.numel(), _stream()), "dlm_prefill")
+        else:
+            _check(lib().dlm_prefill_rows(self.handle, _ptr(ids), ids.numel(), ctypes.byref(self.kv), _ptr(self.ws),
+                                          self.ws.numel(), int(max_rows), _stream()), "dlm_prefill_rows")
 
     def decode_block(self, rule: CommitRule, tokens=None, state=None):
         tokens = self.tokens if tokens is None else tokens

@@ -614,13 +614,20 @@ static bool fusable(const dlm_model* m) {
   return m->d.dtype == DLM_BF16 && m->d.block == 32;
 }
 
+// Dense bf16 models with 32-row blocks take the prompt in forwards of up to 256 rows (8 blocks,
+// block-causal among themselves); the wide GEMMs split those rows over the waves.
+constexpr int kWideBlocks = 8;
+static bool wide_ok(const dlm_model* m) {
+  return m->d.dtype == DLM_BF16 && m->d.block == 32 && m->d.n_experts == 0 && !m->fused;
+}
+
 static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) {
   const dlm_model_desc& d = m->d;
   const size_t el = d.dtype == DLM_BF16 ? 2 : 4;
   // buffers hold 32 rows (the GEMM B operand reads 32), the layer buffers 64 when a round can
   // carry the previous block's commit rows
   const int B = 32;
-  const int BL = fusable(m) ? 64 : 32;
+  const int BL = wide_ok(m) ? 32 * kWideBlocks : fusable(m) ? 64 : 32;
   const int qd = d.hq * d.head_dim;
   const int F = d.n_experts ? d.expert_ffn : d.ffn;
   size_t off = 0;
@@ -729,7 +736,7 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
   const dlm_model_desc& d = m->d;
   const int bf = d.dtype == DLM_BF16;
   const int D = d.head_dim, qd = d.hq * D;
-  const int B = nqb == 1 ? d.block : 64;   // rows through the GEMMs and norms
+  const int B = nqb == 1 ? d.block : 32 * nqb;   // rows through the GEMMs and norms
   const char* pk = (const char*)m->packed;
   int rc;
   PartialSrc ps{};
@@ -1160,29 +1167,51 @@ extern "C" int dlm_commit_pass(const dlm_model* m, const dlm_kv* kv, const int32
   return enqueue_commit_pass(m, kv, tokens, w, (hipStream_t)stream);
 }
 
-extern "C" int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
-                           size_t ws_bytes, void* stream) {
+// The prompt as forwards of up to max_blocks blocks: each forward's rows attend to the cached
+// prefix and, block-causally, to each other (block j of the forward sees blocks 0 .. j), as a
+// run of consecutive commit passes would.  Wide forwards (3 to 8 blocks) go to the dense bf16
+// models, pairs to the models that run 64-row rounds, single blocks to every model.
+static int enqueue_prefill(const dlm_model* m, const int32_t* ids, int nb, const dlm_kv* kv, const DecodeWs& w,
+                           int max_blocks, hipStream_t st) {
+  const dlm_model_desc& d = m->d;
+  const int B = d.block;
+  int rc;
+  for (int b = 0; b < nb;) {
+    int c = std::min(max_blocks, nb - b);
+    if (c >= 3 && !wide_ok(m)) c = 2;
+    if (c == 2 && !fusable(m)) c = 1;
+    if (c == 1) {
+      if ((rc = enqueue_commit_pass(m, kv, ids + (size_t)b * B, w, st))) return rc;
+    } else {
+      if ((rc = embed(ids + (size_t)b * B, m->emb, w.x, c * B, d.d, d.vocab, 1, st))) return rc;
+      PartialSrc ps{};
+      if ((rc = enqueue_layers(m, kv, w, nullptr, /*last_kv_only=*/true, st, &ps, /*nqb=*/c))) return rc;
+      if ((rc = len_add(kv->len_dev, c * B, st))) return rc;
+    }
+    b += c;
+  }
+  return DLM_OK;
+}
+
+static int prefill_impl(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws, size_t ws_bytes,
+                        int max_blocks, void* stream) {
   int rc = check_decode(m, kv, ws, ws_bytes);
   if (rc) return rc;
   DLM_REQUIRE(ids, DLM_ERR_ARG, "null ids");
   DLM_REQUIRE(n >= 0 && n % m->d.block == 0, DLM_ERR_SHAPE, "n must be a multiple of the block size");
   DLM_DEVICE_CHECK();
-  DecodeWs w = decode_layout(m, kv, (char*)ws);
-  const int B = m->d.block, nb = n / B;
-  hipStream_t st = (hipStream_t)stream;
-  int b = 0;
-  // models that run 64-row forwards take the prompt two blocks per pass: the second block's
-  // rows attend to the first block's keys and their own, as in two consecutive commit passes
-  if (fusable(m)) {
-    for (; b + 1 < nb; b += 2) {
-      const dlm_model_desc& d = m->d;
-      if ((rc = embed(ids + (size_t)b * B, m->emb, w.x, 2 * B, d.d, d.vocab, 1, st))) return rc;
-      PartialSrc ps{};
-      if ((rc = enqueue_layers(m, kv, w, nullptr, /*last_kv_only=*/true, st, &ps, /*nqb=*/2))) return rc;
-      if ((rc = len_add(kv->len_dev, 2 * B, st))) return rc;
-    }
-  }
-  for (; b < nb; ++b)
-    if ((rc = enqueue_commit_pass(m, kv, ids + (size_t)b * B, w, st))) return rc;
-  return DLM_OK;
+  const DecodeWs w = decode_layout(m, kv, (char*)ws);
+  return enqueue_prefill(m, ids, n / m->d.block, kv, w, max_blocks, (hipStream_t)stream);
+}
+
+extern "C" int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return prefill_impl(m, ids, n, kv, ws, ws_bytes, kWideBlocks, stream);
+}
+
+extern "C" int dlm_prefill_rows(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
+                                size_t ws_bytes, int max_rows, void* stream) {
+  DLM_REQUIRE(m, DLM_ERR_ARG, "model is null");
+  DLM_REQUIRE(max_rows >= m->d.block, DLM_ERR_ARG, "max_rows must be at least one block");
+  return prefill_impl(m, ids, n, kv, ws, ws_bytes, std::min(kWideBlocks, max_rows / m->d.block), stream);
 }

@@ -126,8 +126,8 @@ size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl, int nqb) {
 int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, int hkv, int D,
               int B, int nqb, int cap, float scale, const int32_t* len_dev, int len_host,
               const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st, AttnKv kvf) {
-  if (nqb < 1 || nqb > 2 || (nqb == 2 && B != 32))
-    return fail(DLM_ERR_SHAPE, "attention: one query block, or two of 32 rows");
+  if (nqb < 1 || nqb > 8 || (nqb > 1 && B != 32))
+    return fail(DLM_ERR_SHAPE, "attention: one query block, or up to eight of 32 rows");
   AttnP p;
   p.out_packed = out_packed;
   p.q = (const uint16_t*)q;

@@ -383,6 +383,167 @@ __global__ __launch_bounds__(256, 1) void gemm_owned_kernel(GemmP p) {
   DLM_TRACE_POINT(4);
 }
 
+// ------------------------------------------------------------------ wide activation blocks
+// 64 < M <= 256 rows (the prompt's forward passes).  The same packed weights and plans as the
+// block's skinny GEMMs, but the 4 waves split the rows instead of the contraction: wave w
+// takes the 32-row panels w and w + 4 and runs every step of its workgroup's weight range, so
+// each wave's accumulators hold complete sums (no reduction between waves, no LDS).  The 4
+// waves read the same weight fragments close together in time: one read from HBM, the rest
+// from the compute unit's cache.  Each weight fragment feeds 2 (x NS) products.
+
+__device__ inline void wide_epilogue(const GemmP& p, int rowbase, int rows_s, const f32x16_t& a, int panel,
+                                     int lane) {
+  const int m = 32 * panel + (lane & 31);
+  if (m >= p.ep.M) return;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+    if (row < rows_s) epi_pair_packed(p.ep, p.map, rowbase + row, m, a[r], a[r + 1]);
+  }
+}
+
+// Row-owned plan (the weights packed with pack_bf16_owned for p.R): workgroup g owns packed
+// rows [g R, g R + R) over the full K.
+template <int NS, int P>
+__global__ __launch_bounds__(256, 1) void gemm_wide_owned_kernel(GemmP p) {
+  if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int npan = (p.ep.M + 31) / 32;
+  if (v >= npan) return;                       // no barriers below: idle waves may leave
+  const bool two = v + 4 < npan;
+  const int g = blockIdx.x;
+  const int R = p.R;
+  const uint32_t step_bytes = (uint32_t)R * 32u;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.W + (size_t)g * R * p.K, step_bytes * (uint32_t)p.KT);
+  const uint32_t xpanel = (uint32_t)(32 * p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, (uint32_t)npan * xpanel);
+  uint32_t wo[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int rows_s = min(32, R - 32 * s);
+    const int i = lane & 31, h = lane >> 5;
+    wo[s] = i < rows_s ? (uint32_t)(512 * s + (i + rows_s * h) * 8) * 2u : 0x80000000u;
+  }
+  // the wave's two panels (the second past the rows reads zeros)
+  const uint32_t xo0 = (uint32_t)lane * 16u + (uint32_t)v * xpanel;
+  const uint32_t xo1 = two ? xo0 + 4u * xpanel : 0x80000000u;
+  // workgroups start at different steps (as in the skinny kernel) so the activation block is
+  // not requested at one address by every workgroup at once
+  const int kofs = (int)(((long long)g * p.KT) / p.NW);
+  auto step_of = [&](int i) -> int {
+    if (i >= p.KT) return -1;
+    return i + kofs >= p.KT ? i + kofs - p.KT : i + kofs;
+  };
+  u32x4_t wf[P][NS], xf[P][2];
+  auto issue = [&](int u, int i) {
+    const int r = step_of(i);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) wf[u][s] = bload16_nt(wr, r < 0 ? 0x80000000u : wo[s] + (uint32_t)r * step_bytes);
+    xf[u][0] = bload16(xr, r < 0 ? 0x80000000u : xo0 + (uint32_t)r * 1024u);
+    xf[u][1] = bload16(xr, r < 0 || !two ? 0x80000000u : xo1 + (uint32_t)r * 1024u);
+  };
+#pragma unroll
+  for (int u = 0; u < P; ++u) issue(u, u);
+  f32x16_t acc[NS][2];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[s][j][r] = 0.f;
+  for (int k0 = 0; k0 < p.KT; k0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        acc[s][0] = mfma32x32x16(wf[u][s], xf[u][0], acc[s][0]);
+        acc[s][1] = mfma32x32x16(wf[u][s], xf[u][1], acc[s][1]);
+      }
+      issue(u, k0 + u + P);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int rows_s = min(32, R - 32 * s);
+    wide_epilogue(p, g * R + 32 * s, rows_s, acc[s][0], v, lane);
+    if (two) wide_epilogue(p, g * R + 32 * s, rows_s, acc[s][1], v + 4, lane);
+  }
+}
+
+// Stream-K plan (the weights in the (tile, step) unit stream), deferred output only: the wave
+// runs its workgroup's unit range in order and, at the end of each tile segment, stores its
+// panels' sums as the workgroup's partial of that tile ([tile][contributor][m][n], m over all
+// panels); the RMSNorm that consumes the residual adds the partials.
+template <int P>
+__global__ __launch_bounds__(256, 1) void gemm_wide_streamk_kernel(GemmP p) {
+  if (p.ep.cont_dev && *p.ep.cont_dev == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int npan = (p.ep.M + 31) / 32;
+  if (v >= npan) return;                       // no barriers below
+  const bool two = v + 4 < npan;
+  const int g = blockIdx.x;
+  const long long T = (long long)p.tiles * p.KT;
+  const int s0 = (int)((long long)g * T / p.NW), s1 = (int)((long long)(g + 1) * T / p.NW);
+  const int n = s1 - s0;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.W + (size_t)s0 * 512, (uint32_t)n * 1024u);
+  const uint32_t xpanel = (uint32_t)(32 * p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X, (uint32_t)npan * xpanel);
+  const uint32_t xo0 = (uint32_t)lane * 16u + (uint32_t)v * xpanel;
+  const uint32_t xo1 = two ? xo0 + 4u * xpanel : 0x80000000u;
+  u32x4_t wf[P], xf[P][2];
+  auto issue = [&](int u, int i) {
+    const bool ok = i < n;
+    const int kt = (s0 + i) % p.KT;
+    wf[u] = bload16_nt(wr, ok ? (uint32_t)lane * 16u + (uint32_t)i * 1024u : 0x80000000u);
+    xf[u][0] = bload16(xr, ok ? xo0 + (uint32_t)kt * 1024u : 0x80000000u);
+    xf[u][1] = bload16(xr, ok && two ? xo1 + (uint32_t)kt * 1024u : 0x80000000u);
+  };
+  auto flush = [&](int t, f32x16_t (&a)[2]) {
+    int fo;
+    contributors(p, t, T, &fo);
+    float* base = p.partial + ((size_t)t * p.cmax + (g - fo)) * (size_t)(1024 * npan);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j == 1 && !two) break;
+      const int m = 32 * (v + 4 * j) + (lane & 31);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4_t*)(base + (size_t)m * 32 + 8 * q + 4 * (lane >> 5)) =
+            f32x4_t{a[j][4 * q], a[j][4 * q + 1], a[j][4 * q + 2], a[j][4 * q + 3]};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[j][r] = 0.f;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < P; ++u) issue(u, u);
+  f32x16_t acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  int tcur = s0 / p.KT;
+  int nextb = (tcur + 1) * p.KT - s0;          // unit index where the next tile begins
+  for (int k0 = 0; k0 < n; k0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int i = k0 + u;
+      if (i < n) {
+        if (i == nextb) {
+          flush(tcur, acc);
+          ++tcur;
+          nextb += p.KT;
+        }
+        acc[0] = mfma32x32x16(wf[u], xf[u][0], acc[0]);
+        acc[1] = mfma32x32x16(wf[u], xf[u][1], acc[1]);
+      }
+      issue(u, i + P);
+    }
+  }
+  flush(tcur, acc);
+}
+
 // One workgroup per compute unit: the weight stream is split into equal contiguous ranges, so
 // every CU moves the same bytes and the workgroups finish together.  A range covers at most
 // MAXSEG tile segments (n <= 3 K/16 + 1 units).
@@ -423,7 +584,7 @@ static int gemm_cmax(int N, int K, int nw) {
   return (int)((K / 16) / minsteps + 2);
 }
 
-static int panels(int M) { return M > 32 ? 2 : 1; }
+static int panels(int M) { return (M + 31) / 32; }
 
 PartialSrc gemm_partials(int N, int K, GemmPlan plan, void* ws, int M) {
   PartialSrc ps;
@@ -464,9 +625,26 @@ int gemm_bf16(const void* W, const void* X, int N, int K, int map_kind, const Ep
   p.partial = (float*)((char*)ws + kCounterBytes);
   p.ep = ep;
   p.R = plan.R;
-  if (ep.M < 1 || ep.M > 64) return fail(DLM_ERR_SHAPE, "gemm: %d rows (1..64 supported)", ep.M);
+  if (ep.M < 1 || ep.M > 256) return fail(DLM_ERR_SHAPE, "gemm: %d rows (1..256 supported)", ep.M);
   const int mb = panels(ep.M);
   auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(p.NW), dim3(256), 0, st, p); };
+  if (ep.M > 64) {
+    // wide blocks: row-owned plans with any row-owned epilogue, stream-K plans deferred only
+    if (plan.R > 0) {
+      if (ep.kind == EPI_PARTIAL) return fail(DLM_ERR_ARG, "gemm: row-owned plan has no partial sums");
+      if (N != plan.R * plan.splits || plan.R % 2 || plan.R > 32 * kMaxSub)
+        return fail(DLM_ERR_SHAPE, "gemm: bad row-owned plan");
+      const int ns = (plan.R + 31) / 32;
+      if (ns == 1) launch(gemm_wide_owned_kernel<1, 8>);
+      else if (ns == 2) launch(gemm_wide_owned_kernel<2, 8>);
+      else if (ns == 3) launch(gemm_wide_owned_kernel<3, 6>);
+      else launch(gemm_wide_owned_kernel<4, 4>);
+    } else {
+      if (ep.kind != EPI_PARTIAL) return fail(DLM_ERR_ARG, "gemm: more than 64 rows on a stream-K plan need deferred output");
+      launch(gemm_wide_streamk_kernel<8>);
+    }
+    return check_hip(hipGetLastError(), "gemm_bf16 launch");
+  }
   if (plan.R > 0) {
     if (ep.kind == EPI_PARTIAL) return fail(DLM_ERR_ARG, "gemm: row-owned plan has no partial sums");
     if (N != plan.R * plan.splits || plan.R % 2 || plan.R > 32 * kMaxSub)

@@ -362,13 +362,24 @@ int dlm_decode_block_pipelined(const dlm_model* m, const dlm_commit_rule* rule, 
                                const int32_t* prev_tokens, int32_t* tokens, dlm_round_state* state,
                                void* ws, size_t ws_bytes, void* stream);
 
-/* Commit passes over n / block consecutive prompt blocks (n % block == 0): forwards each
- * block of ids (device int32 [n]) and appends its K/V; L += n.  bf16 models with block = 32 take
- * two blocks per 64-row forward (the second block's rows attend to the first block's keys and
- * their own, the prompt attention being block-causal), with the same cache as one pass per
- * block; an odd last block runs alone. */
+/* The prompt: forwards over the n / block consecutive blocks of ids (device int32 [n], n %
+ * block == 0) that append every block's K/V; L += n.  Each forward takes several blocks at
+ * once, block-causally (a block's rows attend to the cached prefix, to the earlier blocks of
+ * the forward and to each other), so its K/V are those of one commit pass per block, and the
+ * weights stream once per forward instead of once per block.  The prompt is processed as a
+ * whole, compute-dense pass, unlike the decode steps ([ORL-news] "dLLM 是什么，为什么能并行生成",
+ * on the prefill and decode phases).  Dense bf16 models with block = 32 take up to 8 blocks (256
+ * rows) per forward, the other bf16 models with block = 32 (MoE) 2 blocks, f32 models 1; a
+ * last forward takes what is left.  ws as for dlm_decode_block. */
 int dlm_prefill(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* dlm_prefill with at most max_rows rows per forward (max_rows >= block; rounded down to whole
+ * blocks and to what the model takes): max_rows = block gives one commit pass per block.  The
+ * caches agree with dlm_prefill's up to float summation order (a wider forward sums its GEMMs'
+ * products in another order).  DLM_ERR_ARG for max_rows < block. */
+int dlm_prefill_rows(const dlm_model* m, const int32_t* ids, int n, const dlm_kv* kv, void* ws,
+                     size_t ws_bytes, int max_rows, void* stream);
 
 /* Debug/test hooks on the decode workspace (device pointers into ws; NULL if absent). */
 typedef struct {

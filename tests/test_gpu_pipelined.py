@@ -133,8 +133,8 @@ def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args, kv
                                                          (MOE_SMALL, 1239, 160, False), (FUSED_SMALL, 1244, 160, True)],
                          ids=["small-3blocks", "qwen4b-2l", "moe-small-5blocks", "fused-small-5blocks"])
 def test_prefill_pairs_bitexact(shape, seed, prompt_len, fused):
-    """dlm_prefill forwards two prompt blocks per 64-row pass: the cache equals the one built
-    block by block (one prefill call per block), bitwise."""
+    """Prefill with 64-row forwards (two prompt blocks per pass, dlm_prefill_rows with 64 rows):
+    the cache equals the one built block by block (one prefill call per block), bitwise."""
     dlm = _dlm()
     _say(f"prefill in block pairs vs block by block: {shape.name} seed {seed} prompt {prompt_len}")
     if shape.n_experts:
@@ -147,7 +147,7 @@ def test_prefill_pairs_bitexact(shape, seed, prompt_len, fused):
         m, _ = _model(shape, seed, cap=prompt_len + 32, fused_layers=fused)
     prompt = torch.from_numpy(synth.prompt_ids(shape, prompt_len, seed))
     m.set_len(0)
-    m.prefill(prompt)
+    m.prefill(prompt, max_rows=64)
     torch.cuda.synchronize()
     assert int(m.len_dev.item()) == prompt_len
     k0 = [x[:, :prompt_len].clone() for x in m.k]
