@@ -244,6 +244,8 @@ def run_moe(args, torch, dlm, synth, np):
         torch.cuda.synchronize()
         model.set_len(args.prompt)
     hits = model.view("moe_hits", (s.n_layers,), torch.int32)
+    torch.cuda.synchronize()
+    hits_before = int(hits.sum().item())     # prefill and warm-up forwards (the workspace starts zeroed)
     hits.zero_()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -281,7 +283,10 @@ def run_moe(args, torch, dlm, synth, np):
            "tok_s": args.moe_blocks * B / sec, "rounds_s": args.moe_blocks * R / sec,
            "ms_per_block": 1e3 * sec / args.moe_blocks, "hbm_frac": total / sec / HBM_PEAK,
            "mean_experts_hit_per_layer_forward": total_hits / (args.moe_blocks * forwards_per_block),
-           "bytes_per_block": total / args.moe_blocks}
+           "bytes_per_block": total / args.moe_blocks,
+           # every forward of the leg (prefill, warm-up, timed): each distinct expert's weights
+           # and scales once per forward -- the algorithmic bytes of all its expert launches
+           "expert_bytes_all_forwards": (hits_before + total_hits) * moe_expert_bytes(s)}
     log(f"moe k={args.k}: {out['tok_s']:.0f} tok/s, {out['ms_per_block']:.2f} ms/block, "
         f"{100 * out['hbm_frac']:.1f}% of 8 TB/s, {out['mean_experts_hit_per_layer_forward']:.1f} experts/layer")
     model.close()
@@ -312,6 +317,9 @@ def main():
                     help="blocks of the MoE model decoded at k = --k (0 skips the MoE leg)")
     ap.add_argument("--separate-commit", action="store_true",
                     help="decode every block with its own commit pass instead of pipelining it")
+    ap.add_argument("--counter-legs", action="store_true",
+                    help="only the legs the HBM byte-counter runs read: head and attention ops, the "
+                         "gate/up launches, a 2-block MoE leg and the reference copy")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel leg plus a 256 MiB device copy (for counter runs)")
     ap.add_argument("--fused-layers", action="store_true",
@@ -411,7 +419,7 @@ def main():
 
     results = {}
     ks = [args.k] + [int(x) for x in args.k_list.split(",") if x and int(x) != args.k]
-    if args.roofline_only:
+    if args.roofline_only or args.counter_legs:
         ks = []
     def block_bytes(L, R, kv_elem_bytes=2):
         if pipelined:
@@ -475,14 +483,16 @@ def main():
     per_layer = (shape.hq + 2 * shape.hkv) * D * shape.d + shape.d * shape.hq * D + 3 * shape.ffn * shape.d
     qkv_last = (shape.hq + 2 * shape.hkv) * D * shape.d
     prefill_gemm_flop = 2 * args.prompt * ((shape.n_layers - 1) * per_layer + qkv_last)
-    pf = {r: time_prefill(r) for r in (256, 64, 32)}
+    counters_only = args.roofline_only or args.counter_legs
+    pf = {r: time_prefill(r) if not counters_only else float("nan") for r in (256, 64, 32)}
     prefill = {"tokens": args.prompt, "ms": round(pf[256], 3), "tok_s": round(args.prompt / (pf[256] / 1e3), 1),
                "gemm_tflop_s": round(prefill_gemm_flop / (pf[256] / 1e3) / 1e12, 1),
                "ms_64_rows": round(pf[64], 3), "ms_32_rows": round(pf[32], 3),
                "how": "dlm_prefill (forwards of up to 256 rows), warm, median of 3; also 64- and 32-row "
                       "forwards (dlm_prefill_rows); gemm_tflop_s counts the projections' 2 x params x tokens"}
-    log(f"prefill {args.prompt} tokens: {pf[256]:.2f} ms wide ({prefill['gemm_tflop_s']} TFLOP/s in the "
-        f"projections), {pf[64]:.2f} ms in 64-row forwards, {pf[32]:.2f} ms in 32-row forwards")
+    if not counters_only:
+        log(f"prefill {args.prompt} tokens: {pf[256]:.2f} ms wide ({prefill['gemm_tflop_s']} TFLOP/s in the "
+            f"projections), {pf[64]:.2f} ms in 64-row forwards, {pf[32]:.2f} ms in 32-row forwards")
 
     # ---- dominant kernel: the FFN gate/up projection + SwiGLU, the round's largest weight
     # stream, launched alone exactly as inside the round (dlm_ffn_gate_up: same kernel, plan
@@ -519,15 +529,26 @@ def main():
                 "bytes_per_launch": gemm_bytes, "us_per_launch": t_launch * 1e6, "launches": n_launch}
     log(f"gate/up + SwiGLU: {t_launch * 1e6:.1f} us/launch, {roofline['achieved']:.0f} GB/s")
 
-    if args.roofline_only:
+    if args.roofline_only or args.counter_legs:
+        extra = {}
+        if args.counter_legs:
+            extra["ops"] = run_ops(torch, dlm, dev_w["emb"], args.seed)
         # a plain device copy of known size, the reference for scaling the HBM byte counters
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         for _ in range(4):
             b.copy_(a)
         torch.cuda.synchronize()
-        print(json.dumps({"roofline": roofline, "copy_bytes_per_launch": a.numel(), "copy_launches": 4}), flush=True)
+        del a, b
         model.close()
+        if args.counter_legs:
+            del model
+            dev_w.clear()
+            torch.cuda.empty_cache()
+            args.moe_blocks = 2
+            extra["moe"] = run_moe(args, torch, dlm, synth, np)
+        print(json.dumps({"roofline": roofline, "copy_bytes_per_launch": 256 << 20, "copy_launches": 4, **extra}),
+              flush=True)
         return
 
     # ---- the head and attention ops alone (uses the model's embedding)
