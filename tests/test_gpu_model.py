@@ -267,7 +267,11 @@ def test_small_bf16_fp8_cache_lockstep():
 def test_prefill_fp8_cache_matches_oracle_cache():
     """Prefill into an FP8 cache: the codes the layers write against the oracle's quantised
     cache.  Layer 0 sees identical bf16 inputs, so its codes differ only where a k or v lies
-    within one bf16 unit of an e4m3 rounding boundary."""
+    within one bf16 unit of an e4m3 rounding boundary.  A later layer's inputs carry the
+    attention kernel's bf16 probabilities, which move some values across e4m3 boundaries (one
+    step, 6-12 % of the value): its relative deviation must stay within twice that of the
+    oracle's prefill under the kernel-arithmetic error model (same FP8 quantisation), plus
+    1e-3."""
     s = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
                           vocab=3001)
     sc = (0.125, 0.0625)
@@ -279,9 +283,13 @@ def test_prefill_fp8_cache_matches_oracle_cache():
     om = OracleModel(s, w, Prec("bf16", kv_scales=sc))
     kv = KVCache.empty(s, 128)
     oracle.prefill(om, kv, prompt, Prec("bf16", kv_scales=sc))
+    kvm = KVCache.empty(s, 128)
+    with _kernel_arithmetic():
+        oracle.prefill(om, kvm, prompt, Prec("bf16", kv_scales=sc))
     gks, gvs = _cache_values(m, sc)
     for l in range(s.n_layers):
-        for g, o, scale in ((gks[l][:, :96], kv.k[l][:, :96], sc[0]), (gvs[l][:, :96], kv.v[l][:, :96], sc[1])):
+        for g, o, mo, scale in ((gks[l][:, :96], kv.k[l][:, :96], kvm.k[l][:, :96], sc[0]),
+                                (gvs[l][:, :96], kv.v[l][:, :96], kvm.v[l][:, :96], sc[1])):
             step = scale * np.exp2(np.floor(np.log2(np.maximum(np.abs(o) / scale, 2.0 ** -6))) - 3)
             i = np.unravel_index(np.argmax(np.abs(g - o) / step), g.shape)
             _say(f"layer {l} scale {scale}: max |o| {np.abs(o).max():.4g}, differing {np.mean(g != o):.4f}, "
@@ -291,8 +299,10 @@ def test_prefill_fp8_cache_matches_oracle_cache():
                 assert np.all(np.abs(g - o) <= 1.01 * step), np.abs(g - o).max()
                 assert np.mean(g != o) < 1e-2, np.mean(g != o)
             else:
-                # the bf16-cache test's tolerance for a later layer, plus one e4m3 step
-                assert np.all(np.abs(g - o) <= 3e-2 + 2e-2 * np.abs(o) + 1.01 * step), np.abs(g - o).max()
+                e_gpu = np.linalg.norm(g - o) / np.linalg.norm(o)
+                e_model = np.linalg.norm(mo - o) / np.linalg.norm(o)
+                _say(f"   relative deviation: GPU {e_gpu:.3e}, kernel-arithmetic model {e_model:.3e}")
+                assert e_gpu <= 2 * e_model + 1e-3, (e_gpu, e_model)
 
 
 def test_small_bf16_threshold_lockstep():
