@@ -551,6 +551,35 @@ def main():
               flush=True)
         return
 
+    # ---- threshold blocks: the rounds after a block is done.  tau = 0 commits every row in round
+    # 0, so a 32-round budget leaves 31 rounds whose kernels only read the continue flag:
+    # dlm_decode_block (one graph of all 32) against dlm_decode_block_gated (round segments,
+    # the host checking the flag between them), and one fixed-k round as the floor
+    def time_threshold(fn, n=6):
+        for _ in range(2):
+            model.set_len(args.prompt)
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            model.set_len(args.prompt)
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    thr_rule = dlm.CommitRule.threshold(0.0, True, 32)
+    one_round = dlm.CommitRule.fixed_k(32)
+    threshold = {
+        "workload": "threshold rule tau=0 with forced top-1 and max_rounds=32 (the block is done in round 0), "
+                    "prompt 256, one block, separate commit pass",
+        "ms_block_graph": round(time_threshold(lambda: model.decode_block(thr_rule)), 3),
+        "ms_gated_seg1": round(time_threshold(lambda: model.decode_block_gated(thr_rule, seg_rounds=1)), 3),
+        "ms_gated_seg4": round(time_threshold(lambda: model.decode_block_gated(thr_rule, seg_rounds=4)), 3),
+        "ms_one_round_floor": round(time_threshold(lambda: model.decode_block(one_round)), 3)}
+    log(f"threshold block done in round 0 of 32: {threshold['ms_block_graph']:.2f} ms (all rounds enqueued), "
+        f"{threshold['ms_gated_seg1']:.2f} ms gated (segments of 1), one round alone {threshold['ms_one_round_floor']:.2f} ms")
+
     # ---- the head and attention ops alone (uses the model's embedding)
     ops = run_ops(torch, dlm, dev_w["emb"], args.seed) if not args.no_ops else None
 
@@ -714,7 +743,7 @@ def main():
         "per_k": {str(k): {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r.items()}
                   for k, r in results.items()},
         "roofline": roofline, "cpu_baseline": cpu, "cpu_baseline_1core": cpu1, "moe": moe,
-        "full_generation": full, "tiny_fp32": tiny,
+        "full_generation": full, "tiny_fp32": tiny, "threshold_dead_rounds": threshold,
     }
     print(json.dumps(line), flush=True)
     if model is not None:

@@ -129,6 +129,7 @@ def lib():
         "dlm_decode_block_pipelined": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, vp, sz, vp]),
         "dlm_prefill": (i, [vp, vp, i, P(KV), vp, sz, vp]),
         "dlm_prefill_rows": (i, [vp, vp, i, P(KV), vp, sz, i, vp]),
+        "dlm_decode_block_gated": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, sz, i, vp]),
         "dlm_decode_views_get": (i, [vp, P(KV), vp, sz, P(DecodeViews)]),
         "dlm_decode_round": (i, [vp, P(CommitRule), P(KV), vp, vp, vp, sz, vp]),
         "dlm_decode_begin": (i, [vp, P(KV), vp, vp, vp, sz, vp]),
@@ -434,6 +435,17 @@ class Model:
         state = self.state if state is None else state
         _check(lib().dlm_decode_block(self.handle, ctypes.byref(rule), ctypes.byref(self.kv), _ptr(tokens),
                                       _ptr(state), _ptr(self.ws), self.ws.numel(), _stream()), "dlm_decode_block")
+        return tokens
+
+    def decode_block_gated(self, rule: CommitRule, seg_rounds=1, tokens=None, state=None):
+        """dlm_decode_block without the rounds after the block is done (threshold rules): round
+        segments of seg_rounds, the host checking the continue flag between them; blocks the
+        calling thread until the commit pass is enqueued (dlm_decode_block_gated)."""
+        tokens = self.tokens if tokens is None else tokens
+        state = self.state if state is None else state
+        _check(lib().dlm_decode_block_gated(self.handle, ctypes.byref(rule), ctypes.byref(self.kv), _ptr(tokens),
+                                            _ptr(state), _ptr(self.ws), self.ws.numel(), int(seg_rounds),
+                                            _stream()), "dlm_decode_block_gated")
         return tokens
 
     def decode_block_pipelined(self, rule: CommitRule, prev_tokens, tokens, state=None):

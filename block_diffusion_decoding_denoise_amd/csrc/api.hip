@@ -356,6 +356,11 @@ struct dlm_model {
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::vector<hipGraph_t> graph_objs;
   hipStream_t cap_stream = nullptr;
+  // gated block decode (dlm_decode_block_gated): the continue flag after each round segment is
+  // copied to pinned host memory and an event marks it; two slots (one segment in flight ahead)
+  std::mutex gate_mu;
+  int32_t* gate_flags = nullptr;
+  hipEvent_t gate_ev[2] = {nullptr, nullptr};
 };
 
 static int check_model_desc(const dlm_model_desc* d) {
@@ -571,6 +576,9 @@ extern "C" void dlm_model_destroy(dlm_model* m) {
   for (auto& kv : m->graphs) hipGraphExecDestroy(kv.second);
   for (auto g : m->graph_objs) hipGraphDestroy(g);
   if (m->cap_stream) hipStreamDestroy(m->cap_stream);
+  for (hipEvent_t e : m->gate_ev)
+    if (e) hipEventDestroy(e);
+  if (m->gate_flags) hipHostFree(m->gate_flags);
   delete m;
 }
 
@@ -1080,21 +1088,16 @@ extern "C" int dlm_model_graph_count(const dlm_model* m) {
   return (int)mm->graphs.size();
 }
 
-// Captures (once per key) and launches the graph of one block.
-static int launch_block_graph(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
-                              const int32_t* prev_tokens, int pipelined, int32_t* tokens, dlm_round_state* state,
-                              void* ws, hipStream_t st) {
+// Captures (once per key) the work enq(stream) enqueues, and launches it.
+template <class Enq>
+static int launch_cached_graph(const dlm_model* m, const GraphKey& key, Enq enq, hipStream_t st) {
   dlm_model* mm = const_cast<dlm_model*>(m);
-  DecodeWs w = decode_layout(m, kv, (char*)ws);
-  GraphKey key;
-  block_graph_key(m, rule, kv, prev_tokens, pipelined, tokens, state, ws, &key);
   std::lock_guard<std::mutex> lock(mm->mu);
   auto it = mm->graphs.find(key);
   if (it == mm->graphs.end()) {
     if (!mm->cap_stream) DLM_HIP(hipStreamCreateWithFlags(&mm->cap_stream, hipStreamNonBlocking));
     DLM_HIP(hipStreamBeginCapture(mm->cap_stream, hipStreamCaptureModeThreadLocal));
-    int rc = pipelined ? enqueue_block_pipelined(m, *rule, kv, prev_tokens, tokens, state, w, mm->cap_stream)
-                       : enqueue_block(m, *rule, kv, tokens, state, w, mm->cap_stream);
+    int rc = enq(mm->cap_stream);
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(mm->cap_stream, &g);
     if (rc) {
@@ -1112,6 +1115,19 @@ static int launch_block_graph(const dlm_model* m, const dlm_commit_rule* rule, c
     it = mm->graphs.emplace(key, ex).first;
   }
   return check_hip(hipGraphLaunch(it->second, st), "hipGraphLaunch");
+}
+
+// Captures (once per key) and launches the graph of one block.
+static int launch_block_graph(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                              const int32_t* prev_tokens, int pipelined, int32_t* tokens, dlm_round_state* state,
+                              void* ws, hipStream_t st) {
+  const DecodeWs w = decode_layout(m, kv, (char*)ws);
+  GraphKey key;
+  block_graph_key(m, rule, kv, prev_tokens, pipelined, tokens, state, ws, &key);
+  return launch_cached_graph(m, key, [&](hipStream_t cs) {
+    return pipelined ? enqueue_block_pipelined(m, *rule, kv, prev_tokens, tokens, state, w, cs)
+                     : enqueue_block(m, *rule, kv, tokens, state, w, cs);
+  }, st);
 }
 
 extern "C" int dlm_decode_block(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv, int32_t* tokens,
@@ -1134,6 +1150,65 @@ extern "C" int dlm_decode_block_pipelined(const dlm_model* m, const dlm_commit_r
   DLM_REQUIRE(prev_tokens != tokens, DLM_ERR_ARG, "prev_tokens and tokens must be distinct buffers");
   DLM_DEVICE_CHECK();
   return launch_block_graph(m, rule, kv, prev_tokens, 1, tokens, state, ws, (hipStream_t)stream);
+}
+
+// A threshold block as graphs of seg_rounds rounds, one segment in flight ahead of the one the
+// host waits on: after each segment the continue flag goes to pinned host memory behind an
+// event, and no further segment is launched once a segment has ended the block.  At most one
+// speculative segment runs without work (its kernels read the flag and exit); the commit pass
+// follows as its own graph.  Graphs are cached under the block's key plus the segment kind.
+extern "C" int dlm_decode_block_gated(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                                      int32_t* tokens, dlm_round_state* state, void* ws, size_t ws_bytes,
+                                      int seg_rounds, void* stream) {
+  int rc = check_decode(m, kv, ws, ws_bytes);
+  if (rc) return rc;
+  if ((rc = check_rule(rule))) return rc;
+  DLM_REQUIRE(tokens && state, DLM_ERR_ARG, "null pointer");
+  DLM_REQUIRE(seg_rounds >= 1, DLM_ERR_ARG, "seg_rounds must be at least 1");
+  DLM_DEVICE_CHECK();
+  hipStream_t st = (hipStream_t)stream;
+  if (rule->mode == DLM_COMMIT_FIXED_K)   // the round count is known: no round runs without work
+    return launch_block_graph(m, rule, kv, nullptr, 0, tokens, state, ws, st);
+  dlm_model* mm = const_cast<dlm_model*>(m);
+  std::lock_guard<std::mutex> gate_lock(mm->gate_mu);
+  if (!mm->gate_flags) {
+    DLM_HIP(hipHostMalloc((void**)&mm->gate_flags, 2 * sizeof(int32_t), hipHostMallocDefault));
+    for (hipEvent_t& e : mm->gate_ev) DLM_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
+  const DecodeWs w = decode_layout(m, kv, (char*)ws);
+  const int S = std::min(seg_rounds, rule->max_rounds);
+  const int nseg = (rule->max_rounds + S - 1) / S;
+  GraphKey base;
+  block_graph_key(m, rule, kv, nullptr, 0, tokens, state, ws, &base);
+  auto key_of = [&](uint64_t kind) {
+    GraphKey k = base;
+    k.push_back(0x6761746564ull);   // gated-decode graphs
+    k.push_back(kind);
+    k.push_back((uint64_t)S);
+    return k;
+  };
+  auto launch_seg = [&](int j) -> int {
+    int r2 = launch_cached_graph(m, key_of(j == 0 ? 0 : 1), [&](hipStream_t cs) {
+      int r3;
+      if (j == 0 && (r3 = block_reset(m->d.block, w.committed, tokens, state, w.pe, 32 * m->d.d, cs))) return r3;
+      for (int r = 0; r < S; ++r)
+        if ((r3 = enqueue_round(m, *rule, kv, tokens, state, w, cs))) return r3;
+      return (int)DLM_OK;
+    }, st);
+    if (r2) return r2;
+    DLM_HIP(hipMemcpyAsync(&mm->gate_flags[j & 1], &state->cont, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    DLM_HIP(hipEventRecord(mm->gate_ev[j & 1], st));
+    return DLM_OK;
+  };
+  if ((rc = launch_seg(0))) return rc;
+  if (nseg > 1 && (rc = launch_seg(1))) return rc;
+  for (int j = 0; j < nseg; ++j) {
+    DLM_HIP(hipEventSynchronize(mm->gate_ev[j & 1]));
+    if (((volatile int32_t*)mm->gate_flags)[j & 1] == 0) break;   // segment j ended the block
+    if (j + 2 < nseg && (rc = launch_seg(j + 2))) return rc;
+  }
+  return launch_cached_graph(m, key_of(2), [&](hipStream_t cs) { return enqueue_commit_pass(m, kv, tokens, w, cs); },
+                             st);
 }
 
 extern "C" int dlm_decode_begin(const dlm_model* m, const dlm_kv* kv, int32_t* tokens, dlm_round_state* state,

@@ -362,6 +362,24 @@ int dlm_decode_block_pipelined(const dlm_model* m, const dlm_commit_rule* rule, 
                                const int32_t* prev_tokens, int32_t* tokens, dlm_round_state* state,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* dlm_decode_block for threshold rules without the rounds that run after the block is done.
+ * A graph cannot branch on the device here (HIP graphs have no conditional nodes), so
+ * dlm_decode_block enqueues max_rounds rounds and every kernel of a round after the block's
+ * end reads the continue flag and exits -- still one launch each.  This call replays graphs of
+ * seg_rounds rounds instead, one segment ahead of the one it waits for: after each segment
+ * the continue flag is copied to pinned host memory behind an event, the calling thread
+ * waits for that event, and no further segment is launched once the block is done; then it
+ * enqueues the commit pass and returns.  So at most one segment (seg_rounds rounds) runs
+ * without work, and the device never waits on the host while work remains.  Same tokens,
+ * state and cache as dlm_decode_block ([ORL-blog] "What shipped": the loop stops when the
+ * block is done).  Blocks the calling thread (unlike the other calls); a fixed-k rule (whose
+ * round count is known) takes dlm_decode_block's graph and does not block.  Calls on one
+ * model are serialised.  Other arguments and errors as dlm_decode_block; DLM_ERR_ARG for
+ * seg_rounds < 1. */
+int dlm_decode_block_gated(const dlm_model* m, const dlm_commit_rule* rule, const dlm_kv* kv,
+                           int32_t* tokens, dlm_round_state* state, void* ws, size_t ws_bytes,
+                           int seg_rounds, void* stream);
+
 /* The prompt: forwards over the n / block consecutive blocks of ids (device int32 [n], n %
  * block == 0) that append every block's K/V; L += n.  Each forward takes several blocks at
  * once, block-causally (a block's rows attend to the cached prefix, to the earlier blocks of
