@@ -250,6 +250,80 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
     return counts
 
 
+def _first_divergence_is_near_tie(g_committed, g_tokens, o_committed, o_tokens, stats, o_now, tol_l):
+    """At the first round where the GPU's and the oracle's blocks differ: every row committed by
+    both with different tokens has a GPU token whose oracle logit is within tol_l of the row's
+    maximum, and every row committed by only one side ranks (oracle max-probability) within
+    2 tol_l in log of the last row the oracle's fixed-k rule took.  Returns a description."""
+    both = np.nonzero((g_committed != 0) & (o_committed != 0) & (g_tokens != o_tokens))[0]
+    only = np.nonzero((g_committed != 0) != (o_committed != 0))[0]
+    notes = []
+    for i in both:
+        lg = stats["logits"][i]
+        gap = float(lg.max() - lg[g_tokens[i]])
+        notes.append(f"row {i}: token {g_tokens[i]} vs {o_tokens[i]}, oracle logit gap {gap:.2e}")
+        assert gap <= tol_l, notes[-1]
+    if len(only):
+        mp = stats["maxprob"]
+        ref = min(mp[i] for i in o_now)       # the weakest row the oracle's rule took this round
+        for i in only:
+            d = abs(float(np.log(mp[i]) - np.log(ref)))
+            notes.append(f"row {i}: committed by {'GPU' if g_committed[i] else 'oracle'} only, "
+                         f"log maxprob {np.log(mp[i]):.4f} vs boundary {np.log(ref):.4f}")
+            assert d <= 2 * tol_l, notes[-1]
+    return "; ".join(notes)
+
+
+def test_small_bf16_full_trajectory_first_divergence():
+    """bf16, GPU and oracle each on their own trajectory (nothing recomputed from the GPU's
+    state): blocks are compared round by round until their committed rows or tokens first
+    differ, which must be a near-tie in the oracle's statistics; the round is reported."""
+    dlm = _dlm()
+    s = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
+                          vocab=3001)
+    seed, P, n_blocks, k = 1240, 64, 4, 6
+    cap = P + (n_blocks + 1) * s.block
+    m, w = _gpu_model(s, seed, cap)
+    prec = Prec("bf16")
+    om = OracleModel(s, w, prec)
+    prompt = synth.prompt_ids(s, P, seed)
+    m.set_len(0)
+    m.prefill(torch.from_numpy(prompt))
+    kv = KVCache.empty(s, cap)
+    oracle.prefill(om, kv, prompt, prec)
+    rule = dlm.CommitRule.fixed_k(k)
+    orule = OCommitRule(1, 0.0, k, False, 32)
+    B = s.block
+    R = -(-B // k)
+    first = None
+    for blk in range(n_blocks):
+        m.decode_begin()
+        tok_o = np.zeros(B, np.int32)
+        com_o = np.zeros(B, np.uint8)
+        pe_prev = None
+        for r in range(R):
+            m.decode_round(rule)
+            torch.cuda.synchronize()
+            g_com = m.view("committed", (B,), torch.uint8).cpu().numpy().copy()
+            g_tok = m.tokens.cpu().numpy().copy()
+            res = oracle.denoise_round(om, kv, tok_o, com_o, pe_prev, r, orule, prec, want_logits=True)
+            pe_prev = res.stats["pe"]
+            same = np.array_equal(g_com, com_o) and np.array_equal(g_tok[com_o != 0], tok_o[com_o != 0])
+            if not same:
+                note = _first_divergence_is_near_tie(g_com, g_tok, com_o, tok_o, res.stats, res.committed_now, 2e-2)
+                first = (blk, r, note)
+                break
+        if first:
+            break
+        m.commit_pass()
+        oracle.commit_pass(om, kv, tok_o, prec)
+        assert np.array_equal(m.tokens.cpu().numpy(), tok_o)
+    if first:
+        _say(f"first divergence: block {first[0]} round {first[1]} ({first[2]}), a near-tie")
+    else:
+        _say(f"no divergence over {n_blocks} blocks of {R} rounds")
+
+
 def test_small_bf16_lockstep():
     s = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=2, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
                           vocab=3001)
