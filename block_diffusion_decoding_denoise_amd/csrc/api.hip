@@ -361,6 +361,7 @@ struct dlm_model {
   std::mutex gate_mu;
   int32_t* gate_flags = nullptr;
   hipEvent_t gate_ev[2] = {nullptr, nullptr};
+  int gate_last = -1;   // slot of the last flag copy a call left in flight (-1: none)
 };
 
 static int check_model_desc(const dlm_model_desc* d) {
@@ -1175,6 +1176,10 @@ extern "C" int dlm_decode_block_gated(const dlm_model* m, const dlm_commit_rule*
     DLM_HIP(hipHostMalloc((void**)&mm->gate_flags, 2 * sizeof(int32_t), hipHostMallocDefault));
     for (hipEvent_t& e : mm->gate_ev) DLM_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   }
+  // a flag copy the previous call left in flight (its last, speculative segment) must land
+  // before this call's copies reuse the slots, whatever stream it ran on
+  if (mm->gate_last >= 0) DLM_HIP(hipEventSynchronize(mm->gate_ev[mm->gate_last]));
+  mm->gate_last = -1;
   const DecodeWs w = decode_layout(m, kv, (char*)ws);
   const int S = std::min(seg_rounds, rule->max_rounds);
   const int nseg = (rule->max_rounds + S - 1) / S;
@@ -1198,6 +1203,7 @@ extern "C" int dlm_decode_block_gated(const dlm_model* m, const dlm_commit_rule*
     if (r2) return r2;
     DLM_HIP(hipMemcpyAsync(&mm->gate_flags[j & 1], &state->cont, sizeof(int32_t), hipMemcpyDeviceToHost, st));
     DLM_HIP(hipEventRecord(mm->gate_ev[j & 1], st));
+    mm->gate_last = j & 1;
     return DLM_OK;
   };
   if ((rc = launch_seg(0))) return rc;
