@@ -658,6 +658,37 @@ def main():
                          f"{t_round:.1f} s/round, {t_cp:.1f} s/commit pass"}
         log(f"cpu oracle: {cpu_tok_s:.3f} tok/s ({t_round:.1f} s/round)")
         del res
+        # the host, and the oracle's head and attention ops alone (float32 mode, same threads):
+        # the head at 32 open rows over the model's own embedding, the attention at the op leg's
+        # shapes (32 / 8 heads of 128, a 32-query block) on N(0, 1) inputs
+        model_name = ""
+        try:
+            for line_ in open("/proc/cpuinfo"):
+                if line_.startswith("model name"):
+                    model_name = line_.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+        cpu["host"] = {"cpu_model": model_name, "cpu_count": os.cpu_count()}
+        rng = np.random.default_rng(args.seed)
+        hq_ = rng.standard_normal((32, shape.d)).astype(np.float32)
+        hq_ /= np.sqrt((hq_ * hq_).mean(axis=1, keepdims=True))
+        hb_ = oracle.bf16_round(hq_).astype(np.float32)
+        t0 = time.perf_counter()
+        oracle.head_rowstats(hb_, w["emb"], np.zeros(32, np.uint8), prec)
+        t_head = time.perf_counter() - t0
+        t_attn = {}
+        for L_ in (512, 4096, 32768):
+            q_ = rng.standard_normal((B, 32, 128)).astype(np.float32)
+            k_ = rng.standard_normal((8, L_ + B, 128)).astype(np.float32)
+            v_ = rng.standard_normal((8, L_ + B, 128)).astype(np.float32)
+            t0 = time.perf_counter()
+            oracle.attention(q_, k_, v_, 1.0 / math.sqrt(128))
+            t_attn[L_] = time.perf_counter() - t0
+        cpu["ops"] = {"head_32_open_rows_s": round(t_head, 3),
+                      "attention_s": {str(L_): round(t, 4) for L_, t in t_attn.items()}}
+        log(f"cpu oracle ops: head (32 open rows) {t_head:.2f} s; attention " +
+            ", ".join(f"L={L_} {t:.3f} s" for L_, t in t_attn.items()))
 
     # ---- the tiny fp32 model: prompt 64, 4 blocks, threshold 0.9 with forced top-1, 32 rounds at
     # most (random weights: every round commits its top-1 only, so 32 rounds per block)
