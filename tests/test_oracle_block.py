@@ -195,3 +195,28 @@ def test_bf16_round_points():
     assert bf16_round(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6   # halfway, even is up
     assert bf16_round(np.array([1.0 + 2 ** -8 + 2 ** -20]))[0] == 1.0 + 2 ** -7
     assert bf16_round(np.array([-3.0]))[0] == -3.0
+
+
+def test_bf16_round_matches_library_conversion():
+    """On fp32 values (random magnitudes over 24 binades, both signs, plus exact halfway
+    cases) the oracle's rounding equals torch's float32 -> bfloat16 conversion, which rounds
+    to nearest even."""
+    import torch
+    from oracle import bf16_round
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-12, 12, 200000))).astype(np.float32)
+    # halfway between two bf16 values: a bf16 value plus half its unit in the last place
+    base = torch.from_numpy(x[:1000]).to(torch.bfloat16).float().numpy()
+    half = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, half])
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(bf16_round(x.astype(np.float64)), ref)
+
+
+def test_decode_storage_matches_library_widening():
+    import torch
+    from oracle import decode_storage
+    bits = np.random.default_rng(12).integers(0, 1 << 16, 100000, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]          # finite values only
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(decode_storage(bits), ref)
