@@ -49,6 +49,17 @@ def test_qwen4b_full_model_lockstep(prompt_len, rounds):
     assert counts["rounds"] == len(rounds)
 
 
+def test_qwen4b_full_model_lockstep_fused_layers():
+    """The opt-in fused layer path (one launch per sublayer, XCD-local synchronisation) at the
+    full 36-layer 4B shape, which it is built for: rounds 0 and 5 after a 256-token prompt,
+    checked in the same two stages; the XCD barriers and placement stay clean."""
+    t0 = time.time()
+    counts = _lockstep(synth.QWEN4B, 1274, 256, 1, (1, 0.0, 6, 0, 32), check_rounds={0, 5}, cache_layers=False,
+                       trunk_model=True, fused_layers=True)
+    _say(f"qwen4b fused-layer lockstep prefix 256: {counts} in {time.time() - t0:.0f} s")
+    assert counts["rounds"] == 2
+
+
 def _moe_full_model(dlm, seed, cap):
     """The 20-layer MoE model: dense weights from synth, expert codes and scales drawn on the
     device from a seeded generator (their values do not change the work; scale codes 119..121
