@@ -630,6 +630,13 @@ static bool wide_ok(const dlm_model* m) {
   return m->d.dtype == DLM_BF16 && m->d.block == 32 && m->d.n_experts == 0 && !m->fused;
 }
 
+// Decode rounds of bf16 models with 8 (kv head, query-head group) groups merge the attention's
+// key splits inside its launch, behind XCD-local barriers whose counters and sync words live
+// in the decode workspace (zeroed once by the caller).
+static bool xcd_combine(const dlm_model* m) {
+  return m->d.dtype == DLM_BF16 && attn_xcd_combine_ok(m->d.hq, m->d.hkv, m->d.block, 1);
+}
+
 static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) {
   const dlm_model_desc& d = m->d;
   const size_t el = d.dtype == DLM_BF16 ? 2 : 4;
@@ -681,6 +688,8 @@ static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) 
     w.pa = (float*)take((size_t)64 * 8 * d.d * 4);
     w.pb = (float*)take((size_t)64 * 8 * d.d * 4);
     w.xn8 = (uint16_t*)take((size_t)8 * 64 * d.d * 2);
+  }
+  if (m->fused || xcd_combine(m)) {
     w.bar = (unsigned*)take(8 * 64 * 4);
     w.err = (int*)take(9 * 128);
   }
@@ -823,7 +832,8 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     const float scale = 1.0f / sqrtf((float)D);
     if (bf) rc = attn_bf16(w.q, kv->k[l], kv->v[l], w.o, d.hq, d.hkv, D, d.block, nqb, kv->cap, scale, kv->len_dev,
                            0, cont, model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st,
-                           AttnKv{kv->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, kv->k_scale, kv->v_scale});
+                           AttnKv{kv->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, kv->k_scale, kv->v_scale},
+                           AttnXSync{w.bar, w.err});
     else rc = attn_f32((const float*)w.q, (const float*)kv->k[l], (const float*)kv->v[l], (float*)w.o, d.hq, d.hkv,
                        D, B, kv->cap, scale, kv->len_dev, 0, cont, st);
     if (rc) return rc;

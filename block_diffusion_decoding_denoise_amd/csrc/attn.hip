@@ -21,8 +21,16 @@
 // splits in index order.  Deterministic throughout.  An FP8 e4m3 cache is widened to bf16 on
 // its way into LDS; the key scale is folded into the softmax scale, the value scale into the
 // output.
+//
+// Decode rounds of models with exactly 8 (kv head, query-head group) groups merge the splits
+// inside the attention launch instead: the 32 splits of group x are workgroups x, x + 8, ..,
+// which the dispatcher places on one XCD, so after storing its split each workgroup meets the
+// other 31 at an XCD-local barrier (xcd.h) and then merges 1/32 of the group's outputs from the
+// XCD's L2, in the same split order and arithmetic as the combine kernel.  That removes one
+// launch from every layer.
 #include "attn.h"
 #include "attn_body.h"
+#include "xcd.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -42,6 +50,33 @@ __global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) v
   const int qblk = blockIdx.x / per_qb, bx = blockIdx.x % per_qb;
   const int s = bx % p.nsplit_max, gh = bx / p.nsplit_max;
   attn_split_body<D, WPG, KV8, false>(p, qblk, gh / HG, gh % HG, s, smem);
+}
+
+// One workgroup per (group x = blockIdx % 8, split s = blockIdx / 8): the group's kWgPerXcd
+// workgroups always launch (splits past the prefix's split count only take part in the
+// merge), so every barrier counts kWgPerXcd arrivals whatever the plan.
+template <int D, int WPG, bool KV8 = false>
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_xcd_kernel(
+    AttnP p, AttnXSync xs) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[attn_smem_bytes<D, WPG>()];
+  const int x = blockIdx.x & (kXcds - 1), s = blockIdx.x / kXcds;
+  const int HG = (p.hq / p.hkv) / WPG;
+  publish_placement(xs.err, x, s);
+  attn_split_body<D, WPG, KV8, false>(p, 0, x / HG, x % HG, s, smem);
+  // the split count, as every workgroup computes it; with one split the output is complete
+  const int N = min((p.len_dev ? *p.len_dev : p.len_host) + p.B, p.cap);
+  const int chunk = split_chunk(N, p.nsplit_max);
+  if ((N + chunk - 1) / chunk <= 1) return;
+  xcd_sync(xs.bar + 64 * x, xs.err);
+  check_placement(xs.err, x);
+  // group x's outputs: query heads WPG x .. WPG x + WPG - 1, D / 4 threads per (head, query)
+  constexpr int TPQ = D / 4;
+  const int items = WPG * p.B * TPQ;
+  for (int it = s * 64 * WPG + (int)threadIdx.x; it < items; it += kWgPerXcd * 64 * WPG) {
+    const int hl = it / (p.B * TPQ), qi = (it / TPQ) % p.B;
+    attn_combine_item<D, true>(p, 0, WPG * x + hl, qi, 4 * (it % TPQ));
+  }
 }
 
 template <int D>
@@ -116,6 +151,16 @@ AttnPlan attn_plan(int hq, int hkv, int D, int B, int max_len) {
   return pl;
 }
 
+static int attn_wpg(int hq, int hkv) {
+  const int G = hq / hkv;
+  return G < 4 ? G : 4;
+}
+
+bool attn_xcd_combine_ok(int hq, int hkv, int B, int nqb) {
+  const int wpg = attn_wpg(hq, hkv);
+  return nqb == 1 && B == 32 && hkv * ((hq / hkv) / wpg) == kXcds;
+}
+
 size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl, int nqb) {
   const int G = hq / hkv;
   const size_t po = (size_t)nqb * hkv * pl.nsplit_max * G * 32 * D * 2;
@@ -125,7 +170,8 @@ size_t attn_ws_bytes(int hq, int hkv, int D, AttnPlan pl, int nqb) {
 
 int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, int hkv, int D,
               int B, int nqb, int cap, float scale, const int32_t* len_dev, int len_host,
-              const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st, AttnKv kvf) {
+              const int32_t* cont_dev, AttnPlan pl, void* ws, int out_packed, hipStream_t st, AttnKv kvf,
+              AttnXSync xs) {
   if (nqb < 1 || nqb > 8 || (nqb > 1 && B != 32))
     return fail(DLM_ERR_SHAPE, "attention: one query block, or up to eight of 32 rows");
   AttnP p;
@@ -150,9 +196,28 @@ int attn_bf16(const void* q, const void* k, const void* v, void* out, int hq, in
   p.len_dev = len_dev;
   p.len_host = len_host;
   p.cont_dev = cont_dev;
-  const int WPG = G < 4 ? G : 4;
+  const int WPG = attn_wpg(hq, hkv);
   if (G % WPG || (WPG != 1 && WPG != 2 && WPG != 4))
     return fail(DLM_ERR_SHAPE, "attention: query heads per kv head must be 1, 2 or a multiple of 4");
+  if (pl.nsplit_max > kMaxSplits) return fail(DLM_ERR_SHAPE, "attention: more key splits than planned for");
+  if (xs.bar && xs.err && attn_xcd_combine_ok(hq, hkv, B, nqb)) {
+    // splits merged in the launch: kXcds groups x kWgPerXcd workgroups (kMaxSplits == kWgPerXcd)
+    static_assert(kMaxSplits == kWgPerXcd, "one workgroup per split slot of a group");
+    auto launch = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(kXcds * kWgPerXcd), dim3(64 * WPG), 0, st, p, xs);
+    };
+#define DLM_ATTN_XCD(DD, KV)                                  \
+  if (WPG == 4) launch(attn_bf16_xcd_kernel<DD, 4, KV>);      \
+  else if (WPG == 2) launch(attn_bf16_xcd_kernel<DD, 2, KV>); \
+  else launch(attn_bf16_xcd_kernel<DD, 1, KV>);
+    if (D == 128) {
+      if (kvf.fp8) { DLM_ATTN_XCD(128, true) } else { DLM_ATTN_XCD(128, false) }
+    } else {
+      if (kvf.fp8) { DLM_ATTN_XCD(64, true) } else { DLM_ATTN_XCD(64, false) }
+    }
+#undef DLM_ATTN_XCD
+    return check_hip(hipGetLastError(), "attn_bf16 launch");
+  }
   const int grid = nqb * hkv * (G / WPG) * pl.nsplit_max;
   auto launch = [&](auto kern, int threads) { hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, p); };
   if (D == 128) {

@@ -38,6 +38,7 @@
 #include <string.h>
 
 #include "epilogue.h"
+#include "xcd.h"
 
 namespace dlm {
 
@@ -81,10 +82,6 @@ void build_xqkv_row_map(int hq, int hkv, int D, int32_t* out) {
 
 namespace {
 
-constexpr int kXcds = 8;
-constexpr int kWgPerXcd = 32;
-constexpr long kSpinLimit = 1L << 22;    // about 0.4 s of polling: then flag and go on
-
 struct LayerP {
   int d, F, hq, hkv, D, mrows;
   FusedDims fd;
@@ -106,69 +103,6 @@ struct LayerP {
   int* err;
   const int32_t* cont_dev;
 };
-
-__device__ __forceinline__ unsigned xcc_id() {
-  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 0xfu;   // HW_REG_XCC_ID[3:0]
-}
-
-// Placement check: the workgroups of group x (blockIdx % 8) must share an XCD.  Which XCD a
-// group gets rotates from launch to launch (the dispatcher continues its round-robin where the
-// previous launch ended), so the check is per launch: workgroup 0 of the group stores its
-// XCC id in word 32 (1 + x) of the sync words (one 128-byte line per group, none shared with
-// the flag word) before the first barrier, and after it every
-// workgroup compares its own id (a group split over two XCDs would not pass the barrier, whose
-// counter lives in one XCD's L2, and would set bit 0 instead); a mismatch sets bit 1 of word 0.
-__device__ __forceinline__ void publish_placement(int* err, int x, int w) {
-  if (threadIdx.x == 0 && w == 0) err[32 * (1 + x)] = (int)xcc_id();
-}
-
-__device__ __forceinline__ void check_placement(int* err, int x) {
-  if (threadIdx.x == 0) {
-    const int pub = (int)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(err, 9 * 128), 128 * (1 + x), 0, 16);
-    if (pub != (int)xcc_id()) __hip_atomic_fetch_or(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// L1-bypassing loads of data written earlier in this kernel by another compute unit of the
-// same XCD (served by the XCD's L2)
-__device__ __forceinline__ u32x4_t ld16_xcd(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16);
-}
-
-// Barrier of the 32 workgroups of one XCD.  The counter only grows: every workgroup adds one
-// per barrier, so at each barrier it starts at a multiple of 32 and the target is the next one.
-// Every wave waits for its own stores to reach L2 before the workgroup arrives; the arrival is
-// an atomic at the XCD's L2 and the wait polls it with L1-bypassing loads.  A wait that gives
-// up sets bit 0 of the error word; once it is set no barrier waits any more, so a broken
-// placement costs one time-out, not one per barrier.
-// issue: loads (prefetches of the next step's weights) that every thread issues after its
-// own stores are complete and before the barrier wait, so that they stream while the
-// workgroups of the XCD meet (vector memory operations complete in issue order, so a
-// prefetch issued before the stores would hold up the arrival).
-struct NoIssue {
-  __device__ __forceinline__ void operator()() const {}
-};
-
-template <typename Issue = NoIssue>
-__device__ __forceinline__ void xcd_sync(unsigned* ctr, int* err, Issue issue = Issue()) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  issue();
-  if (threadIdx.x == 0) {
-    const unsigned v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const unsigned target = (v & ~31u) + 32u;
-    const bool failed = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1;
-    for (long i = 0; !failed; ++i) {
-      const unsigned cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((int)(cur - target) >= 0) break;
-      if (i > kSpinLimit) {
-        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-}
 
 // ------------------------------------------------------------------ residual + RMSNorm
 // A row of the residual: h = base + part[0] + ... + part[7], written to base_out by one XCD

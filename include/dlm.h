@@ -428,7 +428,10 @@ typedef struct {
   float* moe_y;
   int32_t* moe_hits;   /* [n_layers]: running count, per layer, of the distinct experts (shared
                           included) each routed-expert FFN used since the workspace was zeroed */
-  int32_t* sync_err;   /* models on the fused layer path, 288 words: word 0 is 0 unless an
+  int32_t* sync_err;   /* models whose kernels synchronise inside an XCD -- the fused layer
+                          path, and bf16 models with 32-row blocks whose attention has 8 groups
+                          of (kv head, up to 4 of its query heads), which merge the key splits
+                          inside the attention launch -- 288 words: word 0 is 0 unless an
                           XCD-local barrier gave up waiting (bit 0) or a workgroup did not share
                           the XCD of its group, blockIdx % 8 (bit 1) -- then the results are not
                           to be trusted; word 32 (1 + g) holds the XCC id group g ran on in the

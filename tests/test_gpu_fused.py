@@ -50,13 +50,46 @@ def test_fused_path_taken_and_sync_clean():
     dlm = _dlm()
     m, _ = _gpu_model(FUSED_SMALL, 1250, cap=128, fused_layers=True)
     assert m.views.sync_err
-    m0, _ = _gpu_model(FUSED_SMALL, 1250, cap=128)
-    assert not m0.views.sync_err                 # the per-op path has no XCD synchronisation
     prompt = synth.prompt_ids(FUSED_SMALL, 64, 1250)
     toks, states = m.generate(torch.from_numpy(prompt), 2, dlm.CommitRule.fixed_k(6), pipelined=True)
     torch.cuda.synchronize()
     assert _sync_err(m) == 0
     assert [st["round"] for st in states] == [6, 6]
+
+
+def test_per_op_attention_merges_splits_in_launch():
+    """On the per-op path, a model with 8 (kv head, query-head group) groups merges the
+    attention's key splits inside the attention launch, behind XCD-local barriers: its decode
+    workspace has the sync words, and after a prefill and two blocks whose rounds see 2016 and
+    2048 keys (32 splits of one pass: every workgroup has a split) they are clean; a model with
+    2 groups has none."""
+    dlm = _dlm()
+    m, _ = _gpu_model(FUSED_SMALL, 1256, cap=2112)
+    assert m.views.sync_err
+    prompt = synth.prompt_ids(FUSED_SMALL, 1984, 1256)
+    toks, states = m.generate(torch.from_numpy(prompt), 2, dlm.CommitRule.fixed_k(6), pipelined=True)
+    torch.cuda.synchronize()
+    assert _sync_err(m) == 0
+    assert [st["round"] for st in states] == [6, 6]
+    s2 = synth.small_shape(synth.QWEN4B, name="small-bf16", n_layers=1, d=512, hq=8, hkv=2, head_dim=64, ffn=1024,
+                           vocab=3001)
+    m2, _ = _gpu_model(s2, 1256, cap=128)
+    assert not m2.views.sync_err
+
+
+def test_per_op_lockstep_in_launch_split_merge_d64():
+    """The in-launch split merge with 64-wide heads (32 query heads over 8 kv heads), prompt
+    long enough for several splits, against the oracle round by round."""
+    s = synth.small_shape(synth.QWEN4B, name="small-bf16-8kv", n_layers=2, d=512, hq=32, hkv=8, head_dim=64,
+                          ffn=1024, vocab=3001)
+    counts = _lockstep(s, 1257, 416, 1, (1, 0.0, 6, 0, 32))
+    assert counts["rounds"] == 6
+
+
+def test_per_op_lockstep_in_launch_split_merge_fp8():
+    """The same merge over an FP8 e4m3 cache (128-wide heads)."""
+    counts = _lockstep(FUSED_SMALL, 1258, 416, 1, (1, 0.0, 6, 0, 32), kv_scales=(0.07, 0.11))
+    assert counts["rounds"] == 6
 
 
 def test_fused_lockstep_fixed_k():
