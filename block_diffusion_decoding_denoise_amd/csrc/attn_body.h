@@ -36,7 +36,9 @@ struct AttnP {
 
 // Keys per split for N keys over at most nsplit_max splits: the smallest multiple of one
 // pass (PT tiles of 32 keys) that needs no more splits, so short prefixes use few splits and
-// long ones spread over all of them.
+// long ones spread over all of them.  The split count is then ceil(N / chunk); the passes are
+// dealt to the splits in turn (pass j to split j % nsplit), so a split holds chunk keys or
+// fewer, interleaved, and its first pass does not depend on N.
 constexpr int PT = 2;           // tiles per pass
 __device__ inline int split_chunk(int N, int nsplit_max) {
   const int unit = PT * TK;
@@ -105,19 +107,11 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
                                                            0, COH ? 16 : 0);
     }
   }
-  const int L = (p.len_dev ? *p.len_dev : p.len_host) + 32 * qblk;
-  const int N = min(L + p.B, p.cap);
-  const int chunk = split_chunk(N, p.nsplit_max);
-  const int nsplit = (N + chunk - 1) / chunk;
-  if (s >= nsplit) return;
-  DLM_TRACE_POINT(1);
-  const int c0 = s * chunk, c1 = min(N, c0 + chunk);
-  const int npass = (c1 - c0 + PT * TK - 1) / (PT * TK);
-  // buffer descriptors: K rows past c1 read as zeros; V^T tiles stay inside this head's
-  // [cap/32][D][32] block (a tile wholly past c1 is not loaded; keys past c1 inside a tile are
-  // masked after the LDS read)
+  // buffer descriptors over this head's whole cache (K [cap][D], V^T [cap/32][D][32]); keys
+  // past the N visible ones are masked after the LDS read, and tiles wholly past N are not
+  // loaded once N is known (kend)
   constexpr int ES = KV8 ? 1 : 2;                          // cache bytes per element
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint8_t*)p.k + (size_t)g * p.cap * D * ES, (uint32_t)c1 * D * ES);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint8_t*)p.k + (size_t)g * p.cap * D * ES, (uint32_t)p.cap * D * ES);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint8_t*)p.v + (size_t)g * D * p.cap * ES, (uint32_t)D * p.cap * ES);
   const int lg = lane >> 4;                                // lane group: keys 8lg .. 8lg+7
 
@@ -134,11 +128,12 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
     if constexpr (KV8) return e4m3x8_to_bf16(x);
     else return x;
   };
+  int kend = p.cap;
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int tu = t0 + u * TK;
-      const bool in = tu < c1;
+      const bool in = tu < kend;
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         const int c = tid + NT * j, key = c / (D / 8), col = c % (D / 8);
@@ -168,7 +163,19 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
       }
     }
   };
-  fetch(c0);
+  // Pass j (keys [PT TK j, PT TK (j + 1))) of the prefix and block belongs to split j % nsplit,
+  // so this split's first pass is pass s whatever the prefix length: it is requested before
+  // the length is read.
+  fetch(s * PT * TK);
+  const int L = (p.len_dev ? *p.len_dev : p.len_host) + 32 * qblk;
+  const int N = min(L + p.B, p.cap);
+  const int chunk = split_chunk(N, p.nsplit_max);
+  const int nsplit = (N + chunk - 1) / chunk;
+  if (s >= nsplit) return;
+  DLM_TRACE_POINT(1);
+  kend = N;
+  const int P = (N + PT * TK - 1) / (PT * TK);
+  const int npass = (P - s + nsplit - 1) / nsplit;        // passes s, s + nsplit, ...
 
   f32x4_t o[DB][2];
 #pragma unroll
@@ -176,10 +183,10 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
 
   stash(0);
-  if (npass > 1) fetch(c0 + PT * TK);
+  if (npass > 1) fetch((s + nsplit) * PT * TK);
   __syncthreads();
   for (int ip = 0; ip < npass; ++ip) {
-    const int p0 = c0 + ip * PT * TK;
+    const int p0 = (s + ip * nsplit) * PT * TK;
     // scores of every tile of the pass.  K rows for score block kb: MFMA row i (= lane % 16)
     // takes key 8(i/4) + 4kb + i%4, so the result rows 4(l/16) + r of block kb are keys
     // 8(l/16) + 4kb + r; lane l ends up holding query 16qb + l%16.
@@ -218,7 +225,7 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
           for (int r = 0; r < 4; ++r) {
             const int key = p0 + u * TK + 8 * lg + 4 * kb + r;
             float v = sc[u][kb][qb][r] * p.scale_log2;
-            v = key < c1 ? v : -INFINITY;
+            v = key < N ? v : -INFINITY;
             sc[u][kb][qb][r] = v;
             mx = fmaxf(mx, v);
           }
@@ -253,12 +260,12 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
         for (int r = 0; r < 4; ++r) o[b][qb][r] *= alpha;
     }
     // O^T[b][qb] += V^T[16b.., keys] P^T[keys, q]; V^T fragments (A operand): lane l: column
-    // dv = 16b + l%16, keys 8lg .. +8 (keys past c1 zeroed: stale cache contents could be
+    // dv = 16b + l%16, keys 8lg .. +8 (keys past N zeroed: stale cache contents could be
     // non-finite)
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const uint8_t* sv = smem(ip & 1, u) + KBYTES;
-      const int nvalid = min(8, max(0, c1 - (p0 + u * TK + 8 * lg)));
+      const int nvalid = min(8, max(0, N - (p0 + u * TK + 8 * lg)));
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
         u32x4_t vc = *(const u32x4_t*)(sv + (16 * b + (lane & 15)) * VROW + 16 * lg);
@@ -274,7 +281,7 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
     // every wave has finished), then the pass after it is requested
     if (ip + 1 < npass) {
       stash((ip + 1) & 1);
-      if (ip + 2 < npass) fetch(p0 + 2 * PT * TK);
+      if (ip + 2 < npass) fetch(p0 + 2 * nsplit * PT * TK);
     }
     __syncthreads();
   }

@@ -54,10 +54,13 @@ def assert_attention_close(got, ref, what=""):
 
 
 def split_bounds(n_keys: int, nsplit_max: int = 32, unit: int = 64):
-    """Key splits of the long-prefix plan: the fewest whole 64-key passes per split that
-    cover the keys within nsplit_max splits."""
+    """Key splits of the long-prefix plan, as lists of the (start, end) of their passes: the
+    fewest whole 64-key passes per split that cover the keys within nsplit_max splits, the
+    passes dealt to the splits in turn (pass j to split j % nsplit)."""
     chunk = -(-n_keys // (nsplit_max * unit)) * unit
-    return [(c, min(n_keys, c + chunk)) for c in range(0, n_keys, chunk)]
+    nsplit = -(-n_keys // chunk)
+    passes = [(c, min(n_keys, c + unit)) for c in range(0, n_keys, unit)]
+    return [passes[s::nsplit] for s in range(nsplit)]
 
 
 def kernel_attention_model(q, k, v, scale, drop=None, pass_keys=64):
@@ -75,14 +78,14 @@ def kernel_attention_model(q, k, v, scale, drop=None, pass_keys=64):
         g = h // G
         s_all = (q[:, h, :] @ k[g].T) * scale
         parts = []
-        for si, (c0, c1) in enumerate(split_bounds(N)):
+        for si, split in enumerate(split_bounds(N, unit=pass_keys)):
             if si == drop:
                 continue
             m = np.full(B, -np.inf)
             l = np.zeros(B)
             acc = np.zeros((B, D))
-            for p0 in range(c0, c1, pass_keys):
-                s = s_all[:, p0:min(c1, p0 + pass_keys)]
+            for p0, p1 in split:
+                s = s_all[:, p0:p1]
                 m_new = np.maximum(m, s.max(axis=1))
                 alpha = np.exp(m - m_new)
                 e = np.exp(s - m_new[:, None])

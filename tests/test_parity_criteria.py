@@ -64,3 +64,17 @@ def test_criterion_rejects_a_wrong_kv_head():
     ref = oracle.attention(q, k, v, 1.0 / math.sqrt(D))
     wrong = oracle.attention(q, k, v[::-1].copy(), 1.0 / math.sqrt(D))
     assert not attention_ok(wrong, ref)
+
+
+@pytest.mark.parametrize("n", [1, 64, 65, 2047, 2048, 2049, 2336, 4128, 32800])
+def test_split_plan_partitions_the_keys(n):
+    """The kernel's split plan as the error model takes it: the passes of all splits cover
+    [0, n) once, in 64-key passes, within 32 splits; split s starts with pass s (keys
+    [64 s, 64 s + 64)) and takes every nsplit-th pass after it."""
+    splits = split_bounds(n)
+    assert 1 <= len(splits) <= 32
+    cover = sorted(p for sp in splits for p in sp)
+    assert cover == [(c, min(n, c + 64)) for c in range(0, n, 64)]
+    for s, sp in enumerate(splits):
+        assert sp[0][0] == 64 * s
+        assert all(b[0] - a[0] == 64 * len(splits) for a, b in zip(sp, sp[1:]))
