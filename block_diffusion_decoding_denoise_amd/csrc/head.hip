@@ -13,9 +13,12 @@
 // ahead) and forms partial logits with v_mfma_f32_16x16x32_bf16 (A = E rows, B = h rows);
 // (2) the NW partials are summed through LDS in a fixed order and 256 threads update the
 // online statistics per row (running max, sum of e^(l-m), sum of e^(l-m)(l-m) for the
-// entropy, argmax with lowest-id ties) and publish p = e^(l - m_new) in bf16 and the
-// rescale factor; (3) each wave adds P (16 rows x 16 vocab) times its E slice, read back
-// transposed from a wave-private LDS copy, with v_mfma_f32_16x16x16bf16_1k.  E is read
+// entropy, argmax with lowest-id ties; 16-lane reductions by DPP row moves) and publish
+// p = e^(l - m_new) in bf16 and the rescale factor; (3) each wave adds P (16 rows x 16
+// vocab) times its E slice with v_mfma_f32_16x16x16bf16_1k.  The slice is kept in a
+// wave-private LDS copy in its natural [vocab][d] layout (one 16-byte write per k-step) and
+// read back transposed, vocabulary-major, by the transpose read ds_read_b64_tr_b16; the
+// accumulators are rescaled only when a row's running max moved.  E is read
 // from HBM once per row group; the groups of one chunk run on one XCD, so the second
 // group mostly hits L2.  Partial statistics and partial pe per chunk go to the workspace
 // and a combine kernel merges the chunks in index order (deterministic).
@@ -71,6 +74,59 @@ __device__ inline int n_chunks_for(int n_groups, int chunks_fixed) {
 // statistics layout per (chunk, open row): m, s, T, best value, best index (as float bits)
 enum { ST_M = 0, ST_S = 1, ST_T = 2, ST_BV = 3, ST_BI = 4 };
 
+// Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15) by DPP moves: swap
+// neighbours, swap pairs, mirror each half-row, mirror the row.  After the two quad swaps
+// the 4 lanes of a quad hold the same value, so each mirror combines two equal-valued groups
+// and every lane of the row ends with the same, order-independent-of-lane result.
+enum : int { DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f<DPP_MIRROR>(v));
+}
+// two sums at once (independent chains)
+__device__ __forceinline__ void row16_sum2(float& a, float& b) {
+  a += dpp_f<DPP_XOR1>(a);
+  b += dpp_f<DPP_XOR1>(b);
+  a += dpp_f<DPP_XOR2>(a);
+  b += dpp_f<DPP_XOR2>(b);
+  a += dpp_f<DPP_HALF_MIRROR>(a);
+  b += dpp_f<DPP_HALF_MIRROR>(b);
+  a += dpp_f<DPP_MIRROR>(a);
+  b += dpp_f<DPP_MIRROR>(b);
+}
+// (value, index) with the larger value, lowest index among equal values
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i);
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+__device__ __forceinline__ void row16_argmax(float& v, int& i) {
+  argmax_step<DPP_XOR1>(v, i);
+  argmax_step<DPP_XOR2>(v, i);
+  argmax_step<DPP_HALF_MIRROR>(v, i);
+  argmax_step<DPP_MIRROR>(v, i);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+// Transpose read (gfx950): within each 16-lane group, lane i receives element i % 4 of the
+// 8-byte loads of lanes 4 j + i / 4 (j = 0..3) of its group.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
 // Loads are branch-free (rows, vocabulary entries and d-steps out of range use out-of-range
 // buffer offsets, which read zeros), so the next tile's loads stay in flight while a tile is
 // processed.  DBG: also store every logit (tests).
@@ -81,7 +137,11 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
   __shared__ float lpart[NW][16][17];            // [wave][v][row]
   __shared__ __attribute__((aligned(16))) uint16_t Pt[16][16];   // [row][v] bf16
   __shared__ float alpha_s[16];
-  __shared__ __attribute__((aligned(16))) uint16_t Et[NW][MAXK * 32][16];  // wave-private E^T
+  // wave-private copy of the wave's E slice, [vocab][d] with rows padded by 16 bytes (the 16
+  // rows of a transpose read then cover the 64 banks twice, the rows of a write once per lane
+  // group)
+  constexpr int EROW = MAXK * 32 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t En[NW][16][EROW];
   const int n_open = compact_open(p.committed, p.rows, s_idx);
   if (n_open == 0) return;
   const int n_groups = (n_open + 15) / 16;
@@ -131,26 +191,20 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
 #pragma unroll
     for (int u = 0; u < MAXK; ++u) ef[u] = bload16(er, (ok && u < nk) ? base + (uint32_t)u * 64u : 0x80000000u);
   };
-  u32x4_t ef[MAXK], en[MAXK];
-  load_tile(t0, ef);
-  for (int t = t0; t < t1; ++t) {
-    load_tile(t + 1, en);     // past t1: zeros, no traffic
+  // Two register buffers: the next tile is requested before this one is processed.  The loop
+  // runs the tiles in pairs so that each buffer stays in fixed registers.  (Requesting two
+  // tiles ahead measured no faster: a compute unit's loads are then held at issue, its
+  // memory pipeline being full.)
+  auto tile_step = [&](int t, u32x4_t* ef) {
     // (1) partial logits over this wave's d-slice: L^T[v][row] (d-steps past nk are zeros)
     f32x4_t lp = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < MAXK; ++u) lp = mfma16x16x32(ef[u], hf[u], lp);
 #pragma unroll
     for (int r = 0; r < 4; ++r) lpart[w][4 * (lane >> 4) + r][lane & 15] = lp[r];
-    // keep this wave's E slice, transposed, for the p.E product
+    // keep this wave's E slice (natural layout) for the p.E product
 #pragma unroll
-    for (int u = 0; u < MAXK; ++u) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dl = u * 32 + 8 * (lane >> 4) + 2 * i;
-        Et[w][dl][lane & 15] = (uint16_t)(ef[u][i] & 0xffffu);
-        Et[w][dl + 1][lane & 15] = (uint16_t)(ef[u][i] >> 16);
-      }
-    }
+    for (int u = 0; u < MAXK; ++u) *(u32x4_t*)&En[w][lane & 15][u * 32 + 8 * (lane >> 4)] = ef[u];
     __syncthreads();
     // (2) reduce partials, update the statistics of row my_row (threads 0..255)
     if (tid < 256) {
@@ -162,25 +216,17 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
       if (!valid) l = -INFINITY;
       const int k = 16 * grp + my_row;
       if (DBG && valid && k < n_open) p.logits_dbg[(size_t)s_idx[k] * p.V + vg] = l;
-      float tm = l;
-      for (int o = 1; o < 16; o <<= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
+      const float tm = row16_max(l);
       // tile argmax (lowest id among equal values)
       float cv = l;
       int ci = valid ? vg : 0x7fffffff;
-      for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(cv, o, 64);
-        const int oi = __shfl_xor(ci, o, 64);
-        if (ov > cv || (ov == cv && oi < ci)) { cv = ov; ci = oi; }
-      }
+      row16_argmax(cv, ci);
       if (cv > bv || (cv == bv && ci < bi)) { bv = cv; bi = ci; }
       const float mn = fmaxf(rm, tm);
       const float al = rs > 0.f ? expf(rm - mn) : 0.f;
       const float e = valid ? expf(l - mn) : 0.f;
       float se = e, te = valid ? e * (l - mn) : 0.f;
-      for (int o = 1; o < 16; o <<= 1) {
-        se += __shfl_xor(se, o, 64);
-        te += __shfl_xor(te, o, 64);
-      }
+      row16_sum2(se, te);
       rT = rs > 0.f ? al * (rT + (rm - mn) * rs) + te : te;
       rs = al * rs + se;
       rm = mn;
@@ -188,27 +234,43 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
       if (my_v == 0) alpha_s[my_row] = al;
     }
     __syncthreads();
-    // (3) acc[rows][d-slice] = alpha * acc + P E_slice
+    // (3) acc[rows][d-slice] = alpha * acc + P E_slice.  B operand of d-block (u, hb): lane
+    // l takes E[vocab 4(l/16) + j][d 32u + 16hb + l%16], j = 0..3, by a transpose read whose
+    // lanes address vocabulary row 4(l/16) + (l%16)/4 at d 32u + 16hb + 4(l%4).
     {
       const u32x2_t pa = *(const u32x2_t*)&Pt[lane & 15][4 * (lane >> 4)];
       float al4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) al4[r] = alpha_s[4 * (lane >> 4) + r];
+      // rescale only when some row's running max moved (alpha 1 leaves acc unchanged)
+      const bool moved = __builtin_amdgcn_ballot_w64(al4[0] != 1.f || al4[1] != 1.f || al4[2] != 1.f ||
+                                                     al4[3] != 1.f) != 0;
+      const uint16_t* eb0 = &En[w][4 * (lane >> 4) + ((lane & 15) >> 2)][4 * (lane & 3)];
 #pragma unroll
       for (int u = 0; u < MAXK; ++u) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-          const u32x2_t eb = *(const u32x2_t*)&Et[w][u * 32 + 16 * hb + (lane & 15)][4 * (lane >> 4)];
+          const u32x2_t eb = lds_read_tr16(eb0 + u * 32 + 16 * hb);
           f32x4_t a = acc[u][hb];
+          if (moved) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) a[r] *= al4[r];
+            for (int r = 0; r < 4; ++r) a[r] *= al4[r];
+          }
           acc[u][hb] = mfma16x16x16(pa, eb, a);
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < MAXK; ++u) ef[u] = en[u];
+  };
+  u32x4_t b0[MAXK], b1[MAXK];
+  load_tile(t0, b0);
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    load_tile(t + 1, b1);           // past t1: zeros, no traffic
+    tile_step(t, b0);
+    load_tile(t + 2, b0);
+    tile_step(t + 1, b1);
   }
+  if (t < t1) tile_step(t, b0);     // uniform over the workgroup
   // partial outputs for rows k = 16grp + r
   if (tid < 256 && my_v == 0) {
     const int k = 16 * grp + my_row;
