@@ -265,9 +265,14 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
   load_tile(t0, b0);
   int t = t0;
   for (; t + 1 < t1; t += 2) {
+    // the scheduling barriers keep each request ahead of the matrix ops that wait for the
+    // current tile (left alone, the scheduler sinks the loads below them to shorten register
+    // lifetimes, and the next tile is then requested only once this one has arrived)
     load_tile(t + 1, b1);           // past t1: zeros, no traffic
+    __builtin_amdgcn_sched_barrier(0);
     tile_step(t, b0);
     load_tile(t + 2, b0);
+    __builtin_amdgcn_sched_barrier(0);
     tile_step(t + 1, b1);
   }
   if (t < t1) tile_step(t, b0);     // uniform over the workgroup
