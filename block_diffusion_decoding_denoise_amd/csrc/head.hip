@@ -18,7 +18,9 @@
 // vocab) times its E slice with v_mfma_f32_16x16x16bf16_1k.  The slice is kept in a
 // wave-private LDS copy in its natural [vocab][d] layout (one 16-byte write per k-step) and
 // read back transposed, vocabulary-major, by the transpose read ds_read_b64_tr_b16; the
-// accumulators are rescaled only when a row's running max moved.  E is read
+// accumulators are rescaled only when a row's running max moved.  The three steps are
+// software-pipelined over tiles: (1) of tile t + 1 and (2) of tile t run between the same two
+// barriers, (3) of tile t after them, so a tile costs one barrier.  E is read
 // from HBM once per row group; the groups of one chunk run on one XCD, so the second
 // group mostly hits L2.  Partial statistics and partial pe per chunk go to the workspace
 // and a combine kernel merges the chunks in index order (deterministic).
@@ -134,9 +136,13 @@ template <int MAXK, int NW, bool DBG>
 __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
   __shared__ int s_idx[DLM_MAX_ROWS];
-  __shared__ float lpart[NW][16][17];            // [wave][v][row]
-  __shared__ __attribute__((aligned(16))) uint16_t Pt[16][16];   // [row][v] bf16
-  __shared__ float alpha_s[16];
+  // double-buffered by tile parity: a tile's statistics are taken while the next tile's
+  // partial logits are written (the 16-wave form has LDS for one buffer and takes its
+  // statistics before the next partial logits, behind one more barrier)
+  constexpr int NLP = NW == 8 ? 2 : 1;
+  __shared__ float lpart[NLP][NW][16][17];       // [parity][wave][v][row]
+  __shared__ __attribute__((aligned(16))) uint16_t Pt[2][16][16];   // [parity][row][v] bf16
+  __shared__ float alpha_s[2][16];
   // wave-private copy of the wave's E slice, [vocab][d] with rows padded by 16 bytes (the 16
   // rows of a transpose read then cover the 64 banks twice, the rows of a write once per lane
   // group)
@@ -191,91 +197,111 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
 #pragma unroll
     for (int u = 0; u < MAXK; ++u) ef[u] = bload16(er, (ok && u < nk) ? base + (uint32_t)u * 64u : 0x80000000u);
   };
-  // Two register buffers: the next tile is requested before this one is processed.  The loop
-  // runs the tiles in pairs so that each buffer stays in fixed registers.  (Requesting two
-  // tiles ahead measured no faster: a compute unit's loads are then held at issue, its
-  // memory pipeline being full.)
-  auto tile_step = [&](int t, u32x4_t* ef) {
-    // (1) partial logits over this wave's d-slice: L^T[v][row] (d-steps past nk are zeros)
+  // Software-pipelined over tiles, one barrier per tile.  Between barriers: tile t + 1's
+  // partial logits (all waves) and tile t's statistics (threads 0..255, from the partials
+  // written before the previous barrier); after the barrier: tile t's P . E (from the LDS copy)
+  // and the LDS copy of tile t + 1.  Two register buffers alternate: a buffer's tile is
+  // requested two tiles before its partial logits, right after the buffer was copied to LDS.
+  // Past t1 the loads read zeros and the extra partial logits and copy are never used.
+  auto logits = [&](const u32x4_t* ef, int par) {
+    // partial logits over this wave's d-slice: L^T[v][row] (d-steps past nk are zeros)
     f32x4_t lp = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < MAXK; ++u) lp = mfma16x16x32(ef[u], hf[u], lp);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lpart[w][4 * (lane >> 4) + r][lane & 15] = lp[r];
-    // keep this wave's E slice (natural layout) for the p.E product
+    for (int r = 0; r < 4; ++r) lpart[par % NLP][w][4 * (lane >> 4) + r][lane & 15] = lp[r];
+  };
+  auto stash = [&](const u32x4_t* ef) {
 #pragma unroll
     for (int u = 0; u < MAXK; ++u) *(u32x4_t*)&En[w][lane & 15][u * 32 + 8 * (lane >> 4)] = ef[u];
-    __syncthreads();
-    // (2) reduce partials, update the statistics of row my_row (threads 0..255)
-    if (tid < 256) {
-      float l = 0.f;
+  };
+  // reduce tile t's partials and update the statistics of row my_row (threads 0..255)
+  auto stats = [&](int t, int par) {
+    if (tid >= 256) return;
+    float l = 0.f;
 #pragma unroll
-      for (int q = 0; q < NW; ++q) l += lpart[q][my_v][my_row];
-      const int vg = t * 16 + my_v;
-      const bool valid = vg < p.V;
-      if (!valid) l = -INFINITY;
-      const int k = 16 * grp + my_row;
-      if (DBG && valid && k < n_open) p.logits_dbg[(size_t)s_idx[k] * p.V + vg] = l;
-      const float tm = row16_max(l);
-      // tile argmax (lowest id among equal values)
-      float cv = l;
-      int ci = valid ? vg : 0x7fffffff;
-      row16_argmax(cv, ci);
-      if (cv > bv || (cv == bv && ci < bi)) { bv = cv; bi = ci; }
-      const float mn = fmaxf(rm, tm);
-      const float al = rs > 0.f ? expf(rm - mn) : 0.f;
-      const float e = valid ? expf(l - mn) : 0.f;
-      float se = e, te = valid ? e * (l - mn) : 0.f;
-      row16_sum2(se, te);
-      rT = rs > 0.f ? al * (rT + (rm - mn) * rs) + te : te;
-      rs = al * rs + se;
-      rm = mn;
-      Pt[my_row][my_v] = f2bf(e);
-      if (my_v == 0) alpha_s[my_row] = al;
-    }
-    __syncthreads();
-    // (3) acc[rows][d-slice] = alpha * acc + P E_slice.  B operand of d-block (u, hb): lane
-    // l takes E[vocab 4(l/16) + j][d 32u + 16hb + l%16], j = 0..3, by a transpose read whose
-    // lanes address vocabulary row 4(l/16) + (l%16)/4 at d 32u + 16hb + 4(l%4).
-    {
-      const u32x2_t pa = *(const u32x2_t*)&Pt[lane & 15][4 * (lane >> 4)];
-      float al4[4];
+    for (int q = 0; q < NW; ++q) l += lpart[par % NLP][q][my_v][my_row];
+    const int vg = t * 16 + my_v;
+    const bool valid = vg < p.V;
+    if (!valid) l = -INFINITY;
+    const int k = 16 * grp + my_row;
+    if (DBG && valid && k < n_open) p.logits_dbg[(size_t)s_idx[k] * p.V + vg] = l;
+    const float tm = row16_max(l);
+    // tile argmax (lowest id among equal values)
+    float cv = l;
+    int ci = valid ? vg : 0x7fffffff;
+    row16_argmax(cv, ci);
+    if (cv > bv || (cv == bv && ci < bi)) { bv = cv; bi = ci; }
+    const float mn = fmaxf(rm, tm);
+    const float al = rs > 0.f ? expf(rm - mn) : 0.f;
+    const float e = valid ? expf(l - mn) : 0.f;
+    float se = e, te = valid ? e * (l - mn) : 0.f;
+    row16_sum2(se, te);
+    rT = rs > 0.f ? al * (rT + (rm - mn) * rs) + te : te;
+    rs = al * rs + se;
+    rm = mn;
+    Pt[par][my_row][my_v] = f2bf(e);
+    if (my_v == 0) alpha_s[par][my_row] = al;
+  };
+  // acc[rows][d-slice] = alpha * acc + P E_slice.  B operand of d-block (u, hb): lane l takes
+  // E[vocab 4(l/16) + j][d 32u + 16hb + l%16], j = 0..3, by a transpose read whose lanes address
+  // vocabulary row 4(l/16) + (l%16)/4 at d 32u + 16hb + 4(l%4).
+  auto pe_step = [&](int par) {
+    const u32x2_t pa = *(const u32x2_t*)&Pt[par][lane & 15][4 * (lane >> 4)];
+    float al4[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) al4[r] = alpha_s[4 * (lane >> 4) + r];
-      // rescale only when some row's running max moved (alpha 1 leaves acc unchanged)
-      const bool moved = __builtin_amdgcn_ballot_w64(al4[0] != 1.f || al4[1] != 1.f || al4[2] != 1.f ||
-                                                     al4[3] != 1.f) != 0;
-      const uint16_t* eb0 = &En[w][4 * (lane >> 4) + ((lane & 15) >> 2)][4 * (lane & 3)];
+    for (int r = 0; r < 4; ++r) al4[r] = alpha_s[par][4 * (lane >> 4) + r];
+    // rescale only when some row's running max moved (alpha 1 leaves acc unchanged)
+    const bool moved = __builtin_amdgcn_ballot_w64(al4[0] != 1.f || al4[1] != 1.f || al4[2] != 1.f ||
+                                                   al4[3] != 1.f) != 0;
+    const uint16_t* eb0 = &En[w][4 * (lane >> 4) + ((lane & 15) >> 2)][4 * (lane & 3)];
 #pragma unroll
-      for (int u = 0; u < MAXK; ++u) {
+    for (int u = 0; u < MAXK; ++u) {
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const u32x2_t eb = lds_read_tr16(eb0 + u * 32 + 16 * hb);
-          f32x4_t a = acc[u][hb];
-          if (moved) {
+      for (int hb = 0; hb < 2; ++hb) {
+        const u32x2_t eb = lds_read_tr16(eb0 + u * 32 + 16 * hb);
+        f32x4_t a = acc[u][hb];
+        if (moved) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] *= al4[r];
-          }
-          acc[u][hb] = mfma16x16x16(pa, eb, a);
+          for (int r = 0; r < 4; ++r) a[r] *= al4[r];
         }
+        acc[u][hb] = mfma16x16x16(pa, eb, a);
       }
     }
   };
+  // one tile: bn holds tile t + 1, bf tile t + 2 (in flight)
+  auto iter = [&](int t, int par, u32x4_t* bn) {
+    if constexpr (NLP == 2) {
+      logits(bn, par ^ 1);
+      stats(t, par);
+    } else {
+      stats(t, par);
+      __syncthreads();
+      logits(bn, par ^ 1);
+    }
+    __syncthreads();
+    pe_step(par);
+    stash(bn);
+    load_tile(t + 3, bn);            // past t1: zeros, no traffic
+    // keep the requests here (left alone, the scheduler sinks loads below the matrix ops that
+    // wait for the tile before, and a tile is then requested only once that one has arrived)
+    __builtin_amdgcn_sched_barrier(0);
+  };
   u32x4_t b0[MAXK], b1[MAXK];
   load_tile(t0, b0);
+  load_tile(t0 + 1, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  logits(b0, 0);
+  stash(b0);
+  load_tile(t0 + 2, b0);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
   int t = t0;
   for (; t + 1 < t1; t += 2) {
-    // the scheduling barriers keep each request ahead of the matrix ops that wait for the
-    // current tile (left alone, the scheduler sinks the loads below them to shorten register
-    // lifetimes, and the next tile is then requested only once this one has arrived)
-    load_tile(t + 1, b1);           // past t1: zeros, no traffic
-    __builtin_amdgcn_sched_barrier(0);
-    tile_step(t, b0);
-    load_tile(t + 2, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_step(t + 1, b1);
+    iter(t, 0, b1);
+    iter(t + 1, 1, b0);
   }
-  if (t < t1) tile_step(t, b0);     // uniform over the workgroup
+  if (t < t1) iter(t, 0, b1);      // uniform over the workgroup
   // partial outputs for rows k = 16grp + r
   if (tid < 256 && my_v == 0) {
     const int k = 16 * grp + my_row;
