@@ -326,6 +326,8 @@ def main():
                     help="decode with the fused layer kernels (one launch per sublayer)")
     ap.add_argument("--no-full", action="store_true", help="skip the in-order 128-block generation leg")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny fp32 model leg")
+    ap.add_argument("--no-threshold", action="store_true",
+                    help="skip the threshold-block leg (whose later rounds' kernels only read the continue flag)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -568,17 +570,20 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
-    thr_rule = dlm.CommitRule.threshold(0.0, True, 32)
-    one_round = dlm.CommitRule.fixed_k(32)
-    threshold = {
-        "workload": "threshold rule tau=0 with forced top-1 and max_rounds=32 (the block is done in round 0), "
-                    "prompt 256, one block, separate commit pass",
-        "ms_block_graph": round(time_threshold(lambda: model.decode_block(thr_rule)), 3),
-        "ms_gated_seg1": round(time_threshold(lambda: model.decode_block_gated(thr_rule, seg_rounds=1)), 3),
-        "ms_gated_seg4": round(time_threshold(lambda: model.decode_block_gated(thr_rule, seg_rounds=4)), 3),
-        "ms_one_round_floor": round(time_threshold(lambda: model.decode_block(one_round)), 3)}
-    log(f"threshold block done in round 0 of 32: {threshold['ms_block_graph']:.2f} ms (all rounds enqueued), "
-        f"{threshold['ms_gated_seg1']:.2f} ms gated (segments of 1), one round alone {threshold['ms_one_round_floor']:.2f} ms")
+    threshold = None
+    if not args.no_threshold:
+        thr_rule = dlm.CommitRule.threshold(0.0, True, 32)
+        one_round = dlm.CommitRule.fixed_k(32)
+        threshold = {
+            "workload": "threshold rule tau=0 with forced top-1 and max_rounds=32 (the block is done in round 0), "
+                        "prompt 256, one block, separate commit pass",
+            "ms_block_graph": round(time_threshold(lambda: model.decode_block(thr_rule)), 3),
+            "ms_gated_seg1": round(time_threshold(lambda: model.decode_block_gated(thr_rule, seg_rounds=1)), 3),
+            "ms_gated_seg4": round(time_threshold(lambda: model.decode_block_gated(thr_rule, seg_rounds=4)), 3),
+            "ms_one_round_floor": round(time_threshold(lambda: model.decode_block(one_round)), 3)}
+        log(f"threshold block done in round 0 of 32: {threshold['ms_block_graph']:.2f} ms (all rounds enqueued), "
+            f"{threshold['ms_gated_seg1']:.2f} ms gated (segments of 1), one round alone "
+            f"{threshold['ms_one_round_floor']:.2f} ms")
 
     # ---- the head and attention ops alone (uses the model's embedding)
     ops = run_ops(torch, dlm, dev_w["emb"], args.seed) if not args.no_ops else None
