@@ -472,11 +472,24 @@ class Model:
         _check(lib().dlm_commit_pass(self.handle, ctypes.byref(self.kv), _ptr(tokens), _ptr(self.ws), self.ws.numel(),
                                      _stream()), "dlm_commit_pass")
 
+    def check_sync(self):
+        """Raise DlmError if a kernel that synchronises inside an XCD (the fused layer path,
+        or the attention's in-launch split merge) reported a barrier wait that gave up or a
+        workgroup off its group's XCD since the workspace was zeroed; the results are then not
+        to be trusted.  No-op for models without such kernels.  Reads one word."""
+        if not self.views.sync_err:
+            return
+        flags = int(self.view("sync_err", (1,), torch.int32).item())
+        if flags:
+            raise DlmError(f"XCD synchronisation failed (sync flags {flags}: 1 a barrier wait gave up, "
+                           f"2 a workgroup ran off its group's XCD)")
+
     def generate(self, prompt_ids, n_blocks, rule: CommitRule, pipelined=False):
         """Prefill, then decode n_blocks blocks (one token readback per block).
         Returns (token ids [n_blocks * B], list of per-block round states).  pipelined: each
         block's commit pass rides along with the next block's round 0 (the last one runs on
-        its own), with the same result."""
+        its own), with the same result.  Raises DlmError if an XCD-local synchronisation
+        failed (check_sync)."""
         self.set_len(0)
         self.prefill(prompt_ids)
         out, states = [], []
@@ -485,6 +498,7 @@ class Model:
                 self.decode_block(rule)
                 out.append(self.tokens.cpu())
                 states.append(state_dict(self.state))
+            self.check_sync()
             return torch.cat(out), states
         bufs = [torch.zeros_like(self.tokens), torch.zeros_like(self.tokens)]
         prev = None
@@ -496,6 +510,7 @@ class Model:
             prev = cur
         if prev is not None:
             self.commit_pass(prev)
+        self.check_sync()
         return torch.cat(out), states
 
 

@@ -77,6 +77,24 @@ def test_per_op_attention_merges_splits_in_launch():
     assert not m2.views.sync_err
 
 
+def test_generate_checks_the_sync_word():
+    """generate() reads the sync word after its blocks: clean after a real run, and a flagged
+    word (set from the host, as a failed barrier would leave it) makes it raise."""
+    dlm = _dlm()
+    m, _ = _gpu_model(FUSED_SMALL, 1259, cap=128)
+    prompt = torch.from_numpy(synth.prompt_ids(FUSED_SMALL, 64, 1259))
+    m.generate(prompt, 1, dlm.CommitRule.fixed_k(11))
+    m.check_sync()
+    word = m.view("sync_err", (1,), torch.int32)
+    word.fill_(1)
+    torch.cuda.synchronize()
+    with pytest.raises(dlm.DlmError, match="XCD synchronisation failed"):
+        m.check_sync()
+    word.zero_()
+    torch.cuda.synchronize()
+    m.check_sync()
+
+
 def test_per_op_lockstep_in_launch_split_merge_d64():
     """The in-launch split merge with 64-wide heads (32 query heads over 8 kv heads), prompt
     long enough for several splits, against the oracle round by round."""
