@@ -24,6 +24,26 @@ __device__ inline int owner_unit(long long s, long long T, int NW) {
   return (int)(((s + 1) * NW - 1) / T);
 }
 
+// Sum over a wave's 64 lanes without LDS round trips: DPP moves reduce each 16-lane row
+// (neighbour swap, pair swap, half-row mirror, row mirror; after the two swaps a quad holds one
+// value, so each mirror adds two equal-valued groups), then the four rows' sums are read from
+// lanes 0, 16, 32 and 48 and added in that order.  Every lane returns the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_move<0xB1>(v);     // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);     // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0x141>(v);    // row_half_mirror
+  v += dpp_move<0x140>(v);    // row_mirror
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((a + b) + c) + d;
+}
+
 template <int NTH>
 __global__ __launch_bounds__(NTH) void rmsnorm_kernel(NormP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
@@ -104,7 +124,7 @@ __global__ __launch_bounds__(NTH) void rmsnorm_kernel(NormP p) {
     if (valid[j])
 #pragma unroll
       for (int e = 0; e < 4; ++e) s = fmaf(xv[j][e], xv[j][e], s);
-  s = wave_sum(s);
+  s = wave_sum_dpp(s);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
   float tot = 0.f;
