@@ -13,7 +13,7 @@
 // the next pass is in flight.  Scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_16x16x32_bf16; the K rows fed to the MFMA are permuted so that lane l owns one
 // query (l % 16) and 8 consecutive keys of each tile, so the online-softmax statistics stay in
-// the lane (two xor shuffles finish a row) and the probabilities are already the B operand of
+// the lane (two permlane-swap exchanges finish a row) and the probabilities are already the B operand of
 // O^T = V^T P^T, whose A operand is one 16-byte LDS read of V^T.  The split count is chosen
 // on the device from the prefix length (the fewest passes per split within 32 splits), and
 // the 64-key passes are dealt to the splits in turn, so each split's first pass (keys

@@ -66,6 +66,28 @@ __device__ inline u32x4_t e4m3x8_to_bf16(u32x2_t x) {
   return r;
 }
 
+// Lane exchanges across 16-lane rows by the gfx950 permlane swaps, in the VALU rather than
+// through LDS.  Given one value in both operands, permlane16_swap returns rows (x0, x0, x2, x2)
+// and (x1, x1, x3, x3), so combining its two results gives every lane the combination of its
+// row pair (lanes l and l ^ 16); permlane32_swap likewise pairs the wave's halves (l ^ 32).
+// Both lanes of a pair compute the same combination in the same operand order.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // One split (key range s of query block qblk of kv head g, query-head group hg) by the WPG
 // waves of the calling workgroup; smem: LDS of at least attn_smem_bytes<D, WPG>() bytes.
 // COH: q and the K/V tiles were written earlier in the same kernel by other compute units of
@@ -229,8 +251,7 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
             sc[u][kb][qb][r] = v;
             mx = fmaxf(mx, v);
           }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_xor32(max_xor16(mx));
       const float mnew = fmaxf(mrow[qb], mx);
       const float alpha = __builtin_amdgcn_exp2f(mrow[qb] - mnew);
       float sum = 0.f;
@@ -250,8 +271,7 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
         for (int i = 0; i < 4; ++i) pk[i] = pack2bf(pv[2 * i], pv[2 * i + 1]);
         pf[u][qb] = pk;
       }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
+      sum = sum_xor32(sum_xor16(sum));
       lrow[qb] = lrow[qb] * alpha + sum;
       mrow[qb] = mnew;
 #pragma unroll
