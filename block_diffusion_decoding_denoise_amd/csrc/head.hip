@@ -22,7 +22,7 @@
 // software-pipelined over tiles: (1) of tile t + 1 and (2) of tile t run between the same two
 // barriers, (3) of tile t after them, so a tile costs one barrier.  E is read
 // from HBM once per row group; the groups of one chunk run on one XCD, so the second
-// group mostly hits L2.  Partial statistics and partial pe per chunk go to the workspace
+// group mostly hits L2.  Partial statistics and partial pe (bf16) per chunk go to the workspace
 // and a combine kernel merges the chunks in index order (deterministic).
 #include "head.h"
 
@@ -36,7 +36,7 @@ struct HeadP {
   const uint8_t* committed;
   int rows, d, V;
   float* st;               // [CH][rows_max][8] partial stats
-  float* pe_part;          // [CH][rows_max][d]
+  float* pe_part;          // [CH][rows_max][d]: f32 path float, bf16 path bf16 (uint16_t)
   float* logits_dbg;       // [rows, V] or null
   int rows_max, chunks_fixed;
   // outputs (combine)
@@ -314,17 +314,19 @@ __global__ __launch_bounds__(NW * 64) void head_bf16_kernel(HeadP p) {
       st[ST_BI] = __int_as_float(bi);
     }
   }
-  // acc[u][hb] lane l: row 4(l/16)+r, d = kw0*32 + u*32 + 16hb + l%16
+  // acc[u][hb] lane l: row 4(l/16)+r, d = kw0*32 + u*32 + 16hb + l%16; stored in bf16 (the
+  // combine reads 256 chunks' partials of every open row, so this halves its bytes; each partial
+  // is one term of a positively weighted sum, and the result feeds a bf16 input anyway)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int k = 16 * grp + 4 * (lane >> 4) + r;
     if (k < n_open) {
-      float* dst = p.pe_part + ((size_t)chunk * p.rows_max + k) * p.d + kw0 * 32;
+      uint16_t* dst = (uint16_t*)p.pe_part + ((size_t)chunk * p.rows_max + k) * p.d + kw0 * 32;
 #pragma unroll
       for (int u = 0; u < MAXK; ++u)
         if (u < nk) {
-          dst[u * 32 + (lane & 15)] = acc[u][0][r];
-          dst[u * 32 + 16 + (lane & 15)] = acc[u][1][r];
+          dst[u * 32 + (lane & 15)] = f2bf(acc[u][0][r]);
+          dst[u * 32 + 16 + (lane & 15)] = f2bf(acc[u][1][r]);
         }
     }
   }
@@ -495,16 +497,24 @@ __global__ __launch_bounds__(256) void head_combine_kernel(HeadP p, int bf16_pat
   if (dcol < p.d) {
     // branch-free buffer loads (chunks past CH read zeros; the host keeps the partial area
     // below 2^31 bytes)
-    const __amdgpu_buffer_rsrc_t pr = make_rsrc(p.pe_part, (uint32_t)((size_t)CH * p.rows_max * p.d * 4));
-    const uint32_t off0 = (uint32_t)(((size_t)k * p.d + dcol) * 4), cstride = (uint32_t)(p.rows_max * p.d * 4);
+    const int es = bf16_path ? 2 : 4;                // partial element bytes
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(p.pe_part, (uint32_t)((size_t)CH * p.rows_max * p.d * es));
+    const uint32_t off0 = (uint32_t)(((size_t)k * p.d + dcol) * es), cstride = (uint32_t)(p.rows_max * p.d * es);
     float a = 0.f;
     constexpr int NB = 64;     // partial loads in flight per thread
     for (int c0 = 0; c0 < CH; c0 += NB) {
       float v[NB];
+      if (bf16_path) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            pr, c0 + j < CH ? (int)(off0 + (uint32_t)(c0 + j) * cstride) : (int)0x80000000, 0, 0));
+        for (int j = 0; j < NB; ++j)
+          v[j] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(
+              pr, c0 + j < CH ? (int)(off0 + (uint32_t)(c0 + j) * cstride) : (int)0x80000000, 0, 0));
+      } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              pr, c0 + j < CH ? (int)(off0 + (uint32_t)(c0 + j) * cstride) : (int)0x80000000, 0, 0));
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j) a = fmaf(wts[c0 + j], v[j], a);     // c0 + j < 256
     }
