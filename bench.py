@@ -322,6 +322,9 @@ def main():
                          "gate/up launches, a 2-block MoE leg and the reference copy")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel leg plus a 256 MiB device copy (for counter runs)")
+    ap.add_argument("--attn-out", action="store_true",
+                    help="per-op kernels with the attention-output projection inside the attention launch "
+                         "(DLM_LAYERS_ATTN_OUT)")
     ap.add_argument("--fused-layers", action="store_true",
                     help="decode with the fused layer kernels (one launch per sublayer)")
     ap.add_argument("--no-full", action="store_true", help="skip the in-order 128-block generation leg")
@@ -329,6 +332,7 @@ def main():
     ap.add_argument("--no-threshold", action="store_true",
                     help="skip the threshold-block leg (whose later rounds' kernels only read the continue flag)")
     args = ap.parse_args()
+    layer_path = 2 if args.attn_out else None        # DLM_LAYERS_ATTN_OUT
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
@@ -358,7 +362,7 @@ def main():
         a = w[n]
         dev_w[n] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
     log(f"weights drawn and uploaded in {time.time() - t0:.1f}s")
-    model = dlm.Model(shape, dev_w, cap=cap, fused_layers=args.fused_layers)
+    model = dlm.Model(shape, dev_w, cap=cap, fused_layers=args.fused_layers, layer_path=layer_path)
     prompt = torch.from_numpy(synth.prompt_ids(shape, args.prompt, args.seed))
     host_tok = torch.empty(max(args.steps, NB), B, dtype=torch.int32).pin_memory()
     # device-side prefix of each timed block: the pending commit pass of the block before it
@@ -455,7 +459,8 @@ def main():
     fp8_cache = None
     if ks and pipelined and not args.no_fp8_cache:
         bf16_model = model
-        model = dlm.Model(shape, dev_w, cap=cap, kv_scales=FP8_CACHE_SCALES, fused_layers=args.fused_layers)
+        model = dlm.Model(shape, dev_w, cap=cap, kv_scales=FP8_CACHE_SCALES, fused_layers=args.fused_layers,
+                          layer_path=layer_path)
         sec, wall, R = run(args.k, args.steps, args.warmup)
         rb = sum(block_bytes(L, R, kv_elem_bytes=1) for L in L_of)
         fp8_cache = {"k": args.k, "kv_scales": list(FP8_CACHE_SCALES), "tok_s": round(n_new / sec, 1),
@@ -617,7 +622,7 @@ def main():
         for n in names:
             dev_w[n] = torch.from_numpy(ws[n].view(np.int16)).view(torch.bfloat16).to("cuda")
         del ws
-        model = dlm.Model(shape, dev_w, cap=cap, fused_layers=args.fused_layers)
+        model = dlm.Model(shape, dev_w, cap=cap, fused_layers=args.fused_layers, layer_path=layer_path)
         prompt = torch.from_numpy(synth.prompt_ids(shape, args.prompt, sd))
         sec, _, _ = run(args.k, args.steps, args.warmup)
         per_seed[str(sd)] = n_new / sec
@@ -769,7 +774,9 @@ def main():
                                f"{h['mean_prefix']:.0f})",
                    "k": args.k, "block": B, "prompt": args.prompt, "new_tokens": NB * B, "timed_blocks": args.steps,
                    "mean_prefix": h["mean_prefix"], "layers": s.n_layers,
-                   "layer_kernels": "fused (one launch per sublayer)" if args.fused_layers else "per op",
+                   "layer_kernels": "fused (one launch per sublayer)" if args.fused_layers else
+                   "per op, attention output projection inside the attention launch" if args.attn_out else
+                   "per op",
                    "commit_pass": "pipelined into the next block's round 0" if pipelined else "separate",
                    "d": s.d, "ffn": s.ffn, "vocab": s.vocab},
         "rounds_per_s": h["rounds_s"], "hbm_frac_step": h["hbm_frac"], "tpf": h["tpf"],

@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdlm.so")
 
 DLM_F32, DLM_BF16, DLM_MXFP4, DLM_FP8_E4M3 = 0, 1, 2, 3
-DLM_LAYERS_PER_OP, DLM_LAYERS_FUSED = 0, 1
+DLM_LAYERS_PER_OP, DLM_LAYERS_FUSED, DLM_LAYERS_ATTN_OUT = 0, 1, 2
 THRESHOLD, FIXED_K = 0, 1
 FLAG_HIT_MAX_ROUNDS, FLAG_NONFINITE = 1, 2
 MAX_ROWS = 64
@@ -323,9 +323,12 @@ class Model:
     wg,wu,wd}``).  bf16 tensors are given as torch.bfloat16.
     kv_scales: None for a cache in the model dtype, or (k_scale, v_scale) for an FP8 e4m3
     cache (bf16 models): uint8 codes, stored value = scale * e4m3(code).
+    fused_layers: one launch per sublayer (DLM_LAYERS_FUSED).  layer_path: the descriptor's value
+    itself (DLM_LAYERS_PER_OP, DLM_LAYERS_FUSED or DLM_LAYERS_ATTN_OUT), overriding fused_layers.
     """
 
-    def __init__(self, shape, weights, cap, max_len=None, device="cuda", kv_scales=None, fused_layers=False):
+    def __init__(self, shape, weights, cap, max_len=None, device="cuda", kv_scales=None, fused_layers=False,
+                 layer_path=None):
         self.shape = shape
         self.w = weights
         self.device = device
@@ -333,7 +336,8 @@ class Model:
         dt = DLM_BF16 if s.dtype == "bf16" else DLM_F32
         self.desc = ModelDesc(dt, s.n_layers, s.d, s.hq, s.hkv, s.head_dim, s.ffn, s.vocab, s.block, s.rope_base,
                               s.eps, s.n_experts, s.expert_ffn, s.top_k, s.n_shared,
-                              DLM_LAYERS_FUSED if fused_layers else DLM_LAYERS_PER_OP)
+                              layer_path if layer_path is not None
+                              else DLM_LAYERS_FUSED if fused_layers else DLM_LAYERS_PER_OP)
         L = lib()
         self._layers = (LayerWeights * s.n_layers)()
         for i in range(s.n_layers):

@@ -352,6 +352,12 @@ struct dlm_model {
   // QKV, attention-output and down matrices are then packed in its layouts
   bool fused;
   FusedDims fd;
+  // per-op path with the attention-output projection inside the attention launch (layer.hip
+  // attn_out_xcd) for 32- and 64-row forwards, on request: the attention-output matrix is also
+  // packed as the fused path's 8 column slices (off_ox); wide prefill forwards keep the
+  // separate GEMM
+  bool xo;
+  std::vector<size_t> off_ox;
   std::mutex mu;
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::vector<hipGraph_t> graph_objs;
@@ -373,7 +379,9 @@ static int check_model_desc(const dlm_model_desc* d) {
   DLM_REQUIRE(d->head_dim == 64 || d->head_dim == 128, DLM_ERR_SHAPE, "head_dim must be 64 or 128");
   DLM_REQUIRE(d->block <= 32, DLM_ERR_SHAPE, "block must be <= 32");
   DLM_REQUIRE(d->d % 32 == 0 && d->d <= 4096, DLM_ERR_SHAPE, "d must be a multiple of 32, <= 4096");
-  DLM_REQUIRE(d->layer_path == DLM_LAYERS_PER_OP || d->layer_path == DLM_LAYERS_FUSED, DLM_ERR_ARG,
+  DLM_REQUIRE(d->layer_path == DLM_LAYERS_PER_OP || d->layer_path == DLM_LAYERS_FUSED ||
+                  d->layer_path == DLM_LAYERS_ATTN_OUT,
+              DLM_ERR_ARG,
               "layer_path %d", d->layer_path);
   const bool moe = d->n_experts > 0;
   if (!moe) DLM_REQUIRE(d->ffn > 0 && d->ffn % 32 == 0, DLM_ERR_SHAPE, "ffn must be a positive multiple of 32");
@@ -390,10 +398,19 @@ static int check_model_desc(const dlm_model_desc* d) {
   return DLM_OK;
 }
 
+// On request (DLM_LAYERS_ATTN_OUT), dense bf16 models with 8 kv heads of 4 query heads of 128,
+// 32-row blocks, d % 512 == 0 and d <= 3072 (at most 96 output features per workgroup in the
+// projection) take the attention and its output projection as one launch on the per-op path.
+static bool xo_ok(const dlm_model_desc& d) {
+  return d.layer_path == DLM_LAYERS_ATTN_OUT && d.dtype == DLM_BF16 && d.n_experts == 0 && d.hq == 32 &&
+         d.hkv == 8 && d.head_dim == 128 && d.block == 32 && d.d % 512 == 0 && d.d <= 3072;
+}
+
 static void layout_packed(dlm_model* m) {
   const dlm_model_desc& d = m->d;
   const int D = d.head_dim;
   m->n_qkv = (d.hq + 2 * d.hkv) * D;
+  m->xo = xo_ok(d);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes, 256); return o; };
   m->off_sc = take((size_t)d.d * d.d * 2);
@@ -403,9 +420,11 @@ static void layout_packed(dlm_model* m) {
   m->off_dn.resize(d.n_layers);
   m->off_router.resize(d.n_layers);
   m->off_moe.resize(d.n_layers);
+  m->off_ox.assign(d.n_layers, 0);
   for (int l = 0; l < d.n_layers; ++l) {
     m->off_qkv[l] = take((size_t)m->n_qkv * d.d * 2);
     m->off_o[l] = take((size_t)d.d * d.hq * D * 2);
+    if (m->xo) m->off_ox[l] = take((size_t)d.d * d.hq * D * 2);
     if (d.n_experts == 0) {
       m->off_gu[l] = take((size_t)2 * d.ffn * d.d * 2);
       m->off_dn[l] = take((size_t)d.d * d.ffn * 2);
@@ -428,7 +447,7 @@ static void layout_packed(dlm_model* m) {
   m->fused = d.layer_path == DLM_LAYERS_FUSED &&
              layer_fused_ok(d.dtype, d.n_experts, d.d, d.hq, d.hkv, D, d.ffn, d.block) &&
              m->pl_gu.R == 2 * d.ffn / 256 && m->pl_gu.splits == 256;
-  if (m->fused) m->fd = fused_dims(d.d, d.ffn, d.hq, d.hkv, D);
+  if (m->fused || m->xo) m->fd = fused_dims(d.d, d.ffn, d.hq, d.hkv, D);
 }
 
 extern "C" size_t dlm_packed_bytes(const dlm_model_desc* d) {
@@ -523,6 +542,17 @@ extern "C" int dlm_pack_model(const dlm_model_desc* d, const void* w_sc, const d
     rc = m.pl_o.R ? pack_bf16_owned(so, ro, 1, d->d, d->hq * D, nullptr, m.pl_o.R, out + m.off_o[l], st)
                   : pack_bf16(so, ro, 1, d->d, d->hq * D, nullptr, out + m.off_o[l], st);
     if (rc) return rc;
+    if (m.xo) {
+      // the same matrix as 8 column slices (each XCD's query heads) for the fused attention output
+      const FusedDims& fd = m.fd;
+      for (int x = 0; x < 8; ++x) {
+        const void* sx[1] = {(const uint16_t*)L.wo + (size_t)x * fd.ko};
+        int rx[1] = {d->d};
+        if ((rc = pack_bf16_owned(sx, rx, 1, d->d, fd.ko, nullptr, fd.ro,
+                                  out + m.off_ox[l] + (size_t)x * d->d * fd.ko * 2, st, d->hq * D)))
+          return rc;
+      }
+    }
     if (d->n_experts == 0) {
       const void* s2[2] = {L.wg, L.wu};
       int r2[2] = {d->ffn, d->ffn};
@@ -689,7 +719,8 @@ static DecodeWs decode_layout(const dlm_model* m, const dlm_kv* kv, char* base) 
     w.pb = (float*)take((size_t)64 * 8 * d.d * 4);
     w.xn8 = (uint16_t*)take((size_t)8 * 64 * d.d * 2);
   }
-  if (m->fused || xcd_combine(m)) {
+  if (m->xo) w.pa = (float*)take((size_t)64 * 8 * d.d * 4);   // the attention output's XCD partials
+  if (m->fused || m->xo || xcd_combine(m)) {
     w.bar = (unsigned*)take(8 * 64 * 4);
     w.err = (int*)take(9 * 128);
   }
@@ -830,29 +861,42 @@ static int enqueue_layers(const dlm_model* m, const dlm_kv* kv, const DecodeWs& 
     if (rc) return rc;
     if (last && last_kv_only) break;
     const float scale = 1.0f / sqrtf((float)D);
-    if (bf) rc = attn_bf16(w.q, kv->k[l], kv->v[l], w.o, d.hq, d.hkv, D, d.block, nqb, kv->cap, scale, kv->len_dev,
-                           0, cont, model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st,
-                           AttnKv{kv->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, kv->k_scale, kv->v_scale},
-                           AttnXSync{w.bar, w.err});
-    else rc = attn_f32((const float*)w.q, (const float*)kv->k[l], (const float*)kv->v[l], (float*)w.o, d.hq, d.hkv,
-                       D, B, kv->cap, scale, kv->len_dev, 0, cont, st);
-    if (rc) return rc;
-    e = epi_zero();
-    e.kind = bf && !m->pl_o.R ? EPI_PARTIAL : EPI_RESID;
-    e.M = B;
-    e.bf16_out = bf;
-    e.out = w.x;
-    e.ld_out = d.d;
-    e.cont_dev = cont;
-    if (bf) {
-      rc = gemm_bf16(pk + m->off_o[l], w.o, d.d, qd, MAP_IDENTITY, e, m->pl_o, w.gemm_ws, st);
-      if (!m->pl_o.R) ps = gemm_partials(d.d, qd, m->pl_o, w.gemm_ws, B);
+    if (m->xo && nqb <= 2) {
+      // attention and output projection in one launch; its 8 XCD partials are added into x by
+      // the next RMSNorm, in XCD order
+      if ((rc = attn_out_xcd(m->fd, nqb, (const uint16_t*)(pk + m->off_ox[l]), (const uint16_t*)w.q, kv->k[l],
+                             kv->v[l], (uint16_t*)w.o, w.attn_ws, w.pa, w.bar, w.err, kv->cap, kv->len_dev,
+                             model_attn_plan(m, kv), scale,
+                             AttnKv{kv->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, kv->k_scale, kv->v_scale}, cont, st)))
+        return rc;
+      ps = PartialSrc{};
+      ps.slots = w.pa;
+      ps.nslot = 8;
     } else {
-      F32Mats W{};
-      W.w[0] = (const float*)L.wo; W.rows[0] = d.d;
-      rc = gemm_f32(W, (const float*)w.o, d.d, qd, MAP_IDENTITY, e, st);
+      if (bf) rc = attn_bf16(w.q, kv->k[l], kv->v[l], w.o, d.hq, d.hkv, D, d.block, nqb, kv->cap, scale, kv->len_dev,
+                             0, cont, model_attn_plan(m, kv), w.attn_ws, /*out_packed=*/1, st,
+                             AttnKv{kv->kv_dtype == DLM_FP8_E4M3 ? 1 : 0, kv->k_scale, kv->v_scale},
+                             AttnXSync{w.bar, w.err});
+      else rc = attn_f32((const float*)w.q, (const float*)kv->k[l], (const float*)kv->v[l], (float*)w.o, d.hq, d.hkv,
+                         D, B, kv->cap, scale, kv->len_dev, 0, cont, st);
+      if (rc) return rc;
+      e = epi_zero();
+      e.kind = bf && !m->pl_o.R ? EPI_PARTIAL : EPI_RESID;
+      e.M = B;
+      e.bf16_out = bf;
+      e.out = w.x;
+      e.ld_out = d.d;
+      e.cont_dev = cont;
+      if (bf) {
+        rc = gemm_bf16(pk + m->off_o[l], w.o, d.d, qd, MAP_IDENTITY, e, m->pl_o, w.gemm_ws, st);
+        if (!m->pl_o.R) ps = gemm_partials(d.d, qd, m->pl_o, w.gemm_ws, B);
+      } else {
+        F32Mats W{};
+        W.w[0] = (const float*)L.wo; W.rows[0] = d.d;
+        rc = gemm_f32(W, (const float*)w.o, d.d, qd, MAP_IDENTITY, e, st);
+      }
+      if (rc) return rc;
     }
-    if (rc) return rc;
     if ((rc = rmsnorm(w.x, L.ffn_norm, w.xn, B, d.d, bf, bf, d.eps, cont, st, &ps))) return rc;
     ps = PartialSrc{};
     if (d.n_experts) {

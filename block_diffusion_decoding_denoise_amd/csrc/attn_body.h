@@ -97,8 +97,15 @@ constexpr int attn_smem_bytes() {
   return 2 * PT * (TK * (2 * D + 16) + D * (64 + 16));
 }
 
-template <int D, int WPG, bool KV8, bool COH>
-__device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g, int hg, int s, uint8_t* smem_base) {
+// hook: called once by every thread when the split's first two passes are in flight (or, for a
+// workgroup without a split, when it knows it has none): loads it issues then queue behind them.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <int D, int WPG, bool KV8, bool COH, typename Hook = NoHook>
+__device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g, int hg, int s, uint8_t* smem_base,
+                                                Hook hook = Hook()) {
   constexpr int DS = D / 32;    // d-steps of the score MFMA
   constexpr int DB = D / 16;    // dv blocks of the output
   constexpr int NT = 64 * WPG;
@@ -193,7 +200,10 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
   const int N = min(L + p.B, p.cap);
   const int chunk = split_chunk(N, p.nsplit_max);
   const int nsplit = (N + chunk - 1) / chunk;
-  if (s >= nsplit) return;
+  if (s >= nsplit) {
+    hook();
+    return;
+  }
   DLM_TRACE_POINT(1);
   kend = N;
   const int P = (N + PT * TK - 1) / (PT * TK);
@@ -206,6 +216,7 @@ __device__ __forceinline__ void attn_split_body(const AttnP& p, int qblk, int g,
 
   stash(0);
   if (npass > 1) fetch((s + nsplit) * PT * TK);
+  hook();
   __syncthreads();
   for (int ip = 0; ip < npass; ++ip) {
     const int p0 = (s + ip * nsplit) * PT * TK;

@@ -57,6 +57,16 @@ int fused_attn_sublayer(const FusedDims& fd, int mb, const uint16_t* wqkv, const
                         const void* gain, float eps, const LayerIO& io, const LayerBufs& b, const EpiParams& qkv_epi,
                         AttnPlan plan, float softmax_scale, AttnKv kvf, int last_kv_only, const int32_t* cont_dev,
                         hipStream_t st);
+// The attention (32 key splits per kv head), its split combine and the attention-output
+// projection in one launch, for the per-op path of the models the fused path serves: q
+// [32 mb][hq][D] and the K/V cache as the QKV launch before left them; o_packed receives the
+// attention output (packed 32-row panels); the projection leaves 8 XCD partials,
+// part_out[row][8][d], for the next RMSNorm to add in XCD order.  wo_slices: the
+// attention-output matrix as 8 column slices in the row-owned layout (as the fused path packs it).
+int attn_out_xcd(const FusedDims& fd, int mb, const uint16_t* wo_slices, const uint16_t* q, const void* k_cache,
+                 const void* v_cache, uint16_t* o_packed, void* attn_ws, float* part_out, unsigned* bar, int* err,
+                 int cap, const int32_t* len_dev, AttnPlan plan, float softmax_scale, AttnKv kvf,
+                 const int32_t* cont_dev, hipStream_t st);
 // FFN sublayer: norm, gate/up + SwiGLU, down.
 int fused_ffn_sublayer(const FusedDims& fd, int mb, const uint16_t* wgu, const uint16_t* wd_slices, const void* gain,
                        float eps, const LayerIO& io, const LayerBufs& b, const int32_t* cont_dev, hipStream_t st);

@@ -307,6 +307,87 @@ constexpr int smem_bytes() {
 // ------------------------------------------------------------------ attention sublayer
 constexpr int kRing = 8;     // weight steps in flight per wave
 
+// Attention of kv head x's query heads (key split w of each query block), the split combine,
+// and the slice of the attention-output projection that contracts over those heads' columns,
+// left as XCD x's partial of every output row.  q and the K/V cache were written before: earlier
+// in the same launch, or by the launch before.  check: verify the group's XCD placement after
+// the first barrier (a launch whose first barrier is this one's).
+template <int MB, bool KV8>
+__device__ __forceinline__ void attn_out_steps(const LayerP& p, int x, int w, int v, unsigned* bar, float* red,
+                                               uint8_t* smem, bool check) {
+  const int lane = threadIdx.x & 63;
+  const int d = p.d, G = p.hq / p.hkv, D = p.D;
+  // The attention output is computed by waves 2 and 3, the split combine by waves 0 and 1.
+  // Waves 2 and 3 request all of this workgroup's attention-output weights (features
+  // [ro w, +ro) over kv head x's G D columns; kNo steps each) as soon as the first query
+  // block's first two key passes are in flight, so the weights stream while the attention
+  // computes; only later passes of long prefixes queue behind them.
+  constexpr int kNo = 16;           // (G D / 16) / 2 wave steps: G D = 512
+  const int Ro = p.fd.ro, Ko = p.fd.ko;
+  const int vo = v - 2;             // 0, 1 on the output waves
+  WBlk<3> wob;
+  wob.init(p.wo + ((size_t)x * d * Ko + (size_t)w * Ro * Ko), Ro, Ko / 16, 0);
+  u32x4_t wo_r[kNo][3];
+  auto o_step = [&](int i) { return vo + 2 * i; };     // block k-step of output-wave step i
+  auto issue_wo = [&] {
+    if (v >= 2) {
+#pragma unroll
+      for (int i = 0; i < kNo; ++i)
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+          wo_r[i][s] = bload16_nt(wob.r, o_step(i) < Ko / 16 ? wob.wo[s] + (uint32_t)o_step(i) * wob.sb : 0x80000000u);
+    }
+  };
+
+  // 3. attention: key split w of kv head x, for each query block
+  attn_split_body<128, 4, KV8, true>(p.attn, 0, x, 0, w, smem, issue_wo);
+  if (MB == 2) attn_split_body<128, 4, KV8, true>(p.attn, 1, x, 0, w, smem);
+  DLM_LAYER_TRACE(0, 5);
+  xcd_sync(bar, p.err);
+  if (check) check_placement(p.err, x);
+  DLM_LAYER_TRACE(0, 6);
+
+  // 4. split combine of kv head x's (query block, head, query, 4 columns) items, waves 0 and 1
+  if (v < 2) {
+    for (int it = w * 128 + (int)threadIdx.x; it < MB * 4 * 32 * 32; it += kWgPerXcd * 128) {
+      const int dvg = it & 31, qi = (it >> 5) & 31, hl = (it >> 10) & 3, qb = it >> 12;
+      attn_combine_item<128, true>(p.attn, qb, G * x + hl, qi, 4 * dvg);
+    }
+  }
+  DLM_LAYER_TRACE(0, 7);
+  xcd_sync(bar, p.err);
+  DLM_LAYER_TRACE(0, 8);
+
+  // 5. attention output from the held weights (waves 2 and 3): partial sums over kv head x's
+  // columns, the two waves' sums added in LDS
+  {
+    f32x16_t acc[3][MB];
+    zero_acc(acc);
+    if (v >= 2) {
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.attn.out, (uint32_t)MB * (uint32_t)(p.hq * D / 16) * 1024u);
+      const uint32_t xo = (uint32_t)lane * 16u + (uint32_t)(x * Ko / 16) * 1024u;
+      const uint32_t xpanel = (uint32_t)(p.hq * D / 16) * 1024u;
+      u32x4_t xf[kNo][MB];
+#pragma unroll
+      for (int i = 0; i < kNo; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xf[i][mb] = ld16_xcd(xr, (o_step(i) < Ko / 16 ? xo + (uint32_t)o_step(i) * 1024u : 0x80000000u) + mb * xpanel);
+#pragma unroll
+      for (int i = 0; i < kNo; ++i)
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[s][mb] = mfma32x32x16(wo_r[i][s], xf[i][mb], acc[s][mb]);
+    }
+    DLM_LAYER_TRACE(0, 9);
+    float sums[3][MB][4];
+    wave_reduce(acc, red, sums);        // waves 0 and 1 add zeros: same sums, fixed order
+    store_partial<3, MB>(p, x, w, Ro, sums, red);
+    DLM_LAYER_TRACE(0, 10);
+  }
+}
+
 template <int MB, bool KV8>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_sublayer_kernel(LayerP p) {
   if (p.cont_dev && *p.cont_dev == 0) return;
@@ -394,73 +475,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   xcd_sync(bar, p.err);
   DLM_LAYER_TRACE(0, 4);
+  attn_out_steps<MB, KV8>(p, x, w, v, bar, red, smem, false);
+}
 
-  // 3. attention: key split w of kv head x, for each query block
-#pragma unroll
-  for (int qb = 0; qb < MB; ++qb) attn_split_body<128, 4, KV8, true>(p.attn, qb, x, 0, w, smem);
-  DLM_LAYER_TRACE(0, 5);
-
-  // The attention output is computed by waves 2 and 3, the split combine by waves 0 and 1:
-  // waves 2 and 3 request all of this workgroup's attention-output weights (features
-  // [ro w, +ro) over kv head x's G D columns; kNo steps each) while the XCD meets after the
-  // attention, and their loads never sit ahead of the combine's in a memory queue.
-  constexpr int kNo = 16;           // (G D / 16) / 2 wave steps: G D = 512
-  const int Ro = p.fd.ro, Ko = p.fd.ko;
-  const int vo = v - 2;             // 0, 1 on the output waves
-  WBlk<3> wob;
-  wob.init(p.wo + ((size_t)x * d * Ko + (size_t)w * Ro * Ko), Ro, Ko / 16, 0);
-  u32x4_t wo_r[kNo][3];
-  auto o_step = [&](int i) { return vo + 2 * i; };     // block k-step of output-wave step i
-  xcd_sync(bar, p.err, [&] {
-    if (v >= 2) {
-#pragma unroll
-      for (int i = 0; i < kNo; ++i)
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-          wo_r[i][s] = bload16_nt(wob.r, o_step(i) < Ko / 16 ? wob.wo[s] + (uint32_t)o_step(i) * wob.sb : 0x80000000u);
-    }
-  });
-  DLM_LAYER_TRACE(0, 6);
-
-  // 4. split combine of kv head x's (query block, head, query, 4 columns) items, waves 0 and 1
-  if (v < 2) {
-    for (int it = w * 128 + (int)threadIdx.x; it < MB * 4 * 32 * 32; it += kWgPerXcd * 128) {
-      const int dvg = it & 31, qi = (it >> 5) & 31, hl = (it >> 10) & 3, qb = it >> 12;
-      attn_combine_item<128, true>(p.attn, qb, G * x + hl, qi, 4 * dvg);
-    }
-  }
-  DLM_LAYER_TRACE(0, 7);
-  xcd_sync(bar, p.err);
-  DLM_LAYER_TRACE(0, 8);
-
-  // 5. attention output from the held weights (waves 2 and 3): partial sums over kv head x's
-  // columns, the two waves' sums added in LDS
-  {
-    f32x16_t acc[3][MB];
-    zero_acc(acc);
-    if (v >= 2) {
-      const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.attn.out, (uint32_t)MB * (uint32_t)(p.hq * D / 16) * 1024u);
-      const uint32_t xo = (uint32_t)lane * 16u + (uint32_t)(x * Ko / 16) * 1024u;
-      const uint32_t xpanel = (uint32_t)(p.hq * D / 16) * 1024u;
-      u32x4_t xf[kNo][MB];
-#pragma unroll
-      for (int i = 0; i < kNo; ++i)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          xf[i][mb] = ld16_xcd(xr, (o_step(i) < Ko / 16 ? xo + (uint32_t)o_step(i) * 1024u : 0x80000000u) + mb * xpanel);
-#pragma unroll
-      for (int i = 0; i < kNo; ++i)
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[s][mb] = mfma32x32x16(wo_r[i][s], xf[i][mb], acc[s][mb]);
-    }
-    DLM_LAYER_TRACE(0, 9);
-    float sums[3][MB][4];
-    wave_reduce(acc, red, sums);        // waves 0 and 1 add zeros: same sums, fixed order
-    store_partial<3, MB>(p, x, w, Ro, sums, red);
-    DLM_LAYER_TRACE(0, 10);
-  }
+// The attention and its output projection alone, for the per-op path: q and the K/V cache come
+// from the QKV launch before, and the 8 XCD partials go to the next RMSNorm, which adds them to
+// the residual in XCD order.  One launch in place of two (attention, output projection).
+template <int MB, bool KV8>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_out_kernel(LayerP p) {
+  if (p.cont_dev && *p.cont_dev == 0) return;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<MB>()];
+  const int x = blockIdx.x & 7, w = blockIdx.x >> 3;
+  const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  publish_placement(p.err, x, w);
+  attn_out_steps<MB, KV8>(p, x, w, v, p.bar + x * 64, (float*)smem, smem, true);
 }
 
 // ------------------------------------------------------------------ FFN sublayer
@@ -673,6 +701,52 @@ int fused_attn_sublayer(const FusedDims& fd, int mb, const uint16_t* wqkv, const
     else launch(attn_sublayer_kernel<2, false>);
   }
   return check_hip(hipGetLastError(), "fused attention sublayer launch");
+}
+
+int attn_out_xcd(const FusedDims& fd, int mb, const uint16_t* wo_slices, const uint16_t* q, const void* k_cache,
+                 const void* v_cache, uint16_t* o_packed, void* attn_ws, float* part_out, unsigned* bar, int* err,
+                 int cap, const int32_t* len_dev, AttnPlan plan, float softmax_scale, AttnKv kvf,
+                 const int32_t* cont_dev, hipStream_t st) {
+  if (mb != 1 && mb != 2) return fail(DLM_ERR_SHAPE, "attention with output: 32 or 64 rows");
+  if (plan.nsplit_max > kWgPerXcd) return fail(DLM_ERR_SHAPE, "attention with output: more key splits than workgroups");
+  LayerIO io{};
+  io.part_out = part_out;
+  LayerBufs b{};
+  b.bar = bar;
+  b.err = err;
+  LayerP p = base_params(fd, mb, nullptr, 0.f, io, b, cont_dev);
+  p.wo = wo_slices;
+  AttnP& a = p.attn;
+  a.q = q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.out = o_packed;
+  const int G = fd.hq / fd.hkv;
+  const size_t po = (size_t)mb * fd.hkv * plan.nsplit_max * G * 32 * fd.D * 2;
+  a.part_o = (uint16_t*)attn_ws;
+  a.part_ml = (float*)((char*)attn_ws + align_up(po, 256));
+  a.hq = fd.hq;
+  a.hkv = fd.hkv;
+  a.B = 32;
+  a.nqb = mb;
+  a.cap = cap;
+  a.chunk = plan.chunk;
+  a.nsplit_max = plan.nsplit_max;
+  a.out_packed = 1;
+  a.scale_log2 = softmax_scale * (kvf.fp8 ? kvf.k_scale : 1.f) * 1.4426950408889634f;
+  a.v_scale = kvf.fp8 ? kvf.v_scale : 1.f;
+  a.len_dev = len_dev;
+  a.len_host = 0;
+  a.cont_dev = nullptr;
+  auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(256), dim3(256), 0, st, p); };
+  if (mb == 1) {
+    if (kvf.fp8) launch(attn_out_kernel<1, true>);
+    else launch(attn_out_kernel<1, false>);
+  } else {
+    if (kvf.fp8) launch(attn_out_kernel<2, true>);
+    else launch(attn_out_kernel<2, false>);
+  }
+  return check_hip(hipGetLastError(), "attention with output launch");
 }
 
 int fused_ffn_sublayer(const FusedDims& fd, int mb, const uint16_t* wgu, const uint16_t* wd_slices, const void* gain,

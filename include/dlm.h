@@ -247,11 +247,16 @@ typedef struct {
                                 DLM_LAYERS_FUSED (1): one launch per sublayer with XCD-local
                                 synchronisation, for dense bf16 models with 8 kv heads of 4 query
                                 heads of 128, 32-row blocks, d % 512 == 0 and ffn % 256 == 0
-                                (other models take the per-op kernels).  The packed layout
-                                depends on it: pack and create with the same value. */
+                                (other models take the per-op kernels);
+                                DLM_LAYERS_ATTN_OUT (2): the per-op kernels, except that the
+                                attention and its output projection run as one launch (forwards
+                                of 32 and 64 rows) on dense bf16 models with 8 kv heads of 4
+                                query heads of 128, 32-row blocks, d % 512 == 0 and d <= 3072.
+                                The packed layout depends on it: pack and create with the same
+                                value. */
 } dlm_model_desc;
 
-enum { DLM_LAYERS_PER_OP = 0, DLM_LAYERS_FUSED = 1 };
+enum { DLM_LAYERS_PER_OP = 0, DLM_LAYERS_FUSED = 1, DLM_LAYERS_ATTN_OUT = 2 };
 
 typedef struct {
   const void* attn_norm;     /* [d] */

@@ -101,6 +101,23 @@ def test_model_desc_validation():
     assert L.dlm_packed_bytes(ctypes.byref(f32)) == 0       # f32 models up to d = 256 only
 
 
+def test_layer_path_packing():
+    """Models whose attention-output projection runs inside the attention launch
+    (DLM_LAYERS_ATTN_OUT) pack that matrix a second time, as 8 column slices: exactly one more
+    d x (hq D) bf16 matrix per layer than the per-op path; models that launch does not serve
+    pack the same bytes either way; an unknown layer path is rejected."""
+    L = dlm.lib()
+
+    def nbytes(path, d=2560, hq=32, hkv=8, D=128):
+        desc = dlm.ModelDesc(dlm.DLM_BF16, 36, d, hq, hkv, D, 9728, 151936, 32, 1e4, 1e-6, 0, 0, 0, 0, path)
+        return L.dlm_packed_bytes(ctypes.byref(desc))
+
+    assert nbytes(dlm.DLM_LAYERS_ATTN_OUT) - nbytes(dlm.DLM_LAYERS_PER_OP) == 36 * 2560 * 4096 * 2
+    for kw in ({"hkv": 4}, {"D": 64}, {"d": 3584}):          # not 8 groups of 4 x 128, or d > 3072
+        assert nbytes(dlm.DLM_LAYERS_ATTN_OUT, **kw) == nbytes(dlm.DLM_LAYERS_PER_OP, **kw) > 0
+    assert nbytes(3) == 0
+
+
 def test_valid_call_without_device_is_unsupported():
     """A fully valid call reaches the device check; with no gfx950 device current it
     returns DLM_ERR_UNSUPPORTED (on a GPU machine this test is skipped)."""

@@ -31,10 +31,11 @@ def _upload(w: synth.Weights):
     return {n: storage(w[n], dt) for n in w.names_dense()}
 
 
-def _gpu_model(shape, seed, cap, max_len=None, kv_scales=None, fused_layers=False):
+def _gpu_model(shape, seed, cap, max_len=None, kv_scales=None, fused_layers=False, layer_path=None):
     dlm = _dlm()
     w = synth.Weights(shape, seed)
-    return dlm.Model(shape, _upload(w), cap=cap, max_len=max_len, kv_scales=kv_scales, fused_layers=fused_layers), w
+    return dlm.Model(shape, _upload(w), cap=cap, max_len=max_len, kv_scales=kv_scales, fused_layers=fused_layers,
+                     layer_path=layer_path), w
 
 
 def _cache_values(m, kv_scales):
@@ -170,7 +171,7 @@ def _rel_rows(a, b):
 
 
 def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_scales=None, check_rounds=None,
-              cache_layers=True, fused_layers=False, trunk_model=False):
+              cache_layers=True, fused_layers=False, trunk_model=False, layer_path=None):
     """Run rounds one at a time; after each round recompute it with the oracle from the
     GPU's own round-start state and compare the statistics and the commit.
 
@@ -190,7 +191,7 @@ def _lockstep(shape, seed, prompt_len, n_blocks, rule_args, check_every=1, kv_sc
     dlm = _dlm()
     _say(f"lockstep {shape.name} d={shape.d} L={shape.n_layers} seed={seed} kv_scales={kv_scales}")
     cap = prompt_len + (n_blocks + 1) * shape.block
-    m, w = _gpu_model(shape, seed, cap, kv_scales=kv_scales, fused_layers=fused_layers)
+    m, w = _gpu_model(shape, seed, cap, kv_scales=kv_scales, fused_layers=fused_layers, layer_path=layer_path)
     prec = Prec(shape.dtype, kv_scales=kv_scales)
     om = OracleModel(shape, w, prec, cache_layers=cache_layers)
     prompt = synth.prompt_ids(shape, prompt_len, seed)

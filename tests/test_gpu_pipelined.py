@@ -35,9 +35,13 @@ def _dlm():
 
 
 def _model(shape, seed, cap, kv_scales=None, fused_layers=False):
+    """fused_layers: False (per-op kernels), True (one launch per sublayer) or "attn-out"
+    (per-op kernels with the attention-output projection inside the attention launch)."""
     dlm = _dlm()
     w = synth.Weights(shape, seed)
     up = {n: storage(w[n], shape.dtype) for n in w.names_dense()}
+    if fused_layers == "attn-out":
+        return dlm.Model(shape, up, cap=cap, kv_scales=kv_scales, layer_path=dlm.DLM_LAYERS_ATTN_OUT), w
     return dlm.Model(shape, up, cap=cap, kv_scales=kv_scales, fused_layers=fused_layers), w
 
 
@@ -71,8 +75,12 @@ FUSED_SMALL = synth.small_shape(synth.QWEN4B, name="fused-small", n_layers=2, d=
     (FUSED_SMALL, 1242, 32, 2, ("threshold", 0.5, True, 32), None, True),
     (FUSED_SMALL, 1243, 64, 2, ("fixed_k", 6), (0.07, 0.11), True),
     (QWEN4B_2L, 1245, 256, 3, ("fixed_k", 6), None, True),
+    (FUSED_SMALL, 1246, 64, 3, ("fixed_k", 6), None, "attn-out"),
+    (FUSED_SMALL, 1247, 32, 2, ("threshold", 0.5, True, 32), (0.07, 0.11), "attn-out"),
+    (QWEN4B_2L, 1248, 256, 2, ("fixed_k", 6), None, "attn-out"),
 ], ids=["small-k6", "small-threshold", "small-k32", "qwen4b-2l-k6", "small-k6-fp8-cache", "qwen4b-2l-k6-fp8-cache",
-        "fused-small-k6", "fused-small-threshold", "fused-small-k6-fp8-cache", "fused-qwen4b-2l-k6"])
+        "fused-small-k6", "fused-small-threshold", "fused-small-k6-fp8-cache", "fused-qwen4b-2l-k6",
+        "attn-out-small-k6", "attn-out-small-threshold-fp8-cache", "attn-out-qwen4b-2l-k6"])
 def test_pipelined_bitexact_bf16(shape, seed, prompt_len, n_blocks, rule_args, kv_scales, fused):
     dlm = _dlm()
     _say(f"pipelined vs separate commit passes: {shape.name} seed {seed} prompt {prompt_len} "
@@ -130,8 +138,10 @@ def test_pipelined_bitexact_moe(shape, seed, prompt_len, n_blocks, rule_args, kv
 
 
 @pytest.mark.parametrize("shape,seed,prompt_len,fused", [(SMALL, 1237, 96, False), (QWEN4B_2L, 1238, 64, False),
-                                                         (MOE_SMALL, 1239, 160, False), (FUSED_SMALL, 1244, 160, True)],
-                         ids=["small-3blocks", "qwen4b-2l", "moe-small-5blocks", "fused-small-5blocks"])
+                                                         (MOE_SMALL, 1239, 160, False), (FUSED_SMALL, 1244, 160, True),
+                                                         (FUSED_SMALL, 1249, 160, "attn-out")],
+                         ids=["small-3blocks", "qwen4b-2l", "moe-small-5blocks", "fused-small-5blocks",
+                              "attn-out-small-5blocks"])
 def test_prefill_pairs_bitexact(shape, seed, prompt_len, fused):
     """Prefill with 64-row forwards (two prompt blocks per pass, dlm_prefill_rows with 64 rows):
     the cache equals the one built block by block (one prefill call per block), bitwise."""
