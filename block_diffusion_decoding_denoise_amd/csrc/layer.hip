@@ -311,7 +311,7 @@ constexpr int kRing = 8;     // weight steps in flight per wave
 // and the slice of the attention-output projection that contracts over those heads' columns,
 // left as XCD x's partial of every output row.  q and the K/V cache were written before: earlier
 // in the same launch, or by the launch before.  check: verify the group's XCD placement after
-// the first barrier (a launch whose first barrier is this one's).
+// this function's first barrier (set when that barrier is the launch's first).
 template <int MB, bool KV8>
 __device__ __forceinline__ void attn_out_steps(const LayerP& p, int x, int w, int v, unsigned* bar, float* red,
                                                uint8_t* smem, bool check) {
